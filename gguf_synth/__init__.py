@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs for the block-quantized matmul: raw GGUF-layout
+weight blocks, fp32 activations and top-k routing tables.
+
+Both the HIP path and the CPU oracle consume the identical buffers made here.
+This module holds none of the method's arithmetic: it only places random
+draws into block fields (fp16 scale fields at their byte offsets, uniformly
+random bytes for packed quants).  Uniform random bytes give uniform 4-bit
+quants and, for Q4_K, uniform independent 6-bit scales and mins, because
+the 12 scale bytes carry each of their 96 bits in exactly one of the 16
+six-bit fields.
+
+Streams: numpy.random.default_rng([20261202, cfg, tensor]) with tensor ids
+0 = scales, 1 = quants, 2 = activations, 3 = expert ids, 4 = router logits,
+and 100 + 3*e + {0, 1, 2} for expert e's gate / up / down matrices.
+"""
+import numpy as np
+
+SEED = 20261202
+
+Q4_0, Q4_1, Q8_0, Q4_K = 2, 3, 8, 12
+FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K}
+NAMES = {v: k for k, v in FORMATS.items()}
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144}
+
+# scale distributions (fp64 uniform draws, rounded to fp16 by numpy)
+D_RANGE = (1e-3, 2e-2)
+M_RANGE = (-0.16, 0.0)  # Q4_1 block offset m
+
+
+def rng(cfg, tensor):
+    return np.random.default_rng([SEED, int(cfg), int(tensor)])
+
+
+def row_bytes(fmt, k):
+    return k // BLOCK_ELEMS[fmt] * BLOCK_BYTES[fmt]
+
+
+def _f16_field(g, count, lo, hi):
+    return g.uniform(lo, hi, size=count).astype(np.float16).view(np.uint8).reshape(count, 2)
+
+
+def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
+    """Random GGUF blocks for an [n][k] weight matrix -> uint8 [n][row_bytes]."""
+    qk, bs = BLOCK_ELEMS[fmt], BLOCK_BYTES[fmt]
+    if k % qk:
+        raise ValueError(f"k={k} is not a multiple of {qk}")
+    nblk = n * (k // qk)
+    gs = rng(cfg, 10 * tensor + 0)  # scale fields
+    gq = rng(cfg, 10 * tensor + 1)  # quant bytes
+    out = np.empty((nblk, bs), np.uint8)
+    if fmt == Q4_0:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)
+        out[:, 2:18] = gq.integers(0, 256, size=(nblk, 16), dtype=np.uint8)
+    elif fmt == Q4_1:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)
+        out[:, 2:4] = _f16_field(gs, nblk, *m_range)
+        out[:, 4:20] = gq.integers(0, 256, size=(nblk, 16), dtype=np.uint8)
+    elif fmt == Q8_0:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)
+        out[:, 2:34] = gq.integers(-127, 128, size=(nblk, 32), dtype=np.int8).view(np.uint8)
+    elif fmt == Q4_K:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)   # d
+        out[:, 2:4] = _f16_field(gs, nblk, *d_range)   # dmin
+        out[:, 4:144] = gq.integers(0, 256, size=(nblk, 140), dtype=np.uint8)
+    else:
+        raise ValueError(f"unknown format {fmt}")
+    return out.reshape(n, row_bytes(fmt, k))
+
+
+def activations(m, k, cfg, tensor=2, scale=1.0):
+    """fp32 [m][k], standard normal drawn in fp64 then rounded to fp32."""
+    return (rng(cfg, tensor).standard_normal((m, k)) * scale).astype(np.float32)
+
+
+def routing(n_tokens, n_experts, top_k, cfg):
+    """Top-k routing table: distinct uniform expert ids per token and softmax
+    weights over standard-normal logits (softmax taken over the k chosen
+    logits in fp64, stored fp32)."""
+    gi = rng(cfg, 3)
+    ids = np.stack([gi.choice(n_experts, top_k, replace=False) for _ in range(n_tokens)])
+    logits = rng(cfg, 4).standard_normal((n_tokens, top_k))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w = e / e.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w.astype(np.float32)
+
+
+def expert_weights(fmt, n_experts, n, k, cfg, which):
+    """n_experts consecutive [n][k] matrices; which = 0 gate, 1 up, 2 down."""
+    return np.concatenate(
+        [weights(fmt, n, k, cfg, tensor=100 + 3 * e + which) for e in range(n_experts)], axis=0)
+
+
+# The workloads.  Sizes are those of real GGUF tensors: a 1B-class attention
+# projection, an 8B-class FFN-up, a 128K-vocabulary LM head, and an lfm2moe
+# routed FFN (32 experts, top 4, hidden 2048, expert FFN width 1536).
+CONFIGS = {
+    "q4_0_gemv_2048": dict(cfg=0, kind="gemv", fmt=Q4_0, n=2048, k=2048, batches=(1,)),
+    "q8_0_gemv_ffn_up": dict(cfg=1, kind="gemv", fmt=Q8_0, n=14336, k=4096, batches=(1, 5)),
+    "q4_1_gemv_ffn_up": dict(cfg=11, kind="gemv", fmt=Q4_1, n=14336, k=4096, batches=(1, 5)),
+    "q4_k_gemv_lm_head": dict(cfg=2, kind="gemv", fmt=Q4_K, n=128256, k=4096, batches=(1, 4)),
+    "q4_0_gemm_prefill_512": dict(cfg=3, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=512),
+    "q4_0_gemm_prefill_2048": dict(cfg=13, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=2048),
+    "q4_k_moe_ffn": dict(cfg=4, kind="moe", fmt=Q4_K, n_tokens=256, hidden=2048, ffn=1536,
+                         n_experts=32, top_k=4),
+}

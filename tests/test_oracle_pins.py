@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against things other than itself: hand-decoded
+blocks, the block sizes the pages print, library fp16 conversions, closed
+forms, invariants, exact rational brute force and a second, independent
+formulation of the dot product.  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import gguf_synth as gs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "blocks.json")
+
+
+def golden_blocks():
+    with open(GOLDEN) as f:
+        return json.load(f)["blocks"]
+
+
+def q4k_golden_bytes(b):
+    qs = bytearray(128)
+    for c in range(4):
+        for i in range(32):
+            qs[32 * c + i] = (i % 16) | ((15 - i % 16) << 4)
+    return bytes.fromhex(b["hex_header"]) + bytes.fromhex(b["scale_bytes_hex"]) + bytes(qs)
+
+
+# --------------------------------------------------------------- block sizes
+def test_block_sizes_match_pages(orc):
+    # alice-llm 2.0.0 README, Quantization Block Specs: Q8_0 32 values / 34 B,
+    # Q4_K 256 values / 144 B.  Q4_0 and Q4_1 sizes follow from the layout
+    # reading (2 or 4 scale bytes + 16 nibble bytes).
+    assert (orc.block_elems(orc.Q8_0), orc.block_bytes(orc.Q8_0)) == (32, 34)
+    assert (orc.block_elems(orc.Q4_K), orc.block_bytes(orc.Q4_K)) == (256, 144)
+    assert (orc.block_elems(orc.Q4_0), orc.block_bytes(orc.Q4_0)) == (32, 18)
+    assert (orc.block_elems(orc.Q4_1), orc.block_bytes(orc.Q4_1)) == (32, 20)
+    # bits per weight printed on the same table: 8.5 (Q8_0), 4.5 (Q4_K)
+    assert 34 * 8 / 32 == 8.5 and 144 * 8 / 256 == 4.5
+    assert orc.block_bytes(99) == -1
+
+
+# ---------------------------------------------------------------------- fp16
+def test_half_decode_exhaustive_vs_numpy(orc):
+    h = np.arange(65536, dtype=np.uint16)
+    ours = orc.half_to_double(h)
+    ref = h.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signs of zeros
+    assert math.copysign(1.0, ours[0x8000]) == -1.0
+
+
+def test_half_encode_sampled_vs_numpy(orc):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[~np.isnan(f)]
+    with np.errstate(over="ignore"):
+        ref = f.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.float_to_half(f), ref)
+    # dense sweep of the range the quantizer uses (fp16 subnormal..normal)
+    g = np.float32(np.linspace(0, 70000, 1_000_003, dtype=np.float64))
+    g = np.concatenate([g, -g, np.float32(np.geomspace(1e-9, 1e-3, 200_000))])
+    with np.errstate(over="ignore"):
+        assert np.array_equal(orc.float_to_half(g), g.astype(np.float16).view(np.uint16))
+
+
+def test_half_encode_closed_forms(orc):
+    f2h = orc.lib().oracle_float_to_half
+    assert f2h(1.0) == 0x3C00
+    assert f2h(65504.0) == 0x7BFF
+    assert f2h(65519.99) == 0x7BFF
+    assert f2h(65520.0) == 0x7C00          # halfway, ties to even -> overflow
+    assert f2h(2.0 ** -24) == 0x0001
+    assert f2h(2.0 ** -25) == 0x0000       # halfway between 0 and 2^-24 -> even (0)
+    assert f2h(3 * 2.0 ** -25) == 0x0002   # halfway between 1 and 2 quanta -> 2
+    assert f2h(1.0 + 2.0 ** -11) == 0x3C00  # halfway -> even
+    assert f2h(1.0 + 3 * 2.0 ** -11) == 0x3C02
+    assert f2h(-0.0) == 0x8000
+
+
+@pytest.mark.timeout(300)
+def test_half_encode_exhaustive_vs_f16c(orc, tmp_path):
+    """All 2^32 fp32 encodings against the host's F16C conversion."""
+    src = os.path.join(os.path.dirname(__file__), "native", "fp16_exhaustive.cpp")
+    exe = tmp_path / "fp16_exhaustive"
+    from oracle import build
+    import subprocess
+    subprocess.run(["g++", "-O2", "-mf16c", "-std=c++17", "-pthread", src, "-o", str(exe),
+                    "-ldl"], check=True)
+    r = subprocess.run([str(exe), build.LIB], capture_output=True, text=True, timeout=280)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches 0" in r.stdout
+
+
+# ------------------------------------------------------- hand-decoded blocks
+@pytest.mark.parametrize("blk", golden_blocks(), ids=lambda b: b["name"])
+def test_golden_block_decodes(orc, blk):
+    t = gs.FORMATS[blk["format"]]
+    if t == gs.Q4_K:
+        raw = np.frombuffer(q4k_golden_bytes(blk), np.uint8)
+        for j in range(8):
+            assert orc.q4k_scale_min(raw[4:16], j) == (blk["sc"][j], blk["m"][j])
+        exp = np.empty(256)
+        for c in range(4):
+            for i in range(32):
+                j0, j1 = 2 * c, 2 * c + 1
+                exp[64 * c + i] = blk["d"] * blk["sc"][j0] * (i % 16) - blk["dmin"] * blk["m"][j0]
+                exp[64 * c + 32 + i] = (blk["d"] * blk["sc"][j1] * (15 - i % 16)
+                                        - blk["dmin"] * blk["m"][j1])
+        assert np.array_equal(orc.dequantize(t, raw, 256), exp)
+        return
+    raw = np.frombuffer(bytes.fromhex(blk["hex"]), np.uint8)
+    got = orc.dequantize(t, raw, 32)
+    if "expected" in blk:
+        assert np.array_equal(got, np.array(blk["expected"], np.float64))
+    else:
+        exp = blk["expected_scale"] * np.array(blk["expected_q"], np.float64)
+        assert np.array_equal(got, exp)
+
+
+# ------------------------------------------------------------- the quantizer
+def test_quantize_zero_block(orc):
+    out = orc.quantize_q8_0(np.zeros((1, 64), np.float32))
+    assert not out.any()
+
+
+def test_quantize_ties_round_to_even(orc):
+    # amax = 127 -> 127/amax = 1 exactly, so each q is rint(x) and d = 1.0
+    x = np.zeros(32, np.float32)
+    x[0] = 127.0
+    x[1:9] = [2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5, 126.5]
+    out = orc.quantize_q8_0(x)[0]
+    assert int(out[0]) | (int(out[1]) << 8) == 0x3C00
+    q = out[2:].view(np.int8)
+    assert list(q[:9]) == [127, 2, 4, -2, -4, 0, 2, 0, 126]
+    assert not q[9:].any()
+
+
+def test_quantize_exact_grid(orc):
+    # x = i (integers), amax 127 -> q = x exactly; d = 1
+    x = np.arange(-15, 17, dtype=np.float32)
+    x[0] = -127.0
+    out = orc.quantize_q8_0(x)[0]
+    assert list(out[2:].view(np.int8)) == list(x.astype(np.int64))
+
+
+def test_quantize_power_of_two_scaling(orc):
+    x = gs.activations(4, 256, cfg=900)
+    base = orc.quantize_q8_0(x)
+    for j in (-6, -1, 1, 5):
+        sc = orc.quantize_q8_0(x * np.float32(2.0 ** j))
+        bq = base.reshape(-1, 34)
+        sq = sc.reshape(-1, 34)
+        assert np.array_equal(sq[:, 2:], bq[:, 2:])
+        d0 = orc.half_to_double(bq[:, :2].copy().view(np.uint16).ravel())
+        d1 = orc.half_to_double(sq[:, :2].copy().view(np.uint16).ravel())
+        assert np.array_equal(d1, d0 * 2.0 ** j)
+
+
+def test_quantize_sign_symmetry(orc):
+    x = gs.activations(3, 128, cfg=901)
+    a = orc.quantize_q8_0(x).reshape(-1, 34)
+    b = orc.quantize_q8_0(-x).reshape(-1, 34)
+    assert np.array_equal(a[:, :2], b[:, :2])
+    assert np.array_equal(a[:, 2:].view(np.int8), -(b[:, 2:].view(np.int8)))
+
+
+def test_quantize_scale_closed_form(orc):
+    # amax = 127 * 2^j gives d = 2^j exactly
+    for j in (-20, -3, 0, 4):
+        x = np.full(32, 0.25 * 2.0 ** j, np.float32)
+        x[7] = -127.0 * 2.0 ** j
+        out = orc.quantize_q8_0(x)[0]
+        d = orc.half_to_double(out[:2].copy().view(np.uint16))[0]
+        assert d == 2.0 ** j
+        assert out[2 + 7].view(np.int8) == -127
+
+
+def test_quantize_spike(orc):
+    x = np.full(32, 1e-3, np.float32)
+    x[5] = 1000.0
+    q = orc.quantize_q8_0(x)[0][2:].view(np.int8)
+    assert q[5] == 127 and not np.delete(q, 5).any()
+
+
+def test_quantize_tiny_amax_overflowing_reciprocal(orc):
+    # 127/amax overflows fp32 -> zeros stay 0, others saturate, d rounds to 0
+    x = np.zeros(32, np.float32)
+    x[3] = 1e-39
+    x[9] = -5e-40
+    out = orc.quantize_q8_0(x)[0]
+    q = out[2:].view(np.int8)
+    assert out[0] == 0 and out[1] == 0
+    assert q[3] == 127 and q[9] == -127
+    assert not np.delete(q, [3, 9]).any()
+
+
+def test_quantize_dequant_error_bound(orc):
+    # |x - d*q| <= d/2 * (1 + tiny) for every element (round to nearest)
+    x = gs.activations(8, 1024, cfg=902)
+    out = orc.quantize_q8_0(x)
+    xh = np.stack([orc.dequantize(gs.Q8_0, out[i], 1024) for i in range(8)])
+    d = orc.half_to_double(out.reshape(-1, 34)[:, :2].copy().view(np.uint16).ravel())
+    dd = np.repeat(d, 32).reshape(8, 1024)
+    # the fp16 scale is within 2^-11 relative of amax/127; quants within 0.5
+    amax = np.abs(x.reshape(-1, 32)).max(axis=1).repeat(32).reshape(8, 1024)
+    assert np.all(np.abs(xh - x) <= 0.5 * dd + 127 * np.abs(dd - amax / 127) + 1e-12)
+
+
+# ------------------------------------------------------- matmul formulations
+def one_hot_rows(k, cols, value=3.0):
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = value if i % 2 == 0 else -value
+    return x
+
+
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K])
+def test_column_extraction(orc, fmt):
+    """One-hot x quantizes to a single +-127 with d = fp16(|c|/127), so y
+    reads one dequantized weight column times 127*d."""
+    n, k = 5, 512
+    w = gs.weights(fmt, n, k, cfg=910)
+    cols = list(range(0, k, 37))
+    x = one_hot_rows(k, cols)
+    xq = orc.quantize_q8_0(x)
+    y, s = orc.matmul(fmt, w, n, k, xq, len(cols))
+    wd = np.stack([orc.dequantize(fmt, w[r], k) for r in range(n)])
+    d = orc.half_to_double(np.array([orc.lib().oracle_float_to_half(np.float32(3.0) / np.float32(127.0))], np.uint16))[0]
+    for i, c in enumerate(cols):
+        sign = 1.0 if i % 2 == 0 else -1.0
+        assert np.array_equal(y[i], sign * 127 * d * wd[:, c])
+        assert np.array_equal(s[i], np.abs(127 * d * wd[:, c]))
+
+
+def test_zero_weights_give_zero(orc):
+    k = 256
+    x = gs.activations(3, k, cfg=911)
+    xq = orc.quantize_q8_0(x)
+    w0 = gs.weights(gs.Q4_0, 4, k, cfg=911)
+    w0.reshape(-1, 18)[:, 2:] = 0x88                  # every q = 8
+    y, _ = orc.matmul(gs.Q4_0, w0, 4, k, xq, 3)
+    assert not y.any()
+    wk = gs.weights(gs.Q4_K, 4, k, cfg=911)
+    wk.reshape(-1, 144)[:, 4:16] = 0                 # all scales and mins 0
+    y, _ = orc.matmul(gs.Q4_K, wk, 4, k, xq, 3)
+    assert not y.any()
+
+
+def test_constant_q8_0_closed_form(orc):
+    k = 1024
+    w = np.zeros((2, k // 32, 34), np.uint8)
+    w[:, :, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    w[:, :, 2:] = 1
+    xq = orc.quantize_q8_0(np.ones((1, k), np.float32))
+    y, s = orc.matmul(gs.Q8_0, w.reshape(2, -1), 2, k, xq, 1)
+    d = float(np.float16(np.float32(1.0) / np.float32(127.0)))
+    assert np.all(y == k * 127 * d) and np.all(s == k * 127 * d)
+
+
+def test_cross_format_identities(orc):
+    """Q4_0(d, q) == Q8_0(d, q-8) == Q4_1(d, -8d, q) exactly."""
+    n, k = 6, 512
+    w40 = gs.weights(gs.Q4_0, n, k, cfg=912).reshape(-1, 18)
+    nb = w40.shape[0]
+    w80 = np.zeros((nb, 34), np.uint8)
+    w41 = np.zeros((nb, 20), np.uint8)
+    w80[:, :2] = w40[:, :2]
+    lo = (w40[:, 2:] & 0x0F).astype(np.int16) - 8
+    hi = (w40[:, 2:] >> 4).astype(np.int16) - 8
+    w80[:, 2:18] = lo.astype(np.int8).view(np.uint8)
+    w80[:, 18:34] = hi.astype(np.int8).view(np.uint8)
+    d = w40[:, :2].copy().view(np.float16).ravel()
+    w41[:, :2] = w40[:, :2]
+    w41[:, 2:4] = (-8 * d.astype(np.float32)).astype(np.float16).view(np.uint8).reshape(-1, 2)
+    w41[:, 4:] = w40[:, 2:]
+    xq = orc.quantize_q8_0(gs.activations(3, k, cfg=912))
+    y0, _ = orc.matmul(gs.Q4_0, w40.reshape(n, -1), n, k, xq, 3)
+    y8, _ = orc.matmul(gs.Q8_0, w80.reshape(n, -1), n, k, xq, 3)
+    y1, _ = orc.matmul(gs.Q4_1, w41.reshape(n, -1), n, k, xq, 3)
+    assert np.array_equal(y0, y8) and np.array_equal(y0, y1)
+
+
+def test_q4k_subblock_equals_q4_1(orc):
+    """A Q4_K sub-block with d*sc and dmin*m exact in fp16 equals the Q4_1
+    block (d*sc, -dmin*m) over the same nibbles."""
+    k = 256
+    wk = gs.weights(gs.Q4_K, 3, k, cfg=913).reshape(-1, 144)
+    wk[:, 0:2] = np.frombuffer(np.float16(2.0 ** -8).tobytes(), np.uint8)
+    wk[:, 2:4] = np.frombuffer(np.float16(2.0 ** -9).tobytes(), np.uint8)
+    w41 = np.zeros((wk.shape[0] * 8, 20), np.uint8).reshape(-1, 8, 20)
+    for r in range(wk.shape[0]):
+        for j in range(8):
+            sc, mn = orc.q4k_scale_min(wk[r, 4:16], j)
+            c = j // 2
+            q = (wk[r, 16 + 32 * c: 48 + 32 * c] & 0x0F) if j % 2 == 0 else (wk[r, 16 + 32 * c: 48 + 32 * c] >> 4)
+            w41[r, j, 0:2] = np.frombuffer(np.float16(2.0 ** -8 * sc).tobytes(), np.uint8)
+            w41[r, j, 2:4] = np.frombuffer(np.float16(-(2.0 ** -9) * mn).tobytes(), np.uint8)
+            w41[r, j, 4:] = q[:16] | (q[16:] << 4)
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=913))
+    yk, _ = orc.matmul(gs.Q4_K, wk.reshape(3, -1), 3, k, xq, 2)
+    y1, _ = orc.matmul(gs.Q4_1, w41.reshape(3, -1), 3, k, xq, 2)
+    assert np.array_equal(yk, y1)
+
+
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K])
+def test_two_formulations_agree(orc, fmt):
+    n, m, k = 33, 5, 1024
+    w = gs.weights(fmt, n, k, cfg=914)
+    xq = orc.quantize_q8_0(gs.activations(m, k, cfg=914))
+    y, s = orc.matmul(fmt, w, n, k, xq, m)
+    yf = orc.matmul_factored(fmt, w, n, k, xq, m)
+    assert np.all(np.abs(y - yf) <= 1e-14 * s)
+    # sampled variant agrees exactly with the full product
+    ai = np.array([0, 4, 2, 1, 3]); ri = np.array([0, 32, 17, 5, 31])
+    ys, ss = orc.matmul_sampled(fmt, w, n, k, xq, m, ai, ri)
+    assert np.array_equal(ys, y[ai, ri]) and np.array_equal(ss, s[ai, ri])
+
+
+@pytest.mark.parametrize("fmt,k", [(gs.Q4_0, 32), (gs.Q4_1, 64), (gs.Q8_0, 96), (gs.Q4_K, 256),
+                                   (gs.Q4_K, 512)])
+def test_exact_rational_brute_force(orc, fmt, k):
+    """Tiny shapes in exact rational arithmetic: the fp64 sums must agree
+    with the exact value to within the fp64 summation bound."""
+    n, m = 3, 2
+    w = gs.weights(fmt, n, k, cfg=915)
+    xq = orc.quantize_q8_0(gs.activations(m, k, cfg=915))
+    y, s = orc.matmul(fmt, w, n, k, xq, m)
+    wd = [[Fraction(v) for v in orc.dequantize(fmt, w[r], k)] for r in range(n)]
+    xd = [[Fraction(v) for v in orc.dequantize(gs.Q8_0, xq[i], k)] for i in range(m)]
+    for i in range(m):
+        for r in range(n):
+            exact = sum(a * b for a, b in zip(wd[r], xd[i]))
+            mag = sum(abs(a * b) for a, b in zip(wd[r], xd[i]))
+            assert abs(Fraction(y[i, r]) - exact) <= Fraction(k) * Fraction(2.0 ** -53) * mag
+            assert Fraction(s[i, r]) == pytest.approx(mag, rel=1e-15) or abs(Fraction(s[i, r]) - mag) <= Fraction(k) * Fraction(2.0 ** -53) * mag
+
+
+def test_dequantize_matches_library_matmul(orc):
+    """y = W_hat @ X_hat^T computed with numpy's matmul on the decoded values."""
+    fmt, n, m, k = gs.Q4_K, 7, 3, 512
+    w = gs.weights(fmt, n, k, cfg=916)
+    xq = orc.quantize_q8_0(gs.activations(m, k, cfg=916))
+    y, s = orc.matmul(fmt, w, n, k, xq, m)
+    wd = np.stack([orc.dequantize(fmt, w[r], k) for r in range(n)])
+    xd = np.stack([orc.dequantize(gs.Q8_0, xq[i], k) for i in range(m)])
+    assert np.allclose(y, xd @ wd.T, rtol=0, atol=1e-13 * s.max())
+    assert np.allclose(s, np.abs(xd) @ np.abs(wd).T, rtol=1e-13)
+
+
+# ------------------------------------------------------------------- SwiGLU
+def test_swiglu_closed_forms(orc):
+    g = np.array([0.0, 100.0, -100.0, math.log(3.0), 1.0], np.float32)
+    u = np.array([5.0, 0.5, 2.0, 1.0, -3.0], np.float32)
+    h = orc.swiglu(g, u)
+    assert h[0] == 0.0
+    assert h[1] == np.float32(50.0)
+    assert abs(h[2]) < 1e-40
+    z = float(np.float32(math.log(3.0)))
+    assert h[3] == np.float32(z / (1 + math.exp(-z)))
+    assert abs(float(h[3]) - 0.75 * math.log(3.0)) < 1e-6
+    sig1 = 1.0 / (1.0 + math.exp(-1.0))
+    assert h[4] == np.float32(-3.0 * sig1)
+
+
+def test_swiglu_odd_part_identity(orc):
+    """silu(z) - silu(-z) = z."""
+    g = gs.activations(1, 4096, cfg=917).ravel() * np.float32(4)
+    one = np.ones_like(g)
+    d = orc.swiglu(g, one).astype(np.float64) - orc.swiglu(-g, one).astype(np.float64)
+    assert np.all(np.abs(d - g) <= 2 * np.abs(g) * 2.0 ** -23 + 1e-30)
+
+
+# ---------------------------------------------------------------------- MoE
+def test_moe_group_vs_stable_argsort(orc):
+    ids, _ = gs.routing(256, 32, 4, cfg=920)
+    offs, pairs = orc.moe_group(ids, 32)
+    flat = ids.ravel()
+    assert np.array_equal(pairs, np.argsort(flat, kind="stable"))
+    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=32))]))
+
+
+def test_moe_group_rejects_bad_id(orc):
+    ids = np.zeros((2, 2), np.int32)
+    ids[1, 1] = 32
+    with pytest.raises(ValueError):
+        orc.moe_group(ids, 32)
+
+
+def test_moe_reduces_to_dense(orc):
+    """All tokens routed to the same experts: each slot is a dense matmul."""
+    fmt, E, n, k, T, K = gs.Q4_K, 4, 16, 256, 5, 2
+    w = gs.expert_weights(fmt, E, n, k, cfg=921, which=0)
+    xq = orc.quantize_q8_0(gs.activations(T, k, cfg=921))
+    ids = np.tile(np.array([[2, 0]], np.int32), (T, 1))
+    y, s = orc.moe_matmul(fmt, w, E, n, k, xq, False, ids)
+    rb = k // 256 * 144
+    for slot, e in enumerate([2, 0]):
+        yd, sd = orc.matmul(fmt, w[e * n:(e + 1) * n], n, k, xq, T)
+        assert np.array_equal(y[slot::K], yd) and np.array_equal(s[slot::K], sd)
+    assert rb == w.shape[1]
+
+
+def test_moe_combine_vs_numpy(orc):
+    rng = np.random.default_rng(3)
+    T, K, n = 6, 4, 10
+    d = rng.standard_normal((T * K, n))
+    _, rw = gs.routing(T, 32, K, cfg=922)
+    y, s = orc.moe_combine(d, np.abs(d), rw)
+    ref = np.einsum("tk,tkn->tn", rw.astype(np.float64), d.reshape(T, K, n))
+    assert np.allclose(y, ref, rtol=1e-15, atol=1e-15)
+    assert np.allclose(s, np.einsum("tk,tkn->tn", np.abs(rw.astype(np.float64)),
+                                    np.abs(d).reshape(T, K, n)), rtol=1e-15)
