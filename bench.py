@@ -1,0 +1,175 @@
+"""Benchmark of the block-quantized decode GEMV on one MI355X.
+
+Workload (one step): the 8B-class FFN-up projection 14336 x 4096 in GGUF
+Q8_0 and in Q4_1; activations fp32 N(0,1), 5 rows (1 decode row + 4
+speculative-verify rows).  A step quantizes the 5 activation rows to Q8_0 and
+runs the GEMV over each weight format at batch 1 and at batch 5 (4 GEMVs).
+Weights are resident in HBM before timing; every GEMV reads a different copy
+of its weights (>= 512 MB of copies per format) so no launch is served from
+the 256 MB Infinity Cache.
+
+Printed: one JSON line.  value = weight bytes streamed per step / step time
+(GB/s).  roofline: the Q8_0 batch-5 GEMV (the largest launch), algorithmic
+bytes (weights + activation blocks + outputs) over its average duration from
+HIP events recorded around each of its launches on the launch stream.
+cpu_baseline: the CPU oracle on the same step (fp64 reference, not a tuned
+CPU kernel).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gguf_synth as gs
+    import quantized_gguf_block_amd as cq
+
+    cq.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    n, k, B = 14336, 4096, 5
+    fmts = [gs.Q8_0, gs.Q4_1]
+    cfg_id = {gs.Q8_0: 1, gs.Q4_1: 11}
+    host_w = {f: gs.weights(f, n, k, cfg=cfg_id[f]) for f in fmts}
+    x = gs.activations(B, k, cfg=1)
+    wbytes = {f: host_w[f].nbytes for f in fmts}
+    copies = {}
+    for f in fmts:
+        base = torch.from_numpy(host_w[f]).to(dev)
+        ncopy = max(2, -(-512 * 2**20 // wbytes[f]) + 1)
+        copies[f] = [base] + [base.clone() for _ in range(ncopy - 1)]
+    xd = torch.from_numpy(x).to(dev)
+    xq = torch.empty((B, k // 32 * 34), dtype=torch.uint8, device=dev)
+    y = torch.empty((B, n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    counter = {f: 0 for f in fmts}
+    ev_pairs = []
+
+    def gemv(f, batch, record):
+        w = copies[f][counter[f] % len(copies[f])]
+        counter[f] += 1
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        cq.cq_gemv(f, w, n, k, xq, batch, y=y)
+        if record:
+            e1.record(stream)
+            ev_pairs.append((e0, e1))
+
+    def step(record=False):
+        cq.cq_quantize_q8_0(xd, xq)
+        gemv(gs.Q8_0, 1, False)
+        gemv(gs.Q8_0, B, record)
+        gemv(gs.Q4_1, 1, False)
+        gemv(gs.Q4_1, B, False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step(record=True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    step_bytes = 2 * sum(wbytes.values())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: Q8_0 batch-5 GEMV
+    durs = [a.elapsed_time(b) for a, b in ev_pairs]
+    avg_ms = float(np.mean(durs))
+    alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
+    achieved = alg / (avg_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host_w, x, n, k, B, args.cpu_seconds)
+
+    out = {
+        "metric": "decode GEMV weight GB/s (% HBM peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 dot4 + fp32 scale (Q8_0/Q4_1 weights, Q8_0 activations)",
+        "data": "synthetic",
+        "config": {"workload": "FFN-up decode GEMV 14336x4096, GGUF Q8_0 and Q4_1, "
+                               "batch 1 and 5, activations quantized to Q8_0 each step",
+                   "n": n, "k": k, "batches": [1, B], "formats": ["q8_0", "q4_1"],
+                   "weight_copies": {gs.NAMES[f]: len(copies[f]) for f in fmts}},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<Q8_0, B=5>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": alg},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(host_w, x, n, k, B, seconds):
+    """The CPU oracle on the same step (quantize + the four GEMVs), repeated
+    for about `seconds`; GB/s of weights streamed."""
+    import oracle
+    import gguf_synth as gs
+    threads = oracle.default_threads()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        xq = oracle.quantize_q8_0(x)
+        for f in (gs.Q8_0, gs.Q4_1):
+            oracle.matmul(f, host_w[f], n, k, xq[:1], 1, n_threads=threads, want_s=False)
+            oracle.matmul(f, host_w[f], n, k, xq, B, n_threads=threads, want_s=False)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    step_bytes = 2 * sum(w.nbytes for w in host_w.values())
+    return {"value": round(step_bytes * steps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full steps (quantize + Q8_0/Q4_1 GEMV at batch 1 and 5), "
+                      f"{el:.1f} s, fp64 oracle with {threads} threads"}
+
+
+if __name__ == "__main__":
+    main()

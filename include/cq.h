@@ -1,0 +1,209 @@
+/*
+ * cq.h -- C ABI of libcq: block-quantized GGUF weight x activation matmul
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *   - Weights stay in GGUF block form as stored: Q4_0, Q4_1, Q8_0, Q4_K
+ *     (Cera README, "Quantization"; alice-llm 2.0.0 README, "Quantization
+ *     Block Specs").  The LM head runs on the weight as stored, not on a
+ *     dequantized copy (Cera README, "Performance").
+ *   - Activations are quantized on the fly to Q8_0 blocks of 32 (Cera
+ *     README, "Quantization"; alice-llm 2.0.0 README, "The CPU Optimization
+ *     Journey", Phase 4).
+ *   - Each output is an integer dot inside every 32-value block with the
+ *     scales applied once per block (alice-llm 2.0.0 README, "Computation
+ *     Path (Q4_K)").
+ *   - Decode GEMV for 1..8 activation rows: the batched LM-head verify of
+ *     speculative decoding reads the weights once for all 1+k rows (cera
+ *     0.5.3 README, "Speculative decoding"; alice-llm 2.0.0 README,
+ *     "Batch-4 Speculative Decoding").
+ *   - Batched prefill GEMM (Cera README, "Supported models").
+ *   - lfm2moe-style routed expert FFN with tokens grouped by expert so that
+ *     each expert's weights are read once per chunk (Cera README,
+ *     "Supported models", which names grouping as the follow-up), SwiGLU
+ *     between the projections (alice-llm 2.0.0 README, "The GPU
+ *     Optimization Journey", phase 4).
+ *
+ * Block layouts (little-endian fp16 fields):
+ *   Q4_0  32 values, 18 B: d, 16 bytes; byte i = element i (low nibble) and
+ *         element i+16 (high nibble); value d*(q-8).
+ *   Q4_1  32 values, 20 B: d, m, 16 bytes as Q4_0; value d*q + m.
+ *   Q8_0  32 values, 34 B: d, 32 int8; value d*q.
+ *   Q4_K  256 values, 144 B: d, dmin, 12 bytes of six-bit sub-block scales
+ *         and mins, 128 bytes of nibbles (32-byte chunk c: low nibbles =
+ *         sub-block 2c, high nibbles = sub-block 2c+1); value d*sc*q - dmin*m.
+ *   A weight matrix [n][k] is n rows of k/qk consecutive blocks, row-major,
+ *   no padding.  MoE expert weights are n_experts such matrices back to back.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  They must stay valid until the
+ *     stream reaches the call.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream), performs no host synchronization, and keeps no
+ *     state between calls apart from a read-only per-device property cache.
+ *     Calls are thread-safe.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns a negative cq_status and launches nothing.  Faults
+ *     raised by the GPU surface at the caller's next synchronization.
+ *   - Sizes of zero (n, rows, m, n_tokens) are valid and launch nothing.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on every run (no floating-point atomics).
+ */
+#ifndef CQ_H
+#define CQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t (HIP declares hipStream_t as this same pointer type). */
+typedef struct ihipStream_t* cq_stream_t;
+
+/* Status codes: append-only, never renumbered. */
+typedef enum {
+    CQ_OK = 0,
+    CQ_ERR_INVALID_ARG = -1,      /* null pointer, negative size, bad flag   */
+    CQ_ERR_UNSUPPORTED_TYPE = -2, /* weight type other than the four below   */
+    CQ_ERR_SHAPE = -3,            /* k not a multiple of the block, too big  */
+    CQ_ERR_ALIGNMENT = -4,        /* pointer or leading dim misaligned       */
+    CQ_ERR_WORKSPACE = -5,        /* reserved                                */
+    CQ_ERR_HIP = -6,              /* a HIP runtime call failed               */
+    CQ_ERR_NO_DEVICE = -7         /* no gfx950 device current                */
+} cq_status;
+
+/* Weight types, numbered as the GGUF tensor type ids. */
+typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12 } cq_type;
+
+#define CQ_ABI_VERSION 1
+#define CQ_GEMV_MAX_BATCH 8
+#define CQ_MAX_K 65536
+
+int cq_abi_version(void);
+/* Static, never-null string naming a status code. */
+const char* cq_status_string(int status);
+/* Values per block, bytes per block, bytes per row of k values; -1 for an
+ * unknown type or a k that is not a whole number of blocks. */
+int64_t cq_block_elems(int type);
+int64_t cq_block_bytes(int type);
+int64_t cq_row_bytes(int type, int64_t k);
+
+/*
+ * cq_quantize_q8_0 -- dynamic activation quantization to Q8_0.
+ * (alice-llm 2.0.0 README, "The CPU Optimization Journey", Phase 4: block
+ * amax, scale 127/amax, multiply, round to nearest even, saturate.)
+ *
+ * For each row r < rows and each block b < k/32 of the 32 fp32 values
+ * x[r*ldx + 32b .. +31]:
+ *     amax = max |x_i|;  id = 127.0f / amax;  q_i = rne(x_i * id) clamped to
+ *     [-127, 127] (a zero x_i gives 0 even if id overflows);
+ *     d = fp16_rne(amax / 127.0f); block = d (2 B LE) then q_0..q_31.
+ * All arithmetic is single IEEE fp32 operations, so the bytes are exact and
+ * reproducible on any IEEE machine.
+ *   x    fp32 [rows][ldx], 16-byte aligned, ldx % 4 == 0, ldx >= k.
+ *   xq   out: rows*(k/32) blocks of 34 bytes, contiguous, 2-byte aligned.
+ *   k    multiple of 32, k <= CQ_MAX_K.
+ * Inputs with NaN or Inf are outside the contract.
+ */
+int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k,
+                     void* xq, cq_stream_t stream);
+
+/*
+ * cq_gemv -- decode GEMV for 1..8 activation rows (speculative verify
+ * rows included): y[b*ldy + i] = sum_j w_hat[i][j] * x_hat[b][j].
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   w      [n][k/qk] blocks, 16-byte aligned.
+ *   xq     [batch][k/32] Q8_0 blocks (as written by cq_quantize_q8_0),
+ *          2-byte aligned.
+ *   batch  1..CQ_GEMV_MAX_BATCH.
+ *   y      fp32, row b at y + b*ldy, ldy >= n, 4-byte aligned.
+ *   k      multiple of 32 (of 256 for Q4_K), k <= CQ_MAX_K.
+ * Each row b of a batched call is bitwise equal to the batch-1 call on that
+ * row alone.  Accuracy: |y - y_exact| <= 2e-5 * sum_j |w_hat*x_hat|.
+ */
+int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
+            const void* xq, int64_t batch, float* y, int64_t ldy,
+            cq_stream_t stream);
+
+/*
+ * cq_gemm -- prefill GEMM over m activation rows:
+ *     y[r*ldy + i] = sum_j w_hat[i][j] * x_hat[r][j]
+ * computed as int8 MFMA products of each 32-value block with the two block
+ * scales applied per block in fp32.
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   w      [n][k/qk] blocks, 16-byte aligned; xq [m][k/32] Q8_0 blocks,
+ *          2-byte aligned; y fp32 [m][ldy], ldy >= n, 4-byte aligned.
+ *   k      multiple of 256, k <= CQ_MAX_K.
+ * Accuracy as cq_gemv.
+ */
+int cq_gemm(int wt, const void* w, int64_t n, int64_t k,
+            const void* xq, int64_t m, float* y, int64_t ldy,
+            cq_stream_t stream);
+
+/*
+ * cq_moe_group -- group the (token, slot) pairs of a top-k routing table by
+ * expert (stable counting sort; Cera README, "Supported models": grouping
+ * tokens by expert so an expert's weights are read once per chunk).
+ *   expert_ids  int32 [n_tokens][top_k], each in [0, n_experts).
+ *   offsets     out int32 [n_experts + 1]: pairs of expert e are
+ *               pairs[offsets[e] .. offsets[e+1]).
+ *   pairs       out int32 [n_tokens*top_k]: pair ids p = t*top_k + s,
+ *               ascending within each expert.
+ *   n_experts <= 1024, top_k <= n_experts, n_tokens*top_k <= 2^24.
+ * Ids outside [0, n_experts) are not checked on the host (they live on the
+ * device); the kernel drops such pairs and offsets[n_experts] then falls
+ * short of n_tokens*top_k, which the caller can check.
+ */
+int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
+                 int64_t n_experts, int32_t* offsets, int32_t* pairs,
+                 cq_stream_t stream);
+
+/*
+ * cq_moe_gemm -- grouped expert projection.  For every expert e and every
+ * pair p in pairs[offsets[e] .. offsets[e+1]):
+ *     y[p*ldy + i] = sum_j W_e_hat[i][j] * x_hat[row][j],  i < n,
+ * where row = p / top_k (x_per_pair = 0: gate/up read the token row) or
+ * row = p (x_per_pair = 1: down reads the pair row).  Each expert's weight
+ * matrix is streamed once for all of its pairs.
+ *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   w_experts  n_experts matrices [n][k/qk], back to back, 16-B aligned.
+ *   xq         Q8_0 rows of k/32 blocks (n_tokens or n_tokens*top_k rows).
+ *   offsets, pairs  as written by cq_moe_group.
+ *   y          fp32 [n_tokens*top_k][ldy], ldy >= n.
+ *   k multiple of 256, k <= CQ_MAX_K.  Accuracy as cq_gemv.
+ */
+int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int x_per_pair, const int32_t* offsets,
+                const int32_t* pairs, int64_t n_tokens, int64_t top_k,
+                float* y, int64_t ldy, cq_stream_t stream);
+
+/*
+ * cq_swiglu_quantize_q8_0 -- h = silu(g) * u with silu(z) = z/(1+exp(-z))
+ * (alice-llm 2.0.0 README, "The GPU Optimization Journey", phase 4: fused
+ * gate/up SwiGLU), evaluated in fp64 from the fp32 inputs and rounded once
+ * to fp32, then quantized to Q8_0 exactly as cq_quantize_q8_0.
+ *   g, u   fp32 [rows][ld], 16-byte aligned, ld % 4 == 0, ld >= k.
+ *   h_opt  optional fp32 [rows][k] output of h (NULL to skip).
+ *   hq     out: rows*(k/32) Q8_0 blocks.
+ */
+int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld,
+                            int64_t rows, int64_t k, float* h_opt, void* hq,
+                            cq_stream_t stream);
+
+/*
+ * cq_moe_combine -- y[t*ldy + i] = sum over s = 0..top_k-1, in slot order,
+ * of route_w[t*top_k + s] * d[(t*top_k + s)*n + i], fp32.
+ *   d  fp32 [n_tokens*top_k][n] (as written by cq_moe_gemm with ldy = n).
+ */
+int cq_moe_combine(const float* d, const float* route_w, int64_t n_tokens,
+                   int64_t top_k, int64_t n, float* y, int64_t ldy,
+                   cq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CQ_H */

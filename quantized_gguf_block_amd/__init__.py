@@ -1,0 +1,213 @@
+"""Python binding of libcq, the MI355X block-quantized GGUF matmul.
+
+Thin ctypes marshalling over the C ABI declared in include/cq.h: each
+function here has the name of the C entry point it calls, turns torch device
+tensors into pointers and sizes, passes torch's current HIP stream, and
+raises CQError on a non-zero status.  All computation happens in the HIP
+kernels of libcq.so; there is no fallback path.  Output tensors that the
+caller does not supply are allocated here with torch (the library itself
+never allocates).
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcq.so")
+
+Q4_0, Q4_1, Q8_0, Q4_K = 2, 3, 8, 12
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144}
+GEMV_MAX_BATCH = 8
+
+STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",
+          -3: "CQ_ERR_SHAPE", -4: "CQ_ERR_ALIGNMENT", -5: "CQ_ERR_WORKSPACE",
+          -6: "CQ_ERR_HIP", -7: "CQ_ERR_NO_DEVICE"}
+
+EXPORTS = [
+    "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
+    "cq_quantize_q8_0", "cq_gemv", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
+    "cq_swiglu_quantize_q8_0", "cq_moe_combine",
+]
+
+
+class CQError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libcq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(or python -m quantized_gguf_block_amd.build)")
+    # torch ships its own HIP runtime, linked under the unversioned name
+    # libamdhip64.so.  Loading torch first makes libcq's libamdhip64.so.7
+    # dependency bind to that same, already loaded runtime (by soname), so
+    # pointers, streams and the current device are shared.  Loading libcq
+    # first would put a second HIP runtime into the process.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "cq_abi_version": (I, []),
+        "cq_status_string": (ctypes.c_char_p, [I]),
+        "cq_block_elems": (I64, [I]),
+        "cq_block_bytes": (I64, [I]),
+        "cq_row_bytes": (I64, [I, I64]),
+        "cq_quantize_q8_0": (I, [P, I64, I64, I64, P, P]),
+        "cq_gemv": (I, [I, P, I64, I64, P, I64, P, I64, P]),
+        "cq_gemm": (I, [I, P, I64, I64, P, I64, P, I64, P]),
+        "cq_moe_group": (I, [P, I64, I64, I64, P, P, P]),
+        "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
+        "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, I64, P, P, P]),
+        "cq_moe_combine": (I, [P, P, I64, I64, I64, P, I64, P]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(fn, rc):
+    if rc != 0:
+        msg = load().cq_status_string(rc).decode()
+        raise CQError(fn, rc, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def row_bytes(wt, k):
+    return k // BLOCK_ELEMS[wt] * BLOCK_BYTES[wt]
+
+
+def cq_quantize_q8_0(x, xq=None, stream=None):
+    """x: fp32 [rows][k] (rows may be strided, elements contiguous) ->
+    uint8 [rows][k/32*34] Q8_0 blocks."""
+    import torch
+    _dev_tensor(x, "x", torch.float32)
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    rows, k = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if xq is None:
+        xq = torch.empty((rows, k // 32 * 34), dtype=torch.uint8, device=x.device)
+    _dev_tensor(xq, "xq", torch.uint8)
+    _check("cq_quantize_q8_0", load().cq_quantize_q8_0(
+        _ptr(x), x.stride(0) if rows > 1 else k, rows, k, _ptr(xq), _stream(stream)))
+    return xq
+
+
+def cq_gemv(wt, w, n, k, xq, batch, y=None, ldy=None, stream=None):
+    """y[b][i] = sum_j w_hat[i][j] x_hat[b][j] for b < batch (1..8)."""
+    import torch
+    _dev_tensor(w, "w", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    if y is None:
+        y = torch.empty((batch, n), dtype=torch.float32, device=w.device)
+    _dev_tensor(y, "y", torch.float32)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    _check("cq_gemv", load().cq_gemv(wt, _ptr(w), n, k, _ptr(xq), batch, _ptr(y), ldy,
+                                      _stream(stream)))
+    return y
+
+
+def cq_gemm(wt, w, n, k, xq, m, y=None, ldy=None, stream=None):
+    """y[r][i] = sum_j w_hat[i][j] x_hat[r][j] for r < m (int8 MFMA)."""
+    import torch
+    _dev_tensor(w, "w", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _dev_tensor(y, "y", torch.float32)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    _check("cq_gemm", load().cq_gemm(wt, _ptr(w), n, k, _ptr(xq), m, _ptr(y), ldy,
+                                      _stream(stream)))
+    return y
+
+
+def cq_moe_group(expert_ids, n_experts, offsets=None, pairs=None, stream=None):
+    """expert_ids: int32 [n_tokens][top_k] -> (offsets int32 [E+1], pairs int32 [T*k])."""
+    import torch
+    _dev_tensor(expert_ids, "expert_ids", torch.int32)
+    n_tokens, top_k = expert_ids.shape
+    dev = expert_ids.device
+    if offsets is None:
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    if pairs is None:
+        pairs = torch.empty(max(n_tokens * top_k, 1), dtype=torch.int32, device=dev)
+    _check("cq_moe_group", load().cq_moe_group(_ptr(expert_ids), n_tokens, top_k, n_experts,
+                                                _ptr(offsets), _ptr(pairs), _stream(stream)))
+    return offsets, pairs
+
+
+def cq_moe_gemm(wt, w_experts, n_experts, n, k, xq, x_per_pair, offsets, pairs, n_tokens,
+                top_k, y=None, ldy=None, stream=None):
+    """Grouped expert projection -> y fp32 [n_tokens*top_k][n], row = pair id."""
+    import torch
+    _dev_tensor(w_experts, "w_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    if y is None:
+        y = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_experts.device)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    _check("cq_moe_gemm", load().cq_moe_gemm(
+        wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), int(bool(x_per_pair)), _ptr(offsets),
+        _ptr(pairs), n_tokens, top_k, _ptr(y), ldy, _stream(stream)))
+    return y
+
+
+def cq_swiglu_quantize_q8_0(g, u, h=None, want_h=False, hq=None, stream=None):
+    """h = silu(g)*u (fp64 inside, fp32 out), quantized to Q8_0 -> (h or None, hq)."""
+    import torch
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(u, "u", torch.float32)
+    rows, k = g.shape
+    if u.shape != g.shape or u.stride() != g.stride() or g.stride(1) != 1:
+        raise ValueError("g and u must have the same shape and row stride")
+    if h is None and want_h:
+        h = torch.empty((rows, k), dtype=torch.float32, device=g.device)
+    if hq is None:
+        hq = torch.empty((rows, k // 32 * 34), dtype=torch.uint8, device=g.device)
+    _check("cq_swiglu_quantize_q8_0", load().cq_swiglu_quantize_q8_0(
+        _ptr(g), _ptr(u), g.stride(0) if rows > 1 else k, rows, k, _ptr(h), _ptr(hq),
+        _stream(stream)))
+    return h, hq
+
+
+def cq_moe_combine(d, route_w, y=None, stream=None):
+    """y[t] = sum_s route_w[t][s] * d[t*top_k + s] (slot order, fp32)."""
+    import torch
+    _dev_tensor(d, "d", torch.float32)
+    _dev_tensor(route_w, "route_w", torch.float32)
+    n_tokens, top_k = route_w.shape
+    n = d.shape[1]
+    if y is None:
+        y = torch.empty((n_tokens, n), dtype=torch.float32, device=d.device)
+    _check("cq_moe_combine", load().cq_moe_combine(_ptr(d), _ptr(route_w), n_tokens, top_k, n,
+                                                    _ptr(y), y.stride(0), _stream(stream)))
+    return y

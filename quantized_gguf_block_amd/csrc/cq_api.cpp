@@ -1,0 +1,198 @@
+// cq_api.cpp -- the extern "C" entry points declared in include/cq.h.
+//
+// Every argument is validated here, on the host, before any HIP call; an
+// invalid call returns its cq_status without touching the device.  Valid
+// calls go to the launchers in cq_internal.h, which enqueue kernels on the
+// caller's stream and return at once.
+#include "../../include/cq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "cq_internal.h"
+
+namespace cq {
+
+int gemv_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
+int gemm_shape_ok(int wt, int64_t k);                  // gemm.hip
+int moe_shape_ok(int wt, int64_t n, int64_t k);        // moe.hip
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int64_t elems(int t) {
+    switch (t) {
+        case CQ_Q4_0: case CQ_Q4_1: case CQ_Q8_0: return 32;
+        case CQ_Q4_K: return 256;
+        default: return -1;
+    }
+}
+int64_t bytes(int t) {
+    switch (t) {
+        case CQ_Q4_0: return 18;
+        case CQ_Q4_1: return 20;
+        case CQ_Q8_0: return 34;
+        case CQ_Q4_K: return 144;
+        default: return -1;
+    }
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Common checks for a weight operand: type, k, pointer alignment.
+int check_weights(int wt, const void* w, int64_t n, int64_t k) {
+    if (elems(wt) < 0) return CQ_ERR_UNSUPPORTED_TYPE;
+    if (n < 0 || k <= 0) return CQ_ERR_INVALID_ARG;
+    if (k % elems(wt) != 0 || k % 32 != 0 || k > CQ_MAX_K) return CQ_ERR_SHAPE;
+    if (n > 0 && !w) return CQ_ERR_INVALID_ARG;
+    if (!aligned(w, 16)) return CQ_ERR_ALIGNMENT;
+    return CQ_OK;
+}
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CQ_ERR_NO_DEVICE;
+    return CQ_OK;
+}
+
+int status_of(int rc) { return rc == 0 ? CQ_OK : rc; }
+
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+}  // namespace cq
+
+using namespace cq;
+
+extern "C" {
+
+int cq_abi_version(void) { return CQ_ABI_VERSION; }
+
+const char* cq_status_string(int status) {
+    switch (status) {
+        case CQ_OK: return "CQ_OK";
+        case CQ_ERR_INVALID_ARG: return "CQ_ERR_INVALID_ARG: null pointer, negative size or bad flag";
+        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type is not Q4_0, Q4_1, Q8_0 or Q4_K";
+        case CQ_ERR_SHAPE: return "CQ_ERR_SHAPE: k is not a whole number of blocks or exceeds the kernel's limit";
+        case CQ_ERR_ALIGNMENT: return "CQ_ERR_ALIGNMENT: pointer or leading dimension misaligned";
+        case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE";
+        case CQ_ERR_HIP: return "CQ_ERR_HIP: a HIP runtime call failed";
+        case CQ_ERR_NO_DEVICE: return "CQ_ERR_NO_DEVICE: no HIP device is current";
+        default: return "unknown cq status";
+    }
+}
+
+int64_t cq_block_elems(int type) { return elems(type); }
+int64_t cq_block_bytes(int type) { return bytes(type); }
+int64_t cq_row_bytes(int type, int64_t k) {
+    if (elems(type) < 0 || k < 0 || k % elems(type) != 0) return -1;
+    return k / elems(type) * bytes(type);
+}
+
+int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k, void* xq,
+                     cq_stream_t stream) {
+    if (rows < 0 || k <= 0 || ldx < k) return CQ_ERR_INVALID_ARG;
+    if (k % 32 != 0 || k > CQ_MAX_K) return CQ_ERR_SHAPE;
+    if (rows == 0) return CQ_OK;
+    if (!x || !xq) return CQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(xq, 2)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_quantize_q8_0(x, ldx, rows, k, xq, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
+            float* y, int64_t ldy, cq_stream_t stream) {
+    if (int rc = check_weights(wt, w, n, k)) return rc;
+    if (batch < 1 || batch > CQ_GEMV_MAX_BATCH || ldy < n) return CQ_ERR_INVALID_ARG;
+    if (gemv_shape_ok(wt, k, batch) != 0) return CQ_ERR_SHAPE;
+    if (n == 0) return CQ_OK;
+    if (!xq || !y) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_gemv(wt, w, n, k, xq, batch, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,
+            int64_t ldy, cq_stream_t stream) {
+    if (int rc = check_weights(wt, w, n, k)) return rc;
+    if (m < 0 || ldy < n) return CQ_ERR_INVALID_ARG;
+    if (k % 256 != 0 || gemm_shape_ok(wt, k) != 0) return CQ_ERR_SHAPE;
+    if (n == 0 || m == 0) return CQ_OK;
+    if (!xq || !y) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_gemm(wt, w, n, k, xq, m, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                 int32_t* offsets, int32_t* pairs, cq_stream_t stream) {
+    if (n_tokens < 0 || top_k < 1 || n_experts < 1 || n_experts > 1024 || top_k > n_experts)
+        return CQ_ERR_INVALID_ARG;
+    if (n_tokens * top_k > (int64_t(1) << 24)) return CQ_ERR_SHAPE;
+    if (!offsets || (n_tokens > 0 && (!expert_ids || !pairs))) return CQ_ERR_INVALID_ARG;
+    if (!aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(pairs, 4))
+        return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_group(expert_ids, n_tokens, top_k, n_experts, offsets, pairs,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int x_per_pair, const int32_t* offsets, const int32_t* pairs,
+                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, cq_stream_t stream) {
+    if (int rc = check_weights(wt, w_experts, n, k)) return rc;
+    if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || ldy < n ||
+        (x_per_pair != 0 && x_per_pair != 1))
+        return CQ_ERR_INVALID_ARG;
+    if (k % 256 != 0 || moe_shape_ok(wt, n, k) != 0) return CQ_ERR_SHAPE;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    if (!xq || !offsets || !pairs || !y) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(offsets, 4) || !aligned(pairs, 4) || !aligned(y, 4))
+        return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_gemm(wt, w_experts, n_experts, n, k, xq, x_per_pair, offsets,
+                                     pairs, n_tokens, top_k, y, ldy,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld, int64_t rows, int64_t k,
+                            float* h_opt, void* hq, cq_stream_t stream) {
+    if (rows < 0 || k <= 0 || ld < k) return CQ_ERR_INVALID_ARG;
+    if (k % 32 != 0 || k > CQ_MAX_K) return CQ_ERR_SHAPE;
+    if (rows == 0) return CQ_OK;
+    if (!g || !u || !hq) return CQ_ERR_INVALID_ARG;
+    if (!aligned(g, 16) || !aligned(u, 16) || ld % 4 != 0 || !aligned(h_opt, 16) ||
+        !aligned(hq, 2))
+        return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_swiglu_quantize_q8_0(g, u, ld, rows, k, h_opt, hq,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
+                   int64_t n, float* y, int64_t ldy, cq_stream_t stream) {
+    if (n_tokens < 0 || top_k < 1 || n < 0 || ldy < n) return CQ_ERR_INVALID_ARG;
+    if (n_tokens == 0 || n == 0) return CQ_OK;
+    if (!d || !route_w || !y) return CQ_ERR_INVALID_ARG;
+    if (!aligned(d, 4) || !aligned(route_w, 4) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_combine(d, route_w, n_tokens, top_k, n, y, ldy,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

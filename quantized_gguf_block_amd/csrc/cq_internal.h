@@ -1,0 +1,30 @@
+// cq_internal.h -- launchers behind the C ABI (host side, HIP runtime).
+// Arguments reaching these functions have been validated by cq_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cq {
+
+// Compute-unit count of the current device (cached per device id).
+int device_cu_count();
+
+int launch_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k, void* xq,
+                         hipStream_t stream);
+int launch_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld, int64_t rows,
+                                int64_t k, float* h, void* hq, hipStream_t stream);
+int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
+                float* y, int64_t ldy, hipStream_t stream);
+int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m,
+                float* y, int64_t ldy, hipStream_t stream);
+int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                     int32_t* offsets, int32_t* pairs, hipStream_t stream);
+int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                    const void* xq, int x_per_pair, const int32_t* offsets,
+                    const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
+                    int64_t ldy, hipStream_t stream);
+int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
+                       int64_t n, float* y, int64_t ldy, hipStream_t stream);
+
+}  // namespace cq

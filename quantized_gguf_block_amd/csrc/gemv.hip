@@ -1,0 +1,400 @@
+// gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K) for
+// 1..8 Q8_0 activation rows.
+//
+// Design (HBM-bound; the weights are read exactly once):
+//  * A workgroup owns row tiles of RT consecutive weight rows.  Because GGUF
+//    rows are stored back to back, a tile is one contiguous byte range; all
+//    threads stage it into LDS with fully coalesced 16-byte loads (a wave
+//    reads 1 KiB per instruction), whatever the 18/20/34/144-byte block
+//    size.  Blocks are then re-sliced out of LDS.
+//  * Each lane owns fixed "columns" of K (one 32-value block, or for Q4_K one
+//    32-byte nibble chunk = two 32-value sub-blocks) and keeps the Q8_0
+//    activation of its columns, for all batch rows, in registers for the
+//    workgroup's lifetime; a grid-stride loop over tiles amortizes that load.
+//  * Per block: nibble unpack in registers, v_dot4 integer dots against the
+//    activation quants, scales applied once per 32-value block in fp32
+//    (alice-llm 2.0.0 README, "Computation Path (Q4_K)").  Batch rows share
+//    the decoded weight registers (alice-llm 2.0.0 README, "Batch-4
+//    Speculative Decoding": one accumulator register per row).
+//  * Cross-lane sums are wave64 DPP reductions (alice-llm 2.0.0 README, "The
+//    GPU Optimization Journey", phase 2: subgroup reduction instead of a
+//    shared-memory tree); with more than one wave per row the per-wave sums
+//    meet in LDS and are added in wave order.
+//  * The column split depends only on (type, k), never on the batch size, so
+//    batch row b gives bitwise the batch-1 result.
+#include "cq_device.h"
+#include "cq_internal.h"
+
+namespace cq {
+namespace {
+
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12 };
+
+// columns per lane: a Q4_K column already spans 64 values
+template <int FMT> constexpr int kCMax = (FMT == T_Q4_K) ? 1 : 2;
+constexpr int kMaxThreads = 512;    // 8 waves
+
+// bytes per block of the 32-value formats
+template <int FMT> struct Fmt;
+template <> struct Fmt<T_Q4_0> { static constexpr int BS = 18; };
+template <> struct Fmt<T_Q4_1> { static constexpr int BS = 20; };
+template <> struct Fmt<T_Q8_0> { static constexpr int BS = 34; };
+
+// Activation registers of one column for one batch row.
+template <int FMT> struct Act {
+    uint32_t q[8];  // 32 int8 quants
+    float dx;       // block scale
+    float sdx;      // dx * sum(q)            (Q4_1)
+    int bias;       // -8 * sum(q)            (Q4_0: start value of the dot)
+};
+template <> struct Act<T_Q4_K> {
+    uint32_t qa[8], qb[8];  // the two 32-value blocks under one nibble chunk
+    float dxa, dxb;
+    float sa, sb;           // dx * sum(q) of each block
+};
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// Load one 34-byte Q8_0 activation block (2-byte aligned) from global memory.
+__device__ __forceinline__ void load_q8(const uint8_t* p, uint32_t* q, float* dx, int* sum) {
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+    *dx = h2f(s[0]);
+    int acc = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        q[t] = static_cast<uint32_t>(s[1 + 2 * t]) | (static_cast<uint32_t>(s[2 + 2 * t]) << 16);
+        acc = sdot4(q[t], 0x01010101u, acc);
+    }
+    *sum = acc;
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a) {
+    int s;
+    load_q8(xq_row + static_cast<int64_t>(col) * 34, a.q, &a.dx, &s);
+    a.bias = -8 * s;
+    a.sdx = a.dx * static_cast<float>(s);
+}
+template <>
+__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a) {
+    int sa, sb;
+    load_q8(xq_row + static_cast<int64_t>(2 * col) * 34, a.qa, &a.dxa, &sa);
+    load_q8(xq_row + static_cast<int64_t>(2 * col + 1) * 34, a.qb, &a.dxb, &sb);
+    a.sa = a.dxa * static_cast<float>(sa);
+    a.sb = a.dxb * static_cast<float>(sb);
+}
+
+// Byte offset, inside the staged tile, of the block that holds column col
+// of tile row r.
+template <int FMT>
+__device__ __forceinline__ int col_offset(int row_base, int col) {
+    if constexpr (FMT == T_Q4_K) return row_base + (col >> 2) * 144;
+    else return row_base + col * Fmt<FMT>::BS;
+}
+
+// acc[j] += dot of one column of one weight row with activation row j.
+template <int FMT, int B>
+__device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Act<FMT>* a,
+                                           float* acc, int col) {
+    if constexpr (FMT == T_Q4_0) {
+        const float dw = h2f(lds_u16(lds, off));
+        uint32_t q[4];
+        lds_dwords_a2<4>(lds, off + 2, q);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            lo[t] = q[t] & 0x0F0F0F0Fu;
+            hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = a[j].bias;  // sum (q-8)*qx = sum q*qx - 8*sum qx
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
+            acc[j] = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
+        }
+    } else if constexpr (FMT == T_Q4_1) {
+        const uint32_t dm = *reinterpret_cast<const uint32_t*>(lds + off);  // 4-aligned
+        const float dw = h2f(dm & 0xFFFFu), mw = h2f(dm >> 16);
+        const uint32_t* qp = reinterpret_cast<const uint32_t*>(lds + off + 4);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t q = qp[t];
+            lo[t] = q & 0x0F0F0F0Fu;
+            hi[t] = (q >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
+            // dx * (d * sum(q*qx) + m * sum(qx))
+            float v = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
+            acc[j] = fmaf(mw, a[j].sdx, v);
+        }
+    } else if constexpr (FMT == T_Q8_0) {
+        const float dw = h2f(lds_u16(lds, off));
+        uint32_t q[8];
+        lds_dwords_a2<8>(lds, off + 2, q);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) s = sdot4(q[t], a[j].q[t], s);
+            acc[j] = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
+        }
+    } else {  // Q4_K: column = nibble chunk c of super-block at off
+        const int c = col & 3;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
+        const uint4 q0 = *reinterpret_cast<const uint4*>(lds + off + 16 + 32 * c);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(lds + off + 32 + 32 * c);
+        const float d = h2f(hdr.x & 0xFFFFu), dmin = h2f(hdr.x >> 16);
+        // six-bit scale/min of sub-blocks j0 = 2c and j1 = 2c + 1 from the 12
+        // scale bytes S[0..11] = hdr.y, hdr.z, hdr.w (little-endian)
+        const uint32_t s03 = hdr.y, s47 = hdr.z, s8b = hdr.w;
+        int sc0, m0, sc1, m1;
+        if (c < 2) {  // sub-blocks 0..3: low six bits of S[j] and S[j+4]
+            const int sh0 = 16 * c, sh1 = 16 * c + 8;
+            sc0 = (s03 >> sh0) & 63;
+            m0 = (s47 >> sh0) & 63;
+            sc1 = (s03 >> sh1) & 63;
+            m1 = (s47 >> sh1) & 63;
+        } else {      // sub-blocks 4..7: nibble of S[j+4], top bits of S[j-4] / S[j]
+            const int sh0 = 16 * (c - 2), sh1 = 16 * (c - 2) + 8;
+            sc0 = ((s8b >> sh0) & 0xF) | (((s03 >> sh0) >> 6 & 3) << 4);
+            m0 = ((s8b >> sh0) >> 4 & 0xF) | (((s47 >> sh0) >> 6 & 3) << 4);
+            sc1 = ((s8b >> sh1) & 0xF) | (((s03 >> sh1) >> 6 & 3) << 4);
+            m1 = ((s8b >> sh1) >> 4 & 0xF) | (((s47 >> sh1) >> 6 & 3) << 4);
+        }
+        const float ds0 = d * static_cast<float>(sc0), dm0 = dmin * static_cast<float>(m0);
+        const float ds1 = d * static_cast<float>(sc1), dm1 = dmin * static_cast<float>(m1);
+        const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            lo[t] = q[t] & 0x0F0F0F0Fu;
+            hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int sa = 0, sb = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sa = sdot4(lo[t], a[j].qa[t], sa);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sb = sdot4(hi[t], a[j].qb[t], sb);
+            // dx*(d*sc*sum(q*qx) - dmin*m*sum(qx)) for each sub-block
+            float v = fmaf(static_cast<float>(sa), ds0 * a[j].dxa, acc[j]);
+            v = fmaf(-dm0, a[j].sa, v);
+            v = fmaf(static_cast<float>(sb), ds1 * a[j].dxb, v);
+            acc[j] = fmaf(-dm1, a[j].sb, v);
+        }
+    }
+}
+
+template <int FMT, int B, int RT>
+__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t rb, int ncols, int C,
+        const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y, int64_t ldy,
+        int tile_lds_bytes) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* red = reinterpret_cast<float*>(smem + tile_lds_bytes);
+    const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+    // columns of this lane and their activations, resident for the whole kernel
+    constexpr int CM = kCMax<FMT>;
+    Act<FMT> act[CM][B];
+    int col[CM];
+    bool valid[CM];
+#pragma unroll
+    for (int i = 0; i < CM; ++i) {
+        col[i] = (wv * C + i) * kWave + lane;
+        valid[i] = (i < C) && (col[i] < ncols);
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (valid[i]) load_act<FMT>(xq + j * xq_row_bytes, col[i], act[i][j]);
+    }
+
+    const int64_t total = n * rb;
+    const int64_t ntiles = (n + RT - 1) / RT;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t r0 = tile * RT;
+        const int rt = static_cast<int>(n - r0 < RT ? n - r0 : RT);
+        const int64_t start = r0 * rb;
+        const int64_t a0 = start & ~static_cast<int64_t>(15);
+        const int delta = static_cast<int>(start - a0);
+        const int nvec = (delta + rt * static_cast<int>(rb) + 15) >> 4;
+
+        __syncthreads();  // the previous tile's LDS reads are done
+        for (int v0 = threadIdx.x; v0 < nvec; v0 += 4 * blockDim.x) {
+            uint4 val[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int v = v0 + u * blockDim.x;
+                const int64_t g = a0 + 16 * static_cast<int64_t>(v);
+                if (v < nvec && g + 16 <= total) {
+                    val[u] = *reinterpret_cast<const uint4*>(w + g);
+                } else if (v < nvec) {  // the matrix ends inside this vector
+                    uint16_t part[8];
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        part[p] = (g + 2 * p + 2 <= total)
+                                      ? *reinterpret_cast<const uint16_t*>(w + g + 2 * p) : 0;
+                    val[u] = make_uint4(part[0] | (part[1] << 16), part[2] | (part[3] << 16),
+                                        part[4] | (part[5] << 16), part[6] | (part[7] << 16));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int v = v0 + u * blockDim.x;
+                if (v < nvec) reinterpret_cast<uint4*>(smem)[v] = val[u];
+            }
+        }
+        __syncthreads();
+
+        float acc[RT][B];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int j = 0; j < B; ++j) acc[r][j] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (r < rt) {
+                const int row_base = delta + r * static_cast<int>(rb);
+#pragma unroll
+                for (int i = 0; i < CM; ++i)
+                    if (valid[i])
+                        column_dot<FMT, B>(smem, col_offset<FMT>(row_base, col[i]), act[i],
+                                           acc[r], col[i]);
+            }
+        }
+
+        // reduce over the wave, then over the waves of the row in wave order
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const float s = wave_sum(acc[r][j]);
+                if (nw == 1) {
+                    if (lane == 0 && r < rt) y[j * ldy + r0 + r] = s;
+                } else if (lane == 0) {
+                    red[(wv * RT + r) * B + j] = s;
+                }
+            }
+        }
+        if (nw > 1) {
+            __syncthreads();
+            const int t = threadIdx.x;
+            if (t < RT * B) {
+                const int r = t / B, j = t - r * B;
+                if (r < rt) {
+                    float s = red[r * B + j];
+                    for (int q = 1; q < nw; ++q) s += red[(q * RT + r) * B + j];
+                    y[j * ldy + r0 + r] = s;
+                }
+            }
+        }
+    }
+}
+
+struct Plan {
+    int ncols, C, nw, RT, tile_lds, red_bytes;
+};
+
+Plan make_plan(int wt, int64_t k, int64_t rb, int batch) {
+    Plan p{};
+    p.ncols = static_cast<int>(wt == T_Q4_K ? k / 64 : k / 32);
+    p.C = (wt == T_Q4_K || p.ncols <= kWave) ? 1 : 2;
+    p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
+    // rows per tile: about 16 KiB of weights per tile, at most 32 live
+    // accumulators per lane
+    int rt = 8;
+    while (rt > 1 && (rt * rb > 20480 || rt * batch > 32)) rt >>= 1;
+    if (rt == 2) rt = 1;  // instantiated tiles: 1, 4, 8
+    p.RT = rt;
+    p.tile_lds = static_cast<int>((rt * rb + 32 + 15) & ~15);
+    p.red_bytes = p.nw > 1 ? p.nw * rt * batch * 4 : 0;
+    return p;
+}
+
+template <int FMT, int B>
+int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
+                 int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
+    const int64_t ntiles = (n + p.RT - 1) / p.RT;
+    const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
+    int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
+    if (grid > ntiles) grid = ntiles;
+    const dim3 g(static_cast<unsigned>(grid)), b(p.nw * kWave);
+    const size_t lds = static_cast<size_t>(p.tile_lds + p.red_bytes);
+    switch (p.RT) {
+        case 8:
+            // make_plan keeps RT * batch <= 32, so RT = 8 exists for B <= 4 only
+            if constexpr (B <= 4) {
+                hipLaunchKernelGGL((gemv_kernel<FMT, B, 8>), g, b, lds, stream, w, n, rb, p.ncols,
+                                   p.C, xq, xrb, y, ldy, p.tile_lds);
+                break;
+            } else {
+                return -3;
+            }
+        case 4: hipLaunchKernelGGL((gemv_kernel<FMT, B, 4>), g, b, lds, stream, w, n, rb, p.ncols,
+                                   p.C, xq, xrb, y, ldy, p.tile_lds); break;
+        default: hipLaunchKernelGGL((gemv_kernel<FMT, B, 1>), g, b, lds, stream, w, n, rb, p.ncols,
+                                    p.C, xq, xrb, y, ldy, p.tile_lds); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+template <int FMT>
+int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb,
+               const uint8_t* xq, int64_t xrb, float* y, int64_t ldy, hipStream_t s) {
+    switch (batch) {
+        case 1: return launch_fmt_b<FMT, 1>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 2: return launch_fmt_b<FMT, 2>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 3: return launch_fmt_b<FMT, 3>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 4: return launch_fmt_b<FMT, 4>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 5: return launch_fmt_b<FMT, 5>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 6: return launch_fmt_b<FMT, 6>(p, w, n, rb, xq, xrb, y, ldy, s);
+        case 7: return launch_fmt_b<FMT, 7>(p, w, n, rb, xq, xrb, y, ldy, s);
+        default: return launch_fmt_b<FMT, 8>(p, w, n, rb, xq, xrb, y, ldy, s);
+    }
+}
+
+}  // namespace
+
+// Returns 0, -3 (shape the kernel cannot tile) or -6 (launch failure).
+int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
+    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const Plan p = make_plan(wt, k, k / qk * bs, static_cast<int>(batch));
+    if (p.nw * kWave > kMaxThreads) return -3;
+    if (p.tile_lds + p.red_bytes > 65536) return -3;
+    return 0;
+}
+
+int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
+                float* y, int64_t ldy, hipStream_t stream) {
+    if (gemv_shape_ok(wt, k, batch) != 0) return -3;
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
+    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t rb = k / qk * bs;
+    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    const uint8_t* xp = static_cast<const uint8_t*>(xq);
+    const int64_t xrb = k / 32 * 34;
+    const int b = static_cast<int>(batch);
+    switch (wt) {
+        case T_Q4_0: return launch_fmt<T_Q4_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q4_1: return launch_fmt<T_Q4_1>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q8_0: return launch_fmt<T_Q8_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q4_K: return launch_fmt<T_Q4_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        default: return -2;
+    }
+}
+
+}  // namespace cq

@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/cq.h
+declares, reports block geometry, and rejects invalid arguments on the host
+with the documented status before touching any device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gguf_block_amd as cq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cq.h")
+
+OK, INVALID, UNSUPPORTED, SHAPE, ALIGN = 0, -1, -2, -3, -4
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cq.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(cq.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.cq_abi_version() == 1
+    for code, name in cq.STATUS.items():
+        assert lib.cq_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.cq_status_string(12345)
+
+
+def test_block_geometry(lib):
+    assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12)] == [32, 32, 32, 256]
+    assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12)] == [18, 20, 34, 144]
+    assert lib.cq_row_bytes(12, 4096) == 2304
+    assert lib.cq_row_bytes(8, 4096) == 4352
+    assert lib.cq_row_bytes(12, 4000) == -1
+    assert lib.cq_block_bytes(7) == -1
+
+
+P = ctypes.c_void_p
+
+
+def test_quantize_validation(lib):
+    f = lib.cq_quantize_q8_0
+    assert f(P(FAKE), 64, 2, 48, P(FAKE), None) == SHAPE            # k % 32
+    assert f(P(FAKE), 16, 2, 64, P(FAKE), None) == INVALID          # ldx < k
+    assert f(None, 64, 2, 64, P(FAKE), None) == INVALID
+    assert f(P(FAKE + 4), 64, 2, 64, P(FAKE), None) == ALIGN        # x not 16-aligned
+    assert f(P(FAKE), 66, 2, 64, P(FAKE), None) == ALIGN            # ldx % 4
+    assert f(P(FAKE), 64, 2, 64, P(FAKE + 1), None) == ALIGN
+    assert f(None, 64, 0, 64, None, None) == OK                     # empty: no launch
+    assert f(P(FAKE), 1 << 20, 1, 1 << 17, P(FAKE), None) == SHAPE  # k > CQ_MAX_K
+
+
+def test_gemv_validation(lib):
+    f = lib.cq_gemv
+    assert f(7, P(FAKE), 8, 256, P(FAKE), 1, P(FAKE), 8, None) == UNSUPPORTED
+    assert f(12, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q4_K needs 256
+    assert f(2, P(FAKE), 8, 48, P(FAKE), 1, P(FAKE), 8, None) == SHAPE
+    assert f(2, P(FAKE), 8, 256, P(FAKE), 0, P(FAKE), 8, None) == INVALID  # batch 0
+    assert f(2, P(FAKE), 8, 256, P(FAKE), 9, P(FAKE), 8, None) == INVALID  # batch 9
+    assert f(2, P(FAKE), 8, 256, P(FAKE), 1, P(FAKE), 7, None) == INVALID  # ldy < n
+    assert f(2, P(FAKE + 8), 8, 256, P(FAKE), 1, P(FAKE), 8, None) == ALIGN
+    assert f(2, P(FAKE), 8, 256, P(FAKE + 1), 1, P(FAKE), 8, None) == ALIGN
+    assert f(2, P(FAKE), 8, 256, P(FAKE), 1, P(FAKE + 2), 8, None) == ALIGN
+    assert f(2, None, 8, 256, P(FAKE), 1, P(FAKE), 8, None) == INVALID
+    assert f(2, None, 0, 256, None, 1, None, 0, None) == OK              # n == 0
+    assert f(8, P(FAKE), -1, 256, P(FAKE), 1, P(FAKE), 8, None) == INVALID
+
+
+def test_gemm_validation(lib):
+    f = lib.cq_gemm
+    assert f(2, P(FAKE), 8, 32, P(FAKE), 4, P(FAKE), 8, None) == SHAPE     # k % 256
+    assert f(2, P(FAKE), 8, 256, P(FAKE), -1, P(FAKE), 8, None) == INVALID
+    assert f(2, P(FAKE), 8, 256, None, 0, None, 8, None) == OK             # m == 0
+    assert f(5, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
+
+
+def test_moe_validation(lib):
+    g = lib.cq_moe_group
+    assert g(P(FAKE), 4, 0, 32, P(FAKE), P(FAKE), None) == INVALID          # top_k 0
+    assert g(P(FAKE), 4, 4, 2000, P(FAKE), P(FAKE), None) == INVALID        # > 1024 experts
+    assert g(P(FAKE), 4, 8, 4, P(FAKE), P(FAKE), None) == INVALID           # top_k > E
+    assert g(P(FAKE + 2), 4, 4, 32, P(FAKE), P(FAKE), None) == ALIGN
+    m = lib.cq_moe_gemm
+    assert m(12, P(FAKE), 32, 64, 256, P(FAKE), 2, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
+             None) == INVALID                                                # x_per_pair
+    assert m(12, P(FAKE), 32, 64, 288, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
+             None) == SHAPE
+    assert m(12, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 0, 4, P(FAKE), 64,
+             None) == OK                                                     # no tokens
+    s = lib.cq_swiglu_quantize_q8_0
+    assert s(P(FAKE), P(FAKE), 64, 2, 48, None, P(FAKE), None) == SHAPE
+    assert s(P(FAKE), P(FAKE + 4), 64, 2, 64, None, P(FAKE), None) == ALIGN
+    assert s(P(FAKE), P(FAKE), 64, 2, 64, P(FAKE + 8), P(FAKE), None) == ALIGN
+    c = lib.cq_moe_combine
+    assert c(P(FAKE), P(FAKE), 4, 4, 64, P(FAKE), 32, None) == INVALID      # ldy < n
+    assert c(P(FAKE), P(FAKE), 0, 4, 64, P(FAKE), 64, None) == OK

@@ -1,0 +1,144 @@
+"""GPU parity of the decode GEMV (cq_gemv) against the fp64 oracle:
+|y - y_ref| <= 2e-5 * sum|w_hat*x_hat| per output, on small shapes that span
+several row tiles with ragged tails, on the full workload shapes, and on the
+invariants batch rows == single rows, determinism, power-of-two scaling and
+row permutation (all bitwise)."""
+import functools
+
+import numpy as np
+import pytest
+
+import gguf_synth as gs
+from gpu_common import assert_close_to_oracle, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K]
+
+
+def run_gemv(cq, fmt, w, n, k, xq, batch):
+    return to_host(cq.cq_gemv(fmt, to_dev(w), n, k, to_dev(xq), batch))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
+@pytest.mark.parametrize("n,k", [(1, 256), (37, 256), (130, 2048), (67, 4096), (9, 8192),
+                                 (21, 352), (45, 1056)])
+def test_gemv_small_shapes(cq, orc, fmt, n, k):
+    if k % gs.BLOCK_ELEMS[fmt]:
+        pytest.skip("k not a whole number of blocks for this type")
+    w = gs.weights(fmt, n, k, cfg=200 + n)
+    x = gs.activations(8, k, cfg=200 + n)
+    xq = orc.quantize_q8_0(x)
+    y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, 8)
+    for batch in (1, 2, 5, 8):
+        note("gemv", gs.NAMES[fmt], n, k, batch)
+        y = run_gemv(cq, fmt, w, n, k, xq[:batch], batch)
+        assert_close_to_oracle(y, y_ref[:batch], s_ref[:batch], what=f"{gs.NAMES[fmt]} b{batch}")
+
+
+@functools.lru_cache(maxsize=2)
+def config_inputs(name):
+    c = gs.CONFIGS[name]
+    w = gs.weights(c["fmt"], c["n"], c["k"], cfg=c["cfg"])
+    x = gs.activations(max(c["batches"]), c["k"], cfg=c["cfg"])
+    return c, w, x
+
+
+@pytest.mark.parametrize("name", ["q4_0_gemv_2048", "q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up"])
+def test_gemv_config_full(cq, orc, name):
+    c, w, x = config_inputs(name)
+    xq = orc.quantize_q8_0(x)
+    B = max(c["batches"])
+    y_ref, s_ref = orc.matmul(c["fmt"], w, c["n"], c["k"], xq, B)
+    wd, xd = to_dev(w), to_dev(xq)
+    for batch in c["batches"]:
+        note("gemv config", name, batch)
+        y = to_host(cq.cq_gemv(c["fmt"], wd, c["n"], c["k"], xd, batch))
+        r = assert_close_to_oracle(y, y_ref[:batch], s_ref[:batch], what=f"{name} b{batch}")
+        print(f"{name} batch {batch}: max |err|/S = {r:.3e}")
+
+
+def test_gemv_lm_head_sampled(cq, orc):
+    """Q4_K LM head 128256 x 4096 at batch 1 and 4: every output of the first
+    and last row tiles plus 4000 random outputs against the oracle, and the
+    batch-4 rows equal the batch-1 results bitwise."""
+    name = "q4_k_gemv_lm_head"
+    c, w, x = config_inputs(name)
+    n, k = c["n"], c["k"]
+    xq = orc.quantize_q8_0(x)
+    wd, xd = to_dev(w), to_dev(xq)
+    note("gemv lm head b4")
+    y4 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 4))
+    note("gemv lm head b1")
+    y1 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 1))
+    assert np.array_equal(y4[0], y1[0])
+    rng = np.random.default_rng(11)
+    rows = np.concatenate([np.arange(0, 64), np.arange(n - 64, n), rng.integers(0, n, 4000)])
+    bs = np.concatenate([np.arange(128) % 4, rng.integers(0, 4, 4000)])
+    y_ref, s_ref = orc.matmul_sampled(c["fmt"], w, n, k, xq, 4, bs, rows)
+    assert_close_to_oracle(y4[bs, rows], y_ref, s_ref, what="lm head b4")
+    # each batch row separately equals a batch-1 call on that row
+    for b in range(1, 4):
+        yb = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd[b:b + 1], 1))
+        assert np.array_equal(yb[0], y4[b])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
+def test_gemv_batch_rows_equal_single_rows(cq, orc, fmt):
+    n, k = 300, 4096
+    w = gs.weights(fmt, n, k, cfg=300)
+    xq = orc.quantize_q8_0(gs.activations(8, k, cfg=300))
+    wd = to_dev(w)
+    note("gemv batch invariance", gs.NAMES[fmt])
+    for batch in (2, 5, 8):
+        yb = to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq[:batch]), batch))
+        for b in range(batch):
+            y1 = to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq[b:b + 1]), 1))
+            assert np.array_equal(yb[b], y1[0]), (batch, b)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
+def test_gemv_deterministic_and_scaling(cq, orc, fmt):
+    n, k = 257, 2048
+    w = gs.weights(fmt, n, k, cfg=301)
+    xq = orc.quantize_q8_0(gs.activations(3, k, cfg=301))
+    note("gemv determinism", gs.NAMES[fmt])
+    y0 = run_gemv(cq, fmt, w, n, k, xq, 3)
+    y1 = run_gemv(cq, fmt, w, n, k, xq, 3)
+    assert np.array_equal(y0, y1)
+    # doubling every weight scale (d, and m or dmin) doubles y bitwise
+    w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[fmt])
+    nf = 2 if fmt in (gs.Q4_1, gs.Q4_K) else 1
+    for f in range(nf):
+        h = w2[:, 2 * f:2 * f + 2].copy().view(np.float16)
+        w2[:, 2 * f:2 * f + 2] = (h * np.float16(2)).view(np.uint8)
+    y2 = run_gemv(cq, fmt, w2.reshape(n, -1), n, k, xq, 3)
+    assert np.array_equal(y2, 2 * y0)
+    # permuting weight rows permutes y
+    perm = np.random.default_rng(1).permutation(n)
+    yp = run_gemv(cq, fmt, w[perm], n, k, xq, 3)
+    assert np.array_equal(yp, y0[:, perm])
+
+
+def test_gemv_strided_output(cq, orc):
+    import torch
+    fmt, n, k = gs.Q8_0, 100, 512
+    w = gs.weights(fmt, n, k, cfg=302)
+    xq = orc.quantize_q8_0(gs.activations(3, k, cfg=302))
+    note("gemv strided y")
+    y = torch.full((3, 160), -7.0, device="cuda")
+    cq.cq_gemv(fmt, to_dev(w), n, k, to_dev(xq), 3, y=y, ldy=160)
+    yh = to_host(y)
+    y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, 3)
+    assert_close_to_oracle(yh[:, :n], y_ref, s_ref, what="strided")
+    assert np.all(yh[:, n:] == -7.0)
+
+
+def test_gemv_zero_weights_exact(cq, orc):
+    k = 1024
+    w = gs.weights(gs.Q4_0, 64, k, cfg=303)
+    w.reshape(-1, 18)[:, 2:] = 0x88
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=303))
+    note("gemv zero weights")
+    y = run_gemv(cq, gs.Q4_0, w, 64, k, xq, 2)
+    assert not y.any()
