@@ -41,15 +41,24 @@ template <> struct Fmt<T_Q4_1> { static constexpr int BS = 20; };
 template <> struct Fmt<T_Q8_0> { static constexpr int BS = 34; };
 
 // Activation registers of one column for one batch row.
+// Integer dots start from kBias = bit pattern of 1.5*2^23: for |s| < 2^22
+// the int32 kBias + s, read as a float, is exactly 12582912 + s, so
+// fma(that, dx, -12582912*dx) = round(s*dx) with no int-to-float convert
+// (-12582912*dx is exact: dx is an fp16 value, 11 significant bits).
+constexpr int kBias = 0x4B400000;
+constexpr float kBiasF = 12582912.0f;
+
 template <int FMT> struct Act {
     uint32_t q[8];  // 32 int8 quants
     float dx;       // block scale
-    float sdx;      // dx * sum(q)            (Q4_1)
-    int bias;       // -8 * sum(q)            (Q4_0: start value of the dot)
+    float ndx;      // -12582912 * dx
+    float sdx;      // dx * sum(q)                  (Q4_1)
+    int start;      // kBias (- 8 * sum(q) for Q4_0): start value of the dot
 };
 template <> struct Act<T_Q4_K> {
     uint32_t qa[8], qb[8];  // the two 32-value blocks under one nibble chunk
     float dxa, dxb;
+    float ndxa, ndxb;       // -12582912 * dx
     float sa, sb;           // dx * sum(q) of each block
 };
 
@@ -74,7 +83,8 @@ template <int FMT>
 __device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a) {
     int s;
     load_q8(xq_row + static_cast<int64_t>(col) * 34, a.q, &a.dx, &s);
-    a.bias = -8 * s;
+    a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
+    a.ndx = -kBiasF * a.dx;
     a.sdx = a.dx * static_cast<float>(s);
 }
 template <>
@@ -84,6 +94,8 @@ __device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col,
     load_q8(xq_row + static_cast<int64_t>(2 * col + 1) * 34, a.qb, &a.dxb, &sb);
     a.sa = a.dxa * static_cast<float>(sa);
     a.sb = a.dxb * static_cast<float>(sb);
+    a.ndxa = -kBiasF * a.dxa;
+    a.ndxb = -kBiasF * a.dxb;
 }
 
 // Byte offset, inside the staged tile, of the block that holds column col
@@ -110,12 +122,13 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = a[j].bias;  // sum (q-8)*qx = sum q*qx - 8*sum qx
+            int s = a[j].start;  // kBias + sum (q-8)*qx = kBias + sum q*qx - 8*sum qx
 #pragma unroll
             for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
 #pragma unroll
             for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
-            acc[j] = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);  // sum * dx
+            acc[j] = fmaf(sx, dw, acc[j]);
         }
     } else if constexpr (FMT == T_Q4_1) {
         const uint32_t dm = *reinterpret_cast<const uint32_t*>(lds + off);  // 4-aligned
@@ -130,14 +143,14 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = 0;
+            int s = kBias;
 #pragma unroll
             for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
 #pragma unroll
             for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
             // dx * (d * sum(q*qx) + m * sum(qx))
-            float v = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
-            acc[j] = fmaf(mw, a[j].sdx, v);
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
+            acc[j] = fmaf(mw, a[j].sdx, fmaf(sx, dw, acc[j]));
         }
     } else if constexpr (FMT == T_Q8_0) {
         const float dw = h2f(lds_u16(lds, off));
@@ -145,10 +158,11 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         lds_dwords_a2<8>(lds, off + 2, q);
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = 0;
+            int s = kBias;
 #pragma unroll
             for (int t = 0; t < 8; ++t) s = sdot4(q[t], a[j].q[t], s);
-            acc[j] = fmaf(static_cast<float>(s), dw * a[j].dx, acc[j]);
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
+            acc[j] = fmaf(sx, dw, acc[j]);
         }
     } else {  // Q4_K: column = nibble chunk c of super-block at off
         const int c = col & 3;
@@ -184,15 +198,17 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int sa = 0, sb = 0;
+            int sa = kBias, sb = kBias;
 #pragma unroll
             for (int t = 0; t < 8; ++t) sa = sdot4(lo[t], a[j].qa[t], sa);
 #pragma unroll
             for (int t = 0; t < 8; ++t) sb = sdot4(hi[t], a[j].qb[t], sb);
             // dx*(d*sc*sum(q*qx) - dmin*m*sum(qx)) for each sub-block
-            float v = fmaf(static_cast<float>(sa), ds0 * a[j].dxa, acc[j]);
+            const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
+            const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
+            float v = fmaf(xa, ds0, acc[j]);
             v = fmaf(-dm0, a[j].sa, v);
-            v = fmaf(static_cast<float>(sb), ds1 * a[j].dxb, v);
+            v = fmaf(xb, ds1, v);
             acc[j] = fmaf(-dm1, a[j].sb, v);
         }
     }
@@ -303,11 +319,199 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
     }
 }
 
+// ---- single-wave variant: one wave covers all of k (every lane owns its
+// columns), so waves never wait for each other.  Each wave streams its row
+// tiles HBM -> LDS with LDS-DMA (global_load_lds_dwordx4: 16 bytes per lane,
+// 1 KiB per instruction, no VGPRs) through a ring of three wave-private
+// buffers: while tile t is computed, tiles t+1 and t+2 are in flight.
+//
+// Wait accounting: every tile is exactly kDmaVec DMA instructions (lanes
+// past the tile re-load the tile's first 16 bytes into the buffer's unused
+// tail) and every processed tile issues exactly one global store, so the
+// number of vector-memory operations issued after a tile's DMA is a
+// compile-time constant and an explicit s_waitcnt vmcnt(N) suffices.  The
+// DMA is issued from inline assembly: the compiler then does not model it,
+// and places no waits of its own for it (its waits for its own loads can
+// only become more conservative); all waits for the DMA are the explicit
+// ones below.
+constexpr int kDmaVec = 10;                        // 1-KiB DMA instructions per tile
+constexpr int kDmaTileBytes = kDmaVec * 1024;
+constexpr int kDmaBufBytes = kDmaTileBytes + 64;   // + read slack
+constexpr int kWavesPerCu = 4;                     // one per SIMD; 3 buffers each: 4 * 31 KiB of LDS
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {      // s_waitcnt vmcnt(N)
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// One LDS-DMA instruction: lane i copies the 16 bytes at gaddr (its own)
+// to LDS[lds_base + 16*i]; lds_base must be wave-uniform.  M0 carries the
+// LDS base; it is saved and restored around the instruction, with one wait
+// state between the M0 write and the DMA that reads it.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gaddr), "s"(lds_base)
+        : "memory");
+}
+
+// Stage bytes [a0, a0 + 16*nvec) of w (a0 16-aligned, a0 + 16*nvec <= size
+// of w) into buf with exactly kDmaVec DMA instructions.
+__device__ __forceinline__ void dma_tile(const uint8_t* __restrict__ w, int64_t a0, int nvec,
+                                         uint8_t* buf, int lane) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(buf));
+#pragma unroll
+    for (int u = 0; u < kDmaVec; ++u) {
+        const int v = u * kWave + lane;
+        const int64_t g = a0 + (v < nvec ? 16 * static_cast<int64_t>(v) : 0);
+        dma16(w + g, base + u * kWave * 16);
+    }
+}
+
+// Sum each of the V = RT*B accumulators over the 64 lanes and store row r,
+// batch j to y[j*ldy + r0 + r] (r < rt) with one store instruction.
+// Groups of four values are transposed across the wave with
+// permlane32_swap / permlane16_swap so that each 16-lane row holds one
+// value, then each row is summed with four DPP steps.  The association
+// order is the same for every value slot.
+template <int RT, int B>
+__device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_t r0,
+                                             float* __restrict__ y, int64_t ldy, int lane) {
+    constexpr int V = RT * B;
+    constexpr int NG = (V + 3) / 4;
+    static_assert(NG <= 16, "at most 64 values");
+    float vals[4 * NG];
+#pragma unroll
+    for (int i = 0; i < 4 * NG; ++i) vals[i] = (i < V) ? acc[i / B][i % B] : 0.0f;
+    float out = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g]),
+                                                         __float_as_uint(vals[4 * g + 1]), false, false);
+        const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g + 2]),
+                                                         __float_as_uint(vals[4 * g + 3]), false, false);
+        const float sab = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);  // rows 0,1: a; 2,3: b
+        const float scd = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);  // rows 0,1: c; 2,3: d
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(sab), __float_as_uint(scd),
+                                                        false, false);
+        float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);             // rows: a, c, b, d
+        v += dpp_f<0xB1>(v);
+        v += dpp_f<0x4E>(v);
+        v += dpp_f<0x141>(v);
+        v += dpp_f<0x140>(v);                                                // row sums
+        if ((lane & 15) == g) out = v;
+    }
+    const int row = lane >> 4, g = lane & 15;
+    const int idx = 4 * g + (row == 1 ? 2 : (row == 2 ? 1 : row));
+    const int r = idx / B, j = idx - (idx / B) * B;
+    if (g < NG && idx < V && r < rt) y[j * ldy + r0 + r] = out;
+}
+
+template <int FMT, int B, int RT>
+__global__ __launch_bounds__(kWave) void gemv_wave_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t rb, int ncols, int C,
+        const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
+        int64_t ldy) {
+    __shared__ __align__(16) uint8_t buf0[kDmaBufBytes];
+    __shared__ __align__(16) uint8_t buf1[kDmaBufBytes];
+    __shared__ __align__(16) uint8_t buf2[kDmaBufBytes];
+    const int lane = threadIdx.x;
+
+    constexpr int CM = kCMax<FMT>;
+    Act<FMT> act[CM][B];
+    int col[CM];
+    bool valid[CM];
+#pragma unroll
+    for (int i = 0; i < CM; ++i) {
+        col[i] = i * kWave + lane;
+        valid[i] = (i < C) && (col[i] < ncols);
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (valid[i]) load_act<FMT>(xq + j * xq_row_bytes, col[i], act[i][j]);
+    }
+
+    const int64_t G = gridDim.x;
+    const int64_t ntiles = (n + RT - 1) / RT;
+    const int64_t nt = ntiles > blockIdx.x ? (ntiles - blockIdx.x + G - 1) / G : 0;
+    auto tile_of = [&](int64_t i) { return blockIdx.x + i * G; };
+    auto issue = [&](int64_t i, uint8_t* buf) {
+        const int64_t r0 = tile_of(i) * RT;
+        const int rt = static_cast<int>(n - r0 < RT ? n - r0 : RT);
+        const int64_t a0 = (r0 * rb) & ~static_cast<int64_t>(15);
+        const int nvec = (static_cast<int>(r0 * rb - a0) + rt * static_cast<int>(rb) + 15) >> 4;
+        wait_lds_all();  // earlier reads of this buffer have completed
+        dma_tile(w, a0, nvec, buf, lane);
+    };
+    auto process = [&](int64_t i, const uint8_t* buf) {
+        const int64_t r0 = tile_of(i) * RT;
+        const int rt = static_cast<int>(n - r0 < RT ? n - r0 : RT);
+        const int delta = static_cast<int>(r0 * rb - ((r0 * rb) & ~static_cast<int64_t>(15)));
+        float acc[RT][B];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int j = 0; j < B; ++j) acc[r][j] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (r < rt) {
+                const int row_base = delta + r * static_cast<int>(rb);
+#pragma unroll
+                for (int c = 0; c < CM; ++c)
+                    if (valid[c])
+                        column_dot<FMT, B>(buf, col_offset<FMT>(row_base, col[c]), act[c],
+                                           acc[r], col[c]);
+            }
+        }
+        reduce_store<RT, B>(acc, rt, r0, y, ldy, lane);
+    };
+    // tile i lives in buffer i % 3; step i issues tile i+2, waits for tile i
+    // (vector-memory operations issued after tile i's DMA: the store of
+    // tile i-2, DMA of tile i+1, store of tile i-1, DMA of tile i+2), then
+    // computes it.
+    auto step = [&](int64_t i, const uint8_t* cur, uint8_t* nxt) {
+        if (i + 2 < nt) {
+            issue(i + 2, nxt);
+            if (i >= 2) wait_vmem<2 * kDmaVec + 2>();
+            else if (i == 1) wait_vmem<2 * kDmaVec + 1>();
+            else wait_vmem<2 * kDmaVec>();
+        } else {
+            wait_vmem<0>();
+        }
+        process(i, cur);
+    };
+    if (nt > 0) issue(0, buf0);
+    if (nt > 1) issue(1, buf1);
+    for (int64_t i = 0; i < nt; i += 3) {
+        step(i, buf0, buf2);
+        if (i + 1 >= nt) break;
+        step(i + 1, buf1, buf0);
+        if (i + 2 >= nt) break;
+        step(i + 2, buf2, buf1);
+    }
+}
+
 struct Plan {
     int ncols, C, nw, RT, tile_lds, red_bytes;
+    bool wave;  // single-wave LDS-DMA kernel
 };
 
-Plan make_plan(int wt, int64_t k, int64_t rb, int batch) {
+// wave_ok: the single-wave LDS-DMA kernel may be used (the matrix is a whole
+// number of 16-byte vectors, so no tile ends inside a vector).
+Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool wave_ok) {
     Plan p{};
     p.ncols = static_cast<int>(wt == T_Q4_K ? k / 64 : k / 32);
     p.C = (wt == T_Q4_K || p.ncols <= kWave) ? 1 : 2;
@@ -317,6 +521,11 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch) {
     int rt = 8;
     while (rt > 1 && (rt * rb > 20480 || rt * batch > 32)) rt >>= 1;
     if (rt == 2) rt = 1;  // instantiated tiles: 1, 4, 8
+    if (p.nw == 1 && wave_ok) {  // single-wave kernel: tiles bounded by its LDS buffers
+        rt = 8;
+        while (rt > 1 && (rt * rb + 15 > kDmaTileBytes || rt * batch > 32)) rt >>= 1;
+        p.wave = rt * rb + 15 <= kDmaTileBytes;
+    }
     p.RT = rt;
     p.tile_lds = static_cast<int>((rt * rb + 32 + 15) & ~15);
     p.red_bytes = p.nw > 1 ? p.nw * rt * batch * 4 : 0;
@@ -327,6 +536,28 @@ template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
+    if (p.wave) {
+        int64_t grid = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
+        if (grid > ntiles) grid = ntiles;
+        const dim3 g(static_cast<unsigned>(grid)), b(kWave);
+        switch (p.RT) {
+            case 8:
+                if constexpr (B <= 4) {
+                    hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 8>), g, b, 0, stream, w, n, rb,
+                                       p.ncols, p.C, xq, xrb, y, ldy);
+                    break;
+                } else {
+                    return -3;
+                }
+            case 4: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 4>), g, b, 0, stream, w, n, rb,
+                                       p.ncols, p.C, xq, xrb, y, ldy); break;
+            case 2: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 2>), g, b, 0, stream, w, n, rb,
+                                       p.ncols, p.C, xq, xrb, y, ldy); break;
+            default: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 1>), g, b, 0, stream, w, n, rb,
+                                        p.ncols, p.C, xq, xrb, y, ldy); break;
+        }
+        return hipGetLastError() == hipSuccess ? 0 : -6;
+    }
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
     if (grid > ntiles) grid = ntiles;
@@ -371,9 +602,9 @@ int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb
 int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
     const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
     const int64_t qk = wt == T_Q4_K ? 256 : 32;
-    const Plan p = make_plan(wt, k, k / qk * bs, static_cast<int>(batch));
+    const Plan p = make_plan(wt, k, k / qk * bs, static_cast<int>(batch), false);
     if (p.nw * kWave > kMaxThreads) return -3;
-    if (p.tile_lds + p.red_bytes > 65536) return -3;
+    if (!p.wave && p.tile_lds + p.red_bytes > 65536) return -3;
     return 0;
 }
 
@@ -383,7 +614,7 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
     const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
     const int64_t qk = wt == T_Q4_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
-    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch));
+    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch), (n * rb) % 16 == 0);
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     const uint8_t* xp = static_cast<const uint8_t*>(xq);
     const int64_t xrb = k / 32 * 34;
