@@ -135,7 +135,7 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  * scales applied per block in fp32.
  *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
  *   w      [n][k/qk] blocks, 16-byte aligned; xq [m][k/32] Q8_0 blocks,
- *          2-byte aligned; y fp32 [m][ldy], ldy >= n, 4-byte aligned.
+ *          4-byte aligned; y fp32 [m][ldy], ldy >= n, 4-byte aligned.
  *   k      multiple of 256, k <= CQ_MAX_K.
  * Accuracy as cq_gemv.
  */

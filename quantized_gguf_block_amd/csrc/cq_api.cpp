@@ -134,7 +134,7 @@ int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t
     if (k % 256 != 0 || gemm_shape_ok(wt, k) != 0) return CQ_ERR_SHAPE;
     if (n == 0 || m == 0) return CQ_OK;
     if (!xq || !y) return CQ_ERR_INVALID_ARG;
-    if (!aligned(xq, 2) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (!aligned(xq, 4) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
     return status_of(launch_gemm(wt, w, n, k, xq, m, y, ldy, reinterpret_cast<hipStream_t>(stream)));
 }
