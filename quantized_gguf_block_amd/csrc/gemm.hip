@@ -39,8 +39,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;          // tokens per workgroup tile
-constexpr int BN = 128;          // weight rows per workgroup tile
 constexpr int KB = 4;            // 32-value blocks per k step
 constexpr int ROW = KB * 32 + 16;  // LDS row stride of the int8 tiles (16 B pad)
 constexpr int kThreads = 256;
@@ -49,6 +47,17 @@ constexpr float kBiasF = 12582912.0f;
 
 template <int FMT> constexpr bool kHasOffset = (FMT == T_Q4_1 || FMT == T_Q4_K);
 
+// Workgroup tile of BM tokens x BN weight rows: 4 waves arranged WMW x WNW,
+// each wave MI x NI tiles of 32 x 32.
+template <int WMW, int WNW, int MI, int NI>
+struct Tile {
+    static constexpr int BM = WMW * MI * 32;
+    static constexpr int BN = WNW * NI * 32;
+    static_assert(WMW * WNW == 4, "four waves");
+    static_assert(BN == 128 && BM <= 128, "staging assumes 128 weight rows, <= 128 tokens");
+};
+
+template <int BM, int BN>
 struct Smem {
     int8_t w[BN * ROW];       // decoded weight quants, row n, k within the step
     int8_t x[BM * ROW];       // activation quants
@@ -56,6 +65,8 @@ struct Smem {
     float dx[KB][BM];         // activation block scale
     float cw[KB][BN];         // Q4_1: m; Q4_K: -dmin*min  (additive weight term)
     float sx[KB][BM];         // dx * sum of the block's activation quants
+    int xrow[BM];             // activation row of each tile row (-1: none)
+    int yrow[BM];             // output row of each tile row
 };
 
 __device__ __forceinline__ uint32_t nib_lo_s8(uint32_t v) {   // low nibbles as q-8
@@ -88,8 +99,8 @@ __device__ __forceinline__ uint32_t half_at(const uint32_t* w, int off) {
 // ---- staging of one k step --------------------------------------------------
 // Two threads per row: thread t stages row t/2, blocks 2*(t%2) and
 // 2*(t%2)+1 of the step.  All global loads are 4-byte loads.
-template <int FMT>
-__device__ __forceinline__ void stage_weights(Smem& s, const uint8_t* __restrict__ w, int64_t n,
+template <int FMT, class S>
+__device__ __forceinline__ void stage_weights(S& s, const uint8_t* __restrict__ w, int64_t n,
                                               int64_t rb, int64_t n0, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
     const int64_t gn = n0 + row;
@@ -173,15 +184,18 @@ __device__ __forceinline__ void stage_weights(Smem& s, const uint8_t* __restrict
     }
 }
 
-template <int FMT>
-__device__ __forceinline__ void stage_acts(Smem& s, const uint8_t* __restrict__ xq, int64_t m,
-                                           int64_t xrb, int64_t m0, int kstep) {
+// Activations: threads t < 2*BM stage tile row t/2 (activation row
+// s.xrow[t/2], -1 = zeros), blocks 2*(t%2) and +1 of the step.
+template <int FMT, int BM, class S>
+__device__ __forceinline__ void stage_acts(S& s, const uint8_t* __restrict__ xq, int64_t xrb,
+                                           int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
-    const int64_t gm = m0 + row;
+    if (row >= BM) return;
+    const int gm = s.xrow[row];
     uint32_t v[17];  // 2 blocks x 34 bytes
-    if (gm < m) {
+    if (gm >= 0) {
         const uint32_t* p = reinterpret_cast<const uint32_t*>(
-            xq + gm * xrb + (static_cast<int64_t>(kstep) * KB + 2 * half) * 34);
+            xq + static_cast<int64_t>(gm) * xrb + (static_cast<int64_t>(kstep) * KB + 2 * half) * 34);
 #pragma unroll
         for (int i = 0; i < 17; ++i) v[i] = p[i];
     } else {
@@ -207,35 +221,29 @@ __device__ __forceinline__ void stage_acts(Smem& s, const uint8_t* __restrict__ 
     }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
-        const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
-        const uint8_t* __restrict__ xq, int64_t m, float* __restrict__ y, int64_t ldy,
-        int tiles_m, int tiles_total) {
-    __shared__ __align__(16) Smem s;
-    // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin,
-    // so give each XCD a contiguous run of tiles (the M tiles of one weight
-    // tile share that XCD's L2).
-    const int G = gridDim.x, g = blockIdx.x;
-    const int per_xcd = G / 8, rem = G % 8;
-    int tile;
-    if (g < 8 * per_xcd) tile = (g % 8) * per_xcd + g / 8;
-    else tile = 8 * per_xcd + (g - 8 * per_xcd);
-    (void)rem;
-    if (tile >= tiles_total) return;
-    const int64_t m0 = static_cast<int64_t>(tile % tiles_m) * BM;
-    const int64_t n0 = static_cast<int64_t>(tile / tiles_m) * BN;
-
+// One workgroup tile: y[yrow[r]][n0 + c] for tile rows r with xrow[r] >= 0,
+// over all of k.  Weights: rows n0.. of w (n rows, rb bytes per row).
+template <int FMT, int WMW, int WNW, int MI, int NI>
+__device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& s,
+                                         const uint8_t* __restrict__ w, int64_t n, int64_t k,
+                                         int64_t rb, int64_t n0, const uint8_t* __restrict__ xq,
+                                         int rows, float* __restrict__ y, int64_t ldy) {
+    constexpr int BM = Tile<WMW, WNW, MI, NI>::BM;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wm = wv >> 1, wn = wv & 1;       // wave tile: tokens 64*wm.., rows 64*wn..
+    const int wm = wv / WNW, wn = wv % WNW;     // wave tile: tokens wm*MI*32.., rows wn*NI*32..
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t xrb = k / 32 * 34;
+    // token sub-tiles of this wave that hold at least one real row
+    int mi_live = 0;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+        if ((wm * MI + mi) * 32 < rows) mi_live = mi + 1;
 
-    v16f acc[2][2];
+    v16f acc[MI][NI];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < MI; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NI; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
     v16i bias;
@@ -246,33 +254,34 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     for (int ks = 0; ks < ksteps; ++ks) {
         __syncthreads();
         stage_weights<FMT>(s, w, n, rb, n0, ks);
-        stage_acts<FMT>(s, xq, m, xrb, m0, ks);
+        stage_acts<FMT, BM>(s, xq, xrb, ks);
         __syncthreads();
 #pragma unroll 2
         for (int b = 0; b < KB; ++b) {
-            v4i A[2], Bv[2];
+            v4i A[NI], Bv[MI];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                A[ni] = *reinterpret_cast<const v4i*>(s.w + (64 * wn + 32 * ni + l32) * ROW + 32 * b + 16 * h);
+            for (int ni = 0; ni < NI; ++ni)
+                A[ni] = *reinterpret_cast<const v4i*>(s.w + ((wn * NI + ni) * 32 + l32) * ROW + 32 * b + 16 * h);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                Bv[mi] = *reinterpret_cast<const v4i*>(s.x + (64 * wm + 32 * mi + l32) * ROW + 32 * b + 16 * h);
-            float dx[2], ndx[2];
+            for (int mi = 0; mi < MI; ++mi)
+                Bv[mi] = *reinterpret_cast<const v4i*>(s.x + ((wm * MI + mi) * 32 + l32) * ROW + 32 * b + 16 * h);
+            float dx[MI], ndx[MI];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
-                dx[mi] = s.dx[b][64 * wm + 32 * mi + l32];
+            for (int mi = 0; mi < MI; ++mi) {
+                dx[mi] = s.dx[b][(wm * MI + mi) * 32 + l32];
                 ndx[mi] = -kBiasF * dx[mi];
             }
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
+            for (int ni = 0; ni < NI; ++ni) {
                 float dwv[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][64 * wn + 32 * ni + 8 * q + 4 * h]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][(wn * NI + ni) * 32 + 8 * q + 4 * h]);
                     dwv[4 * q] = d4.x; dwv[4 * q + 1] = d4.y; dwv[4 * q + 2] = d4.z; dwv[4 * q + 3] = d4.w;
                 }
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
+                for (int mi = 0; mi < MI; ++mi) {
+                    if (mi >= mi_live) break;
                     const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ni], Bv[mi], bias, 0, 0, 0);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -288,11 +297,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
 #pragma unroll
             for (int b2 = 0; b2 < KB; b2 += 2) {
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const float a = s.cw[b2 + h][64 * wn + 32 * ni + l32];
+                for (int ni = 0; ni < NI; ++ni) {
+                    const float a = s.cw[b2 + h][(wn * NI + ni) * 32 + l32];
 #pragma unroll
-                    for (int mi = 0; mi < 2; ++mi) {
-                        const float bx = s.sx[b2 + h][64 * wm + 32 * mi + l32];
+                    for (int mi = 0; mi < MI; ++mi) {
+                        if (mi >= mi_live) break;
+                        const float bx = s.sx[b2 + h][(wm * MI + mi) * 32 + l32];
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bx, acc[mi][ni], 0, 0, 0);
                     }
                 }
@@ -300,23 +310,85 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         }
     }
 
-    // epilogue: lane holds token m = m0 + 64wm + 32mi + l32 and weight rows
-    // n = n0 + 64wn + 32ni + 8q + 4h + s (register r = 4q + s)
+    // epilogue: lane holds tile row (wm*MI + mi)*32 + l32 and weight rows
+    // n0 + (wn*NI + ni)*32 + 8q + 4h + e (register 4q + e)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int64_t gm = m0 + 64 * wm + 32 * mi + l32;
-        if (gm >= m) continue;
-        float* yr = y + gm * ldy;
+    for (int mi = 0; mi < MI; ++mi) {
+        const int r = (wm * MI + mi) * 32 + l32;
+        if (r >= rows || s.xrow[r] < 0) continue;
+        float* yr = y + static_cast<int64_t>(s.yrow[r]) * ldy;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t gn = n0 + 64 * wn + 32 * ni + 8 * q + 4 * h;
+                const int64_t gn = n0 + (wn * NI + ni) * 32 + 8 * q + 4 * h;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (gn + e < n) yr[gn + e] = acc[mi][ni][4 * q + e];
             }
         }
+    }
+}
+
+// Dense GEMM: 128 x 128 tiles, 2 x 2 waves of 64 x 64.
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
+        const uint8_t* __restrict__ xq, int64_t m, float* __restrict__ y, int64_t ldy,
+        int tiles_m, int tiles_total) {
+    using T = Tile<2, 2, 2, 2>;
+    __shared__ __align__(16) Smem<T::BM, 128> s;
+    // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin,
+    // so give each XCD a contiguous run of tiles (the M tiles of one weight
+    // tile then share that XCD's L2).
+    const int G = gridDim.x, g = blockIdx.x;
+    const int per_xcd = G / 8;
+    const int tile = (g < 8 * per_xcd) ? (g % 8) * per_xcd + g / 8 : g;
+    if (tile >= tiles_total) return;
+    const int64_t m0 = static_cast<int64_t>(tile % tiles_m) * T::BM;
+    const int64_t n0 = static_cast<int64_t>(tile / tiles_m) * T::BN;
+    if (threadIdx.x < T::BM) {
+        const int64_t gm = m0 + threadIdx.x;
+        s.xrow[threadIdx.x] = gm < m ? static_cast<int>(gm) : -1;
+        s.yrow[threadIdx.x] = static_cast<int>(gm);
+    }
+    const int rows = static_cast<int>(m - m0 < T::BM ? m - m0 : T::BM);
+    mma_tile<FMT, 2, 2, 2, 2>(s, w, n, k, rb, n0, xq, rows, y, ldy);
+}
+
+// Grouped expert GEMM: workgroup (n tile, expert); 64 x 128 tiles, 1 x 4
+// waves of 64 x 32, looping over the expert's rows 64 at a time.  The
+// activation rows are gathered through the grouped pair list.
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
+        const uint8_t* __restrict__ xq, int x_per_pair, const int32_t* __restrict__ offsets,
+        const int32_t* __restrict__ pairs, int np, int top_k, float* __restrict__ y, int64_t ldy) {
+    using T = Tile<1, 4, 2, 1>;
+    __shared__ __align__(16) Smem<T::BM, 128> s;
+    const int e = blockIdx.y;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * T::BN;
+    // defensive clamps: offsets and pairs come from device memory
+    int off = offsets[e], end = offsets[e + 1];
+    off = off < 0 ? 0 : (off > np ? np : off);
+    end = end < off ? off : (end > np ? np : end);
+    const uint8_t* we = w + static_cast<int64_t>(e) * n * rb;
+    for (int base = off; base < end; base += T::BM) {
+        const int rows = end - base < T::BM ? end - base : T::BM;
+        __syncthreads();  // the previous tile's epilogue has read xrow / yrow
+        if (threadIdx.x < T::BM) {
+            int xr = -1, yr = 0;
+            if (static_cast<int>(threadIdx.x) < rows) {
+                const int p = pairs[base + threadIdx.x];
+                if (p >= 0 && p < np) {
+                    xr = x_per_pair ? p : p / top_k;
+                    yr = p;
+                }
+            }
+            s.xrow[threadIdx.x] = xr;
+            s.yrow[threadIdx.x] = yr;
+        }
+        mma_tile<FMT, 1, 4, 2, 1>(s, we, n, k, rb, n0, xq, rows, y, ldy);
     }
 }
 
@@ -332,7 +404,7 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
     const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
     const int64_t qk = wt == T_Q4_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
-    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+    const int64_t tiles_m = (m + 127) / 128, tiles_n = (n + 127) / 128;
     const int64_t tiles = tiles_m * tiles_n;
     if (tiles > 0x7FFFFFFF) return -3;
     const dim3 g(static_cast<unsigned>(tiles)), b(kThreads);
@@ -344,6 +416,36 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_1: hipLaunchKernelGGL(gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q8_0: hipLaunchKernelGGL(gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q4_K: hipLaunchKernelGGL(gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
+        default: return -2;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int moe_shape_ok(int wt, int64_t n, int64_t k) {
+    (void)wt;
+    (void)n;
+    return (k % 256 == 0) ? 0 : -3;
+}
+
+int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                    const void* xq, int x_per_pair, const int32_t* offsets,
+                    const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
+                    int64_t ldy, hipStream_t stream) {
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
+    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t rb = k / qk * bs;
+    const int64_t tiles_n = (n + 127) / 128;
+    const int64_t np = n_tokens * top_k;
+    if (tiles_n > 0x7FFFFFFF || np > 0x7FFFFFFF) return -3;
+    const dim3 g(static_cast<unsigned>(tiles_n), static_cast<unsigned>(n_experts)), b(kThreads);
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    const uint8_t* xp = static_cast<const uint8_t*>(xq);
+    const int npi = static_cast<int>(np), tk = static_cast<int>(top_k);
+    switch (wt) {
+        case T_Q4_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q4_1: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q8_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q4_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         default: return -2;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;

@@ -126,13 +126,4 @@ int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, i
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-// ---- grouped expert GEMM: placeholder until the MFMA kernel lands -------
-int moe_shape_ok(int, int64_t, int64_t) { return 0; }
-
-int launch_moe_gemm(int, const void*, int64_t, int64_t, int64_t, const void*, int,
-                    const int32_t*, const int32_t*, int64_t, int64_t, float*, int64_t,
-                    hipStream_t) {
-    return -2;
-}
-
 }  // namespace cq

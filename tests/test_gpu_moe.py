@@ -1,0 +1,167 @@
+"""GPU parity of the routed expert FFN (lfm2moe shape: 256 tokens, hidden
+2048, 32 Q4_K experts with gate/up 1536 x 2048 and down 2048 x 1536, top 4).
+
+Checked stage by stage; every stage's inputs come from the oracle (or from
+the seeded generator), never from the GPU:
+  gate / up   grouped GEMM on the oracle's Q8_0 rows and grouping, against
+              the oracle's per-pair dots: |y - y_ref| <= 2e-5 * S;
+  down        grouped GEMM on the oracle's requantized SwiGLU output;
+  combine     slot-order combine of the oracle's expert outputs;
+then the whole GPU pipeline end to end against the oracle pipeline with a
+bound derived from the oracle's values, and the reduction to dense GEMMs
+when every token picks the same experts (bitwise)."""
+import functools
+
+import numpy as np
+import pytest
+
+import gguf_synth as gs
+from gpu_common import assert_close_to_oracle, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+C = gs.CONFIGS["q4_k_moe_ffn"]
+T, H, F, E, K = C["n_tokens"], C["hidden"], C["ffn"], C["n_experts"], C["top_k"]
+FMT = C["fmt"]
+
+
+@functools.lru_cache(maxsize=1)
+def inputs():
+    cfg = C["cfg"]
+    wg = gs.expert_weights(FMT, E, F, H, cfg, 0)
+    wu = gs.expert_weights(FMT, E, F, H, cfg, 1)
+    wd = gs.expert_weights(FMT, E, H, F, cfg, 2)
+    x = gs.activations(T, H, cfg)
+    ids, rw = gs.routing(T, E, K, cfg)
+    return wg, wu, wd, x, ids, rw
+
+
+@functools.lru_cache(maxsize=1)
+def oracle_pipeline():
+    import oracle as orc
+    wg, wu, wd, x, ids, rw = inputs()
+    xq = orc.quantize_q8_0(x)
+    g, sg = orc.moe_matmul(FMT, wg, E, F, H, xq, False, ids)
+    u, su = orc.moe_matmul(FMT, wu, E, F, H, xq, False, ids)
+    h = orc.swiglu(g.astype(np.float32), u.astype(np.float32))
+    hq = orc.quantize_q8_0(h)
+    d, sd = orc.moe_matmul(FMT, wd, E, H, F, hq, True, ids)
+    y, sy = orc.moe_combine(d, sd, rw)
+    offs, pairs = orc.moe_group(ids, E)
+    return dict(xq=xq, g=g, sg=sg, u=u, su=su, h=h, hq=hq, d=d, sd=sd, y=y, sy=sy,
+                offs=offs, pairs=pairs)
+
+
+def test_moe_gate_up(cq):
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    offs, pairs = to_dev(ref["offs"]), to_dev(ref["pairs"])
+    xq = to_dev(ref["xq"])
+    for name, w, yr, sr in (("gate", wg, ref["g"], ref["sg"]), ("up", wu, ref["u"], ref["su"])):
+        note("moe", name)
+        y = to_host(cq.cq_moe_gemm(FMT, to_dev(w), E, F, H, xq, False, offs, pairs, T, K))
+        r = assert_close_to_oracle(y, yr, sr, what=name)
+        print(f"{name}: max |err|/S = {r:.3e}")
+
+
+def test_moe_down(cq):
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    note("moe down")
+    y = to_host(cq.cq_moe_gemm(FMT, to_dev(wd), E, H, F, to_dev(ref["hq"]), True,
+                               to_dev(ref["offs"]), to_dev(ref["pairs"]), T, K))
+    r = assert_close_to_oracle(y, ref["d"], ref["sd"], what="down")
+    print(f"down: max |err|/S = {r:.3e}")
+
+
+def test_moe_combine_stage(cq, orc):
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    d32 = ref["d"].astype(np.float32)
+    note("moe combine stage")
+    y = to_host(cq.cq_moe_combine(to_dev(d32), to_dev(rw)))
+    y_ref, _ = orc.moe_combine(d32.astype(np.float64), None, rw)
+    mag, _ = orc.moe_combine(np.abs(d32).astype(np.float64), None, np.abs(rw))
+    assert np.all(np.abs(y - y_ref) <= 4 * 2.0 ** -24 * mag + 1e-30)
+
+
+def run_gpu_pipeline(cq, wg, wu, wd, x, ids, rw, want_stages=False):
+    xq = cq.cq_quantize_q8_0(to_dev(x))
+    offs, pairs = cq.cq_moe_group(to_dev(ids), E)
+    g = cq.cq_moe_gemm(FMT, to_dev(wg), E, F, H, xq, False, offs, pairs, T, K)
+    u = cq.cq_moe_gemm(FMT, to_dev(wu), E, F, H, xq, False, offs, pairs, T, K)
+    _, hq = cq.cq_swiglu_quantize_q8_0(g, u)
+    d = cq.cq_moe_gemm(FMT, to_dev(wd), E, H, F, hq, True, offs, pairs, T, K)
+    y = cq.cq_moe_combine(d, to_dev(rw))
+    return to_host(y)
+
+
+def test_moe_end_to_end(cq):
+    """The whole GPU pipeline against the oracle pipeline.  Requantizing h can
+    move a quant by one step where the GPU's h and the oracle's h straddle a
+    rounding boundary, so the bound adds, per pair, one quantization step of
+    every element of h (oracle scales) weighted by |W_down| -- a bound derived
+    from the oracle's values alone -- to the 2e-5 * S tolerance."""
+    import oracle as orc
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    note("moe end to end")
+    y = run_gpu_pipeline(cq, wg, wu, wd, x, ids, rw)
+    # |W_down| * (one quant step of h per element) via the oracle's own dots:
+    # quantization step of each h block = its fp16 scale d
+    hq = ref["hq"].reshape(T * K, F // 32, 34)
+    dh = orc.half_to_double(hq[:, :, :2].copy().view(np.uint16)).reshape(T * K, F // 32)
+    # per element of h: |h_gpu - h_ref| is at most the propagated gate/up
+    # error (|dh/dg| <= 1.1|u|, |dh/du| = |silu(g)|) plus fp32 rounding; the two
+    # requantizations then differ by at most that plus one quant step
+    g, u = ref["g"], ref["u"]
+    silu = g / (1.0 + np.exp(-np.clip(g, -700.0, 700.0)))
+    dh_in = 1.1 * np.abs(u) * 2e-5 * ref["sg"] + np.abs(silu) * 2e-5 * ref["su"] \
+        + 2.0 ** -22 * np.abs(ref["h"].astype(np.float64))
+    step = 1.01 * np.repeat(dh, 32, axis=1) + dh_in                       # [pairs][F]
+    wabs = np.stack([np.abs(orc.dequantize(FMT, wd[r], F)) for r in range(E * H)]).reshape(E, H, F)
+    flip = np.zeros((T * K, H))
+    e_of = ids.reshape(-1)
+    for p in range(T * K):
+        flip[p] = wabs[e_of[p]] @ step[p]
+    flip_tok = (np.abs(rw.astype(np.float64)).reshape(T, K, 1) * flip.reshape(T, K, H)).sum(axis=1)
+    err = np.abs(y - ref["y"])
+    bound = 2e-5 * ref["sy"] + flip_tok
+    ratio = err / np.maximum(bound, 1e-300)
+    print(f"end to end: max err/bound = {ratio.max():.3e}, max err/S = {(err / ref['sy']).max():.3e}")
+    assert np.all(err <= bound)
+
+
+def test_moe_reduces_to_dense(cq, orc):
+    """Every token routed to the same experts: each grouped projection must
+    equal the dense GEMM with that expert's weights, bitwise."""
+    wg, wu, wd, x, ids, rw = inputs()
+    tok = 100
+    ids2 = np.tile(np.array([[5, 17, 2, 31]], np.int32), (tok, 1))
+    xq = cq.cq_quantize_q8_0(to_dev(x[:tok]))
+    note("moe dense reduction")
+    offs, pairs = cq.cq_moe_group(to_dev(ids2), E)
+    g = to_host(cq.cq_moe_gemm(FMT, to_dev(wg), E, F, H, xq, False, offs, pairs, tok, K))
+    rb = gs.row_bytes(FMT, H)
+    for s, e in enumerate([5, 17, 2, 31]):
+        yd = to_host(cq.cq_gemm(FMT, to_dev(wg[e * F:(e + 1) * F]), F, H, xq, tok))
+        assert np.array_equal(g[s::K], yd), e
+    assert rb == wg.shape[1]
+
+
+@pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(1, 8, 2, 128, 256), (300, 4, 2, 200, 512),
+                                                          (64, 64, 1, 100, 256)])
+def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
+    """Empty experts, experts with more than one 64-row tile, n not a
+    multiple of 128, per-pair and per-token activation rows."""
+    w = gs.expert_weights(FMT, n_experts, n, k, cfg=700 + n_tokens, which=0)
+    ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=700 + n_tokens)
+    for x_per_pair in (False, True):
+        rows = n_tokens * top_k if x_per_pair else n_tokens
+        xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=701))
+        offs, pairs = orc.moe_group(ids, n_experts)
+        note("moe gemm shape", n_tokens, n_experts, top_k, n, k, x_per_pair)
+        y = to_host(cq.cq_moe_gemm(FMT, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
+                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y_ref, s_ref = orc.moe_matmul(FMT, w, n_experts, n, k, xq, x_per_pair, ids)
+        assert_close_to_oracle(y, y_ref, s_ref, what="moe shape")
