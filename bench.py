@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the LM-head, prefill-GEMM and routed-FFN measurements")
     return ap.parse_args()
 
 
@@ -115,6 +117,8 @@ def main():
     alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
     achieved = alg / (avg_ms * 1e-3) / 1e9
 
+    extra = None if args.no_extra else secondary(cq, gs, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host_w, x, n, k, B, args.cpu_seconds)
@@ -142,9 +146,118 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": alg},
         "cpu_baseline": cpu,
+        "other_workloads": extra,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+MFMA_I8_PEAK_TOPS = 5030.0
+
+
+def _burst_us(fn, reps, stream):
+    """Average duration of `reps` back-to-back calls, HIP events on the
+    launch stream around the whole burst."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def secondary(cq, gs, dev, stream):
+    """The other workloads, each timed as a burst of back-to-back launches
+    (weights rotated through >= 512 MB of copies where they would fit the
+    Infinity Cache): the 128K-vocabulary Q4_K LM head at batch 1 and 4, the
+    2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens, and
+    the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
+    down, combine)."""
+    import torch
+    out = {}
+
+    def copies(host, min_bytes=512 * 2**20):
+        base = torch.from_numpy(host).to(dev)
+        ncopy = max(2, -(-min_bytes // host.nbytes) + 1)
+        return [base] + [base.clone() for _ in range(ncopy - 1)]
+
+    # LM head
+    n, k = 128256, 4096
+    wl = copies(gs.weights(gs.Q4_K, n, k, cfg=2))
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(4, k, cfg=2)).to(dev))
+    y = torch.empty((4, n), dtype=torch.float32, device=dev)
+    for b in (1, 4):
+        us = _burst_us(lambda i: cq.cq_gemv(gs.Q4_K, wl[i % len(wl)], n, k, xq, b, y=y), 50, stream)
+        gbs = wl[0].numel() / us / 1e3
+        out[f"q4_k_lm_head_128256x4096_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    del wl
+    # 2048 x 2048 Q4_0 GEMV (2.36 MB per call: launch-latency bound)
+    n, k = 2048, 2048
+    w0 = copies(gs.weights(gs.Q4_0, n, k, cfg=0))
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(1, k, cfg=0)).to(dev))
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    us = _burst_us(lambda i: cq.cq_gemv(gs.Q4_0, w0[i % len(w0)], n, k, xq, 1, y=y), 400, stream)
+    gbs = w0[0].numel() / us / 1e3
+    out["q4_0_gemv_2048x2048_b1"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                     "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    del w0
+    # prefill GEMM
+    n, k = 14336, 4096
+    wg = torch.from_numpy(gs.weights(gs.Q4_0, n, k, cfg=3)).to(dev)
+    for m in (512, 2048):
+        xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=3)).to(dev))
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        us = _burst_us(lambda i: cq.cq_gemm(gs.Q4_0, wg, n, k, xq, m, y=y), 20, stream)
+        tops = 2 * m * n * k / us / 1e6
+        out[f"q4_0_gemm_{m}x14336x4096"] = {"us": round(us, 2), "TOPS": round(tops, 1),
+                                            "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
+    del wg
+    # routed FFN
+    c = gs.CONFIGS["q4_k_moe_ffn"]
+    T, H, F, E, K = c["n_tokens"], c["hidden"], c["ffn"], c["n_experts"], c["top_k"]
+    mats = [gs.expert_weights(gs.Q4_K, E, F, H, 4, 0), gs.expert_weights(gs.Q4_K, E, F, H, 4, 1),
+            gs.expert_weights(gs.Q4_K, E, H, F, 4, 2)]
+    wbytes = sum(m_.nbytes for m_ in mats)
+    sets = [[torch.from_numpy(m_).to(dev) for m_ in mats]]
+    while len(sets) * wbytes < 512 * 2**20 + wbytes:
+        sets.append([t.clone() for t in sets[0]])
+    x = torch.from_numpy(gs.activations(T, H, 4)).to(dev)
+    ids, rw = gs.routing(T, E, K, 4)
+    ids, rw = torch.from_numpy(ids).to(dev), torch.from_numpy(rw).to(dev)
+    xq = torch.empty((T, H // 32 * 34), dtype=torch.uint8, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(T * K, dtype=torch.int32, device=dev)
+    g = torch.empty((T * K, F), dtype=torch.float32, device=dev)
+    u = torch.empty_like(g)
+    hq = torch.empty((T * K, F // 32 * 34), dtype=torch.uint8, device=dev)
+    d = torch.empty((T * K, H), dtype=torch.float32, device=dev)
+    yt = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def ffn(i):
+        wg_, wu_, wd_ = sets[i % len(sets)]
+        cq.cq_quantize_q8_0(x, xq)
+        cq.cq_moe_group(ids, E, offs, pairs)
+        cq.cq_moe_gemm(gs.Q4_K, wg_, E, F, H, xq, False, offs, pairs, T, K, y=g)
+        cq.cq_moe_gemm(gs.Q4_K, wu_, E, F, H, xq, False, offs, pairs, T, K, y=u)
+        cq.cq_swiglu_quantize_q8_0(g, u, hq=hq)
+        cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq, True, offs, pairs, T, K, y=d)
+        cq.cq_moe_combine(d, rw, y=yt)
+
+    us = _burst_us(ffn, 50, stream)
+    ops = 2 * T * K * (2 * F * H + H * F)
+    out["q4_k_moe_ffn_256tok_32x_top4"] = {
+        "us": round(us, 2), "expert_weight_GB/s": round(wbytes / us / 1e3, 1),
+        "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+        "int8_TOPS": round(ops / us / 1e6, 1),
+        "pct_int8_mfma_peak": round(100 * ops / us / 1e6 / MFMA_I8_PEAK_TOPS, 2)}
+    return out
 
 
 def cpu_baseline(host_w, x, n, k, B, seconds):
