@@ -392,6 +392,279 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(
     }
 }
 
+// ---- streaming grouped GEMM for Q4_K expert weights ---------------------------
+// The routed FFN is bound by streaming each expert's weights once, so here
+// the weights sit on the MFMA's B side (columns = weight rows) and every lane
+// loads its own weight row straight from HBM into registers.  With
+// v_mfma_i32_16x16x32_i8 a lane (row j = lane%16, quarter g = lane/16) holds
+// 8 of the 32 values of a block, so for super-block s it loads the 16-byte
+// header and bytes [8g, 8g+8) of each of the four 32-byte nibble chunks:
+// exactly the B operands of the eight sub-block MFMAs (low nibbles give
+// sub-block 2c, high nibbles 2c+1).  The next super-block's loads are issued
+// before the current one is computed; no barrier is involved.  The expert's
+// gathered Q8_0 activation rows (up to 64 per pass, in 16-row MFMA tiles so
+// padding stays small) are the A side, split per super-block into a
+// double-buffered LDS tile by all 256 threads (one barrier per super-block).
+// Per sub-block: D = mfma(act, w) from the float bias, t = fma(D, d*sc,
+// -12582912*d*sc) = round(I*d*sc) (exact subtrahend: d*sc has 17 significant
+// bits), acc = fma(t, dx, acc); the -dmin*m * dx*sum(qx) term goes through
+// v_mfma_f32_16x16x4_f32, four sub-blocks at a time.
+constexpr int kSbTok = 64;             // tokens per pass
+constexpr int kSbRow = 8 * 32 + 16;    // LDS row stride of the activation tile
+constexpr int kSbRows = 64;            // weight rows per workgroup (16 per wave)
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct ActTile {
+    int8_t x[kSbTok * kSbRow];
+    float dx[8][kSbTok];
+    float sx[8][kSbTok];
+};
+
+struct StreamSmem {
+    ActTile t[2];
+    int xrow[kSbTok];
+    int yrow[kSbTok];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct ARegs {            // two Q8_0 activation blocks (68 bytes)
+    u32x4 v[4];
+    uint32_t t;
+};
+
+struct WRegs {            // one lane's share of one Q4_K super-block
+    u32x4 hdr;            // d, dmin, 12 scale bytes
+    u32x2 q[4];           // 8 bytes of each 32-byte nibble chunk
+};
+
+// Load activation blocks 2q, 2q+1 of super-block sb for tile row r (thread
+// t: r = t/4, q = t%4).  Unconditional: a row that holds no pair reads token
+// row 0 instead, and its outputs are never stored.  (A load under a branch is
+// merged with the other branch's value by a register copy, which waits for
+// the load at once.)
+__device__ __forceinline__ void issue_acts(const StreamSmem& s, const uint8_t* __restrict__ xq,
+                                           int64_t xrb, int sb, ARegs& a) {
+    const int t = threadIdx.x, r = t >> 2, q = t & 3;
+    const int gm = s.xrow[r];
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(
+        xq + static_cast<int64_t>(gm < 0 ? 0 : gm) * xrb + (static_cast<int64_t>(sb) * 8 + 2 * q) * 34);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.v[i] = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+    a.t = p[16];
+}
+
+// Load super-block sb of this lane's weight row (a lane past the last row
+// reads row 0 of the expert and stores nothing).
+__device__ __forceinline__ void issue_w(const uint8_t* __restrict__ row, int sb, int g, WRegs& r) {
+    const uint8_t* p = row + static_cast<int64_t>(sb) * 144;
+    r.hdr = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const u32x2*>(p + 16 + 32 * c + 8 * g);
+}
+
+// Split two loaded blocks into the tile: int8 values, dx and dx*sum(q).
+__device__ __forceinline__ void store_acts(ActTile& at, const ARegs& a) {
+    const int t = threadIdx.x, r = t >> 2, q = t & 3;
+    uint32_t v[17];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[4 * i] = a.v[i].x;
+        v[4 * i + 1] = a.v[i].y;
+        v[4 * i + 2] = a.v[i].z;
+        v[4 * i + 3] = a.v[i].w;
+    }
+    v[16] = a.t;
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl) {
+        const int b = 2 * q + bl;
+        uint32_t o[8];
+        extract<8>(v, bl * 34 + 2, o);
+        const float dx = h2f(half_at(v, bl * 34));
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum = sdot4(o[i], 0x01010101u, sum);
+        at.dx[b][r] = dx;
+        at.sx[b][r] = dx * static_cast<float>(sum);
+        uint4* d4 = reinterpret_cast<uint4*>(at.x + r * kSbRow + 32 * b);
+        d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+__device__ __forceinline__ void q4k_scale_min(const u32x4& hdr, int j, int& sc, int& mn) {
+    if (j < 4) {
+        sc = (hdr.y >> (8 * j)) & 63;
+        mn = (hdr.z >> (8 * j)) & 63;
+    } else {
+        const int sh = 8 * (j - 4);
+        sc = ((hdr.w >> sh) & 0xF) | ((((hdr.y >> sh) >> 6) & 3) << 4);
+        mn = (((hdr.w >> sh) >> 4) & 0xF) | ((((hdr.z >> sh) >> 6) & 3) << 4);
+    }
+}
+
+constexpr int kStreamThreads = 256;    // 4 waves x 16 weight rows; 4 stagers per token row
+static_assert(kStreamThreads == 4 * kSbTok, "every thread stages two activation blocks");
+
+struct StreamLane {
+    const uint8_t* wrow;   // this lane's weight row (expert already applied)
+    bool row_ok;
+    int g, j16;            // lane / 16 and lane % 16
+    int64_t gn;            // this lane's weight row index
+};
+
+// One super-block: MT 16-token tiles against this wave's 16 weight rows.
+template <int MT>
+__device__ __forceinline__ void stream_sb(const ActTile& at, const WRegs& cur, const StreamLane& L,
+                                          const v4i& bias, v4f (&acc)[MT]) {
+    const float d = h2f(cur.hdr.x & 0xFFFFu), dmin = h2f(cur.hdr.x >> 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x2 qv = cur.q[c];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const int j = 2 * c + e2;         // sub-block = local block index
+            const long Bw = static_cast<long>(
+                (static_cast<uint64_t>(((e2 ? qv.y >> 4 : qv.y) & 0x0F0F0F0Fu)) << 32) |
+                ((e2 ? qv.x >> 4 : qv.x) & 0x0F0F0F0Fu));
+            int sc, mn;
+            q4k_scale_min(cur.hdr, j, sc, mn);
+            const float dwj = d * static_cast<float>(sc);
+            const float ndwj = -kBiasF * dwj;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const long A = *reinterpret_cast<const long*>(at.x + (16 * mt + L.j16) * kSbRow + 32 * j + 8 * L.g);
+                const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bw, bias, 0, 0, 0);
+                const float4 dx = *reinterpret_cast<const float4*>(&at.dx[j][16 * mt + 4 * L.g]);
+                acc[mt][0] = fmaf(fmaf(__int_as_float(D[0]), dwj, ndwj), dx.x, acc[mt][0]);
+                acc[mt][1] = fmaf(fmaf(__int_as_float(D[1]), dwj, ndwj), dx.y, acc[mt][1]);
+                acc[mt][2] = fmaf(fmaf(__int_as_float(D[2]), dwj, ndwj), dx.z, acc[mt][2]);
+                acc[mt][3] = fmaf(fmaf(__int_as_float(D[3]), dwj, ndwj), dx.w, acc[mt][3]);
+            }
+        }
+    }
+    // -dmin*m * dx*sum(qx): A = dx*sum(q) [tokens][4 sub-blocks],
+    // B = -dmin*m [4 sub-blocks][weight rows]
+#pragma unroll
+    for (int j4 = 0; j4 < 8; j4 += 4) {
+        int sc, mn;
+        q4k_scale_min(cur.hdr, j4 + L.g, sc, mn);      // sub-block j4 + g of this lane's row
+        const float bm = -(dmin * static_cast<float>(mn));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float ax = at.sx[j4 + L.g][16 * mt + L.j16];
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax, bm, acc[mt], 0, 0, 0);
+        }
+    }
+}
+
+// One pass over up to 16*MT gathered token rows (row maps already in LDS).
+// Weight super-block sb is loaded into register set sb % 3 two steps before it
+// is used; the sets rotate by unrolling, so no set is copied.  The loads for
+// later super-blocks are written before the compute of the current one; past
+// the last super-block they repeat the current one and the store fills the
+// idle tile, so no load or store sits under a branch.
+template <int MT>
+__device__ __forceinline__ void stream_pass(StreamSmem& s, const StreamLane& L, int nsb,
+                                            const uint8_t* __restrict__ xq, int64_t xrb, int rows,
+                                            float* __restrict__ y, int64_t ldy) {
+    v4i bias;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = kBias;
+    ARegs av;
+    WRegs w0, w1, w2;
+    issue_acts(s, xq, xrb, 0, av);
+    issue_w(L.wrow, 0, L.g, w0);
+    issue_w(L.wrow, nsb > 1 ? 1 : 0, L.g, w1);
+    store_acts(s.t[0], av);
+    __syncthreads();
+
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][r] = 0.0f;
+
+#define CQ_STREAM_STEP(SB, CUR, FILL)                                             \
+    {                                                                                   \
+        const int sb_ = (SB);                                                           \
+        issue_acts(s, xq, xrb, sb_ + 1 < nsb ? sb_ + 1 : sb_, av);                      \
+        issue_w(L.wrow, sb_ + 2 < nsb ? sb_ + 2 : sb_, L.g, FILL);                      \
+        stream_sb<MT>(s.t[sb_ & 1], CUR, L, bias, acc);                                 \
+        store_acts(s.t[(sb_ + 1) & 1], av);                                             \
+        __syncthreads();                                                                \
+    }
+    for (int sb = 0; sb < nsb; sb += 3) {
+        CQ_STREAM_STEP(sb, w0, w2)
+        if (sb + 1 >= nsb) break;
+        CQ_STREAM_STEP(sb + 1, w1, w0)
+        if (sb + 2 >= nsb) break;
+        CQ_STREAM_STEP(sb + 2, w2, w1)
+    }
+#undef CQ_STREAM_STEP
+    // epilogue: lane = weight row gn, register r = token row 4g + r of tile mt
+    if (L.row_ok) {
+        const int lim = rows - 4 * L.g;           // token row 4g + c is live when c < lim
+        const int* xr = s.xrow + 4 * L.g;
+        const int* yr = s.yrow + 4 * L.g;
+        float* yc = y + L.gn;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = 16 * mt + r;
+                if (c < lim && xr[c] >= 0) yc[static_cast<int64_t>(yr[c]) * ldy] = acc[mt][r];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kStreamThreads, 3) void moe_stream_q4k_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
+        const uint8_t* __restrict__ xq, int x_per_pair, const int32_t* __restrict__ offsets,
+        const int32_t* __restrict__ pairs, int np, int top_k, float* __restrict__ y, int64_t ldy) {
+    __shared__ __align__(16) StreamSmem s;
+    const int e = blockIdx.y;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    StreamLane L;
+    L.j16 = lane & 15;
+    L.g = lane >> 4;
+    L.gn = static_cast<int64_t>(blockIdx.x) * kSbRows + 16 * wv + L.j16;
+    L.row_ok = L.gn < n;
+    L.wrow = w + (static_cast<int64_t>(e) * n + (L.row_ok ? L.gn : 0)) * rb;
+    const int nsb = static_cast<int>(k / 256);
+    const int64_t xrb = k / 32 * 34;
+    int off = offsets[e], end = offsets[e + 1];
+    off = off < 0 ? 0 : (off > np ? np : off);
+    end = end < off ? off : (end > np ? np : end);
+
+    for (int base = off; base < end; base += kSbTok) {
+        const int rows = end - base < kSbTok ? end - base : kSbTok;
+        __syncthreads();  // the previous pass is done with the tile and row maps
+        if (threadIdx.x < kSbTok) {
+            int xr = -1, yr = 0;
+            if (static_cast<int>(threadIdx.x) < rows) {
+                const int p = pairs[base + threadIdx.x];
+                if (p >= 0 && p < np) {
+                    xr = x_per_pair ? p : p / top_k;
+                    yr = p;
+                }
+            }
+            s.xrow[threadIdx.x] = xr;
+            s.yrow[threadIdx.x] = yr;
+        }
+        __syncthreads();
+        switch ((rows + 15) >> 4) {     // 16-token tiles holding real rows
+            case 1: stream_pass<1>(s, L, nsb, xq, xrb, rows, y, ldy); break;
+            case 2: stream_pass<2>(s, L, nsb, xq, xrb, rows, y, ldy); break;
+            case 3: stream_pass<3>(s, L, nsb, xq, xrb, rows, y, ldy); break;
+            default: stream_pass<4>(s, L, nsb, xq, xrb, rows, y, ldy); break;
+        }
+    }
+}
+
 }  // namespace
 
 int gemm_shape_ok(int wt, int64_t k) {
@@ -445,7 +718,11 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
         case T_Q4_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q4_1: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q8_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
-        case T_Q4_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q4_K: {
+            const dim3 gs(static_cast<unsigned>((n + kSbRows - 1) / kSbRows), static_cast<unsigned>(n_experts));
+            hipLaunchKernelGGL(moe_stream_q4k_kernel, gs, dim3(kStreamThreads), 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);
+            break;
+        }
         default: return -2;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;
