@@ -122,11 +122,16 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = a[j].start;  // kBias + sum (q-8)*qx = kBias + sum q*qx - 8*sum qx
+            // kBias + sum (q-8)*qx = kBias + sum q*qx - 8*sum qx (at batch 1
+            // as two chains, low and high nibbles, joined at the end)
+            int s = a[j].start, s1 = 0;
+            int& s2 = B == 1 ? s1 : s;  // a second chain only at batch 1
 #pragma unroll
-            for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(lo[t], a[j].q[t], s);
+                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);  // sum * dx
             acc[j] = fmaf(sx, dw, acc[j]);
         }
@@ -143,11 +148,14 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = kBias;
+            int s = kBias, s1 = 0;  // a second chain only at batch 1
+            int& s2 = B == 1 ? s1 : s;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) s = sdot4(lo[t], a[j].q[t], s);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s = sdot4(hi[t], a[j].q[4 + t], s);
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(lo[t], a[j].q[t], s);
+                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
             // dx * (d * sum(q*qx) + m * sum(qx))
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(mw, a[j].sdx, fmaf(sx, dw, acc[j]));
@@ -158,9 +166,14 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         lds_dwords_a2<8>(lds, off + 2, q);
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = kBias;
+            int s = kBias, s1 = 0;  // a second chain only at batch 1
+            int& s2 = B == 1 ? s1 : s;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) s = sdot4(q[t], a[j].q[t], s);
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(q[t], a[j].q[t], s);
+                s2 = sdot4(q[4 + t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(sx, dw, acc[j]);
         }
@@ -198,11 +211,20 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int sa = kBias, sb = kBias;
+            int sa = kBias, sb = kBias, sa1 = 0, sb1 = 0;  // four chains at batch 1
+            int& sa2 = B == 1 ? sa1 : sa;
+            int& sb2 = B == 1 ? sb1 : sb;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) sa = sdot4(lo[t], a[j].qa[t], sa);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) sb = sdot4(hi[t], a[j].qb[t], sb);
+            for (int t = 0; t < 4; ++t) {
+                sa = sdot4(lo[t], a[j].qa[t], sa);
+                sb = sdot4(hi[t], a[j].qb[t], sb);
+                sa2 = sdot4(lo[4 + t], a[j].qa[4 + t], sa2);
+                sb2 = sdot4(hi[4 + t], a[j].qb[4 + t], sb2);
+            }
+            if (B == 1) {
+                sa += sa1;
+                sb += sb1;
+            }
             // dx*(d*sc*sum(q*qx) - dmin*m*sum(qx)) for each sub-block
             const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
             const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
@@ -322,22 +344,31 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
 // ---- single-wave variant: one wave covers all of k (every lane owns its
 // columns), so waves never wait for each other.  Each wave streams its row
 // tiles HBM -> LDS with LDS-DMA (global_load_lds_dwordx4: 16 bytes per lane,
-// 1 KiB per instruction, no VGPRs) through a ring of three wave-private
-// buffers: while tile t is computed, tiles t+1 and t+2 are in flight.
+// 1 KiB per instruction, no VGPRs) through a ring of kRing wave-private
+// buffers: while tile t is computed, tiles t+1 .. t+kRing-1 are in flight.
+// The weights are read once, so the DMA carries the non-temporal hint.
 //
-// Wait accounting: every tile is exactly kDmaVec DMA instructions (lanes
-// past the tile re-load the tile's first 16 bytes into the buffer's unused
-// tail) and every processed tile issues exactly one global store, so the
-// number of vector-memory operations issued after a tile's DMA is a
+// Wait accounting: every tile is exactly kDmaVec DMA instructions, each with
+// at least one active lane (lanes past the tile are masked off; an
+// instruction wholly past it re-loads the tile's first KiB onto the buffer's
+// first KiB), and every processed tile issues exactly one global store, so
+// the number of vector-memory operations issued after a tile's DMA is a
 // compile-time constant and an explicit s_waitcnt vmcnt(N) suffices.  The
 // DMA is issued from inline assembly: the compiler then does not model it,
 // and places no waits of its own for it (its waits for its own loads can
 // only become more conservative); all waits for the DMA are the explicit
 // ones below.
-constexpr int kDmaVec = 10;                        // 1-KiB DMA instructions per tile
-constexpr int kDmaTileBytes = kDmaVec * 1024;
-constexpr int kDmaBufBytes = kDmaTileBytes + 64;   // + read slack
-constexpr int kWavesPerCu = 4;                     // one per SIMD; 3 buffers each: 4 * 31 KiB of LDS
+constexpr int kRing = 2;                           // buffers per wave
+constexpr int kTileCap = 9232;                     // tile bytes incl. up to 15 lead bytes
+constexpr int kDmaVec = (kTileCap + 1023) / 1024;  // 1-KiB DMA instructions per tile
+constexpr int kDmaBufBytes = kTileCap + 64;        // + read slack past the last block
+constexpr int kWavesPerCu = 8;                     // most waves per CU (kRing buffers each)
+// waves per CU launched: Q8_0's per-tile work (two unaligned 34-byte blocks
+// per lane and row) runs best with six, the others with eight
+template <int FMT> constexpr int kWaveGrid = FMT == T_Q8_0 ? 6 : kWavesPerCu;
+static_assert(kRing >= 2 && kRing <= 4, "ring depth");
+static_assert(kRing * kWavesPerCu * kDmaBufBytes <= 160 * 1024, "LDS per CU");
+static_assert(kDmaVec * 64 * 16 >= kTileCap && (kDmaVec - 1) * 1024 < kTileCap, "instruction count");
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {      // s_waitcnt vmcnt(N)
@@ -352,33 +383,43 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
 }
 
-// One LDS-DMA instruction: lane i copies the 16 bytes at gaddr (its own)
-// to LDS[lds_base + 16*i]; lds_base must be wave-uniform.  M0 carries the
-// LDS base; it is saved and restored around the instruction, with one wait
-// state between the M0 write and the DMA that reads it.
+// One LDS-DMA instruction: each active lane copies the 16 bytes at gaddr (its
+// own) to LDS[lds_base + 16*lane]; lds_base must be wave-uniform.  M0 carries
+// the LDS base; it is saved and restored around the instruction, with one
+// wait state between the M0 write and the DMA that reads it.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(gaddr), "s"(lds_base)
         : "memory");
 }
 
-// Stage bytes [a0, a0 + 16*nvec) of w (a0 16-aligned, a0 + 16*nvec <= size
-// of w) into buf with exactly kDmaVec DMA instructions.
+// Stage bytes [a0, a0 + 16*nvec) of w (a0 16-aligned, 1 <= nvec,
+// 16*nvec <= kTileCap, a0 + 16*nvec <= size of w) into buf with exactly
+// kDmaVec DMA instructions.  Instruction u covers vectors 64u .. 64u+63 with
+// the lanes past nvec masked off; an instruction with 64u >= nvec instead
+// re-loads the tile's own first vectors (lanes < nvec) onto the same bytes of
+// the buffer, so every instruction has lane 0 active and none writes past
+// 16*nvec.
 __device__ __forceinline__ void dma_tile(const uint8_t* __restrict__ w, int64_t a0, int nvec,
                                          uint8_t* buf, int lane) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(buf));
 #pragma unroll
     for (int u = 0; u < kDmaVec; ++u) {
-        const int v = u * kWave + lane;
-        const int64_t g = a0 + (v < nvec ? 16 * static_cast<int64_t>(v) : 0);
-        dma16(w + g, base + u * kWave * 16);
+        if (u * kWave < nvec) {               // wave-uniform
+            const int v = u * kWave + lane;
+            if (v < nvec) dma16(w + a0 + 16 * static_cast<int64_t>(v), base + u * kWave * 16);
+        } else {
+            // the tile's first vectors again, onto the same bytes (lanes past
+            // nvec masked as above, lane 0 always active)
+            if (lane < nvec) dma16(w + a0 + 16 * static_cast<int64_t>(lane), base);
+        }
     }
 }
 
@@ -426,23 +467,18 @@ __global__ __launch_bounds__(kWave) void gemv_wave_kernel(
         const uint8_t* __restrict__ w, int64_t n, int64_t rb, int ncols, int C,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy) {
-    __shared__ __align__(16) uint8_t buf0[kDmaBufBytes];
-    __shared__ __align__(16) uint8_t buf1[kDmaBufBytes];
-    __shared__ __align__(16) uint8_t buf2[kDmaBufBytes];
+    __shared__ __align__(16) uint8_t ring[kRing][kDmaBufBytes];
     const int lane = threadIdx.x;
 
     constexpr int CM = kCMax<FMT>;
-    Act<FMT> act[CM][B];
     int col[CM];
     bool valid[CM];
 #pragma unroll
     for (int i = 0; i < CM; ++i) {
         col[i] = i * kWave + lane;
         valid[i] = (i < C) && (col[i] < ncols);
-#pragma unroll
-        for (int j = 0; j < B; ++j)
-            if (valid[i]) load_act<FMT>(xq + j * xq_row_bytes, col[i], act[i][j]);
     }
+    Act<FMT> act[CM][B];  // loaded once the first tiles are in flight
 
     const int64_t G = gridDim.x;
     const int64_t ntiles = (n + RT - 1) / RT;
@@ -478,29 +514,51 @@ __global__ __launch_bounds__(kWave) void gemv_wave_kernel(
         }
         reduce_store<RT, B>(acc, rt, r0, y, ldy, lane);
     };
-    // tile i lives in buffer i % 3; step i issues tile i+2, waits for tile i
-    // (vector-memory operations issued after tile i's DMA: the store of
-    // tile i-2, DMA of tile i+1, store of tile i-1, DMA of tile i+2), then
-    // computes it.
+    // Tile i lives in buffer i % kRing.  Step i issues tile i+kRing-1 (into
+    // the buffer computed in step i-1), waits for tile i, computes it and
+    // stores its outputs.  Vector-memory operations issued after tile i's DMA
+    // by the time of that wait: the DMAs of tiles i+1 .. i+kRing-1 and the
+    // stores of the min(i, kRing-1) steps before i.  Once no tile is left to
+    // issue, the wait drains everything.
+    constexpr int kAhead = (kRing - 1) * kDmaVec;
     auto step = [&](int64_t i, const uint8_t* cur, uint8_t* nxt) {
-        if (i + 2 < nt) {
-            issue(i + 2, nxt);
-            if (i >= 2) wait_vmem<2 * kDmaVec + 2>();
-            else if (i == 1) wait_vmem<2 * kDmaVec + 1>();
-            else wait_vmem<2 * kDmaVec>();
+        if (i + kRing - 1 < nt) {
+            issue(i + kRing - 1, nxt);
+            const int64_t stores = i < kRing - 1 ? i : kRing - 1;
+            if (stores == 0) wait_vmem<kAhead>();
+            else if (stores == 1) wait_vmem<kAhead + 1>();
+            else if (stores == 2) wait_vmem<kAhead + 2>();
+            else wait_vmem<kAhead + 3>();
         } else {
             wait_vmem<0>();
         }
         process(i, cur);
     };
-    if (nt > 0) issue(0, buf0);
-    if (nt > 1) issue(1, buf1);
-    for (int64_t i = 0; i < nt; i += 3) {
-        step(i, buf0, buf2);
+#pragma unroll
+    for (int d = 0; d < kRing - 1; ++d)
+        if (d < nt) issue(d, ring[d]);
+    // the activations are loaded after the first tiles are in flight, so the
+    // latencies overlap (their loads only add completed operations to the
+    // counts above, which stay upper bounds).  Unconditional loads (an
+    // unused column reads column 0 and is never consumed) keep all of them in
+    // flight together.
+#pragma unroll
+    for (int i = 0; i < CM; ++i)
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            load_act<FMT>(xq + j * xq_row_bytes, valid[i] ? col[i] : 0, act[i][j]);
+    for (int64_t i = 0; i < nt; i += kRing) {
+        step(i, ring[0], ring[kRing - 1]);
         if (i + 1 >= nt) break;
-        step(i + 1, buf1, buf0);
-        if (i + 2 >= nt) break;
-        step(i + 2, buf2, buf1);
+        step(i + 1, ring[1], ring[0]);
+        if constexpr (kRing > 2) {
+            if (i + 2 >= nt) break;
+            step(i + 2, ring[2], ring[1]);
+        }
+        if constexpr (kRing > 3) {
+            if (i + 3 >= nt) break;
+            step(i + 3, ring[3], ring[2]);
+        }
     }
 }
 
@@ -522,9 +580,14 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool wave_ok) {
     while (rt > 1 && (rt * rb > 20480 || rt * batch > 32)) rt >>= 1;
     if (rt == 2) rt = 1;  // instantiated tiles: 1, 4, 8
     if (p.nw == 1 && wave_ok) {  // single-wave kernel: tiles bounded by its LDS buffers
-        rt = 8;
-        while (rt > 1 && (rt * rb + 15 > kDmaTileBytes || rt * batch > 32)) rt >>= 1;
-        p.wave = rt * rb + 15 <= kDmaTileBytes;
+        static constexpr int kRts[] = {8, 4, 3, 2, 1};
+        for (int cand : kRts) {
+            if (cand * rb + 15 <= kTileCap && cand * batch <= 32) {
+                rt = cand;
+                p.wave = true;
+                break;
+            }
+        }
     }
     p.RT = rt;
     p.tile_lds = static_cast<int>((rt * rb + 32 + 15) & ~15);
@@ -537,7 +600,7 @@ int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const u
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     if (p.wave) {
-        int64_t grid = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
+        int64_t grid = static_cast<int64_t>(device_cu_count()) * kWaveGrid<FMT>;
         if (grid > ntiles) grid = ntiles;
         const dim3 g(static_cast<unsigned>(grid)), b(kWave);
         switch (p.RT) {
@@ -550,6 +613,8 @@ int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const u
                     return -3;
                 }
             case 4: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 4>), g, b, 0, stream, w, n, rb,
+                                       p.ncols, p.C, xq, xrb, y, ldy); break;
+            case 3: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 3>), g, b, 0, stream, w, n, rb,
                                        p.ncols, p.C, xq, xrb, y, ldy); break;
             case 2: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 2>), g, b, 0, stream, w, n, rb,
                                        p.ncols, p.C, xq, xrb, y, ldy); break;
