@@ -11,7 +11,11 @@ the 256 MB Infinity Cache.
 Printed: one JSON line.  value = weight bytes streamed per step / step time
 (GB/s).  roofline: the Q8_0 batch-5 GEMV (the largest launch), algorithmic
 bytes (weights + activation blocks + outputs) over its average duration from
-HIP events recorded around each of its launches on the launch stream.
+HIP events recorded around each of its launches on the launch stream (these
+brackets also hold the kernel-boundary time, about 3 us, that the profiler's
+kernel duration leaves out; both are reported).  traffic: HBM bytes per launch
+from the committed rocprofv3 counter summary, null once the GEMV source has
+changed since it was taken.
 cpu_baseline: the CPU oracle on the same step (fp64 reference, not a tuned
 CPU kernel).
 """
@@ -25,6 +29,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+GEMV_SOURCES = ("quantized_gguf_block_amd/csrc/gemv.hip", "quantized_gguf_block_amd/csrc/cq_device.h")
+
+
+def gemv_source_sha():
+    import hashlib
+    m = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()
+
+
+def profiled(kernel):
+    """HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy of
+    known size) and profiled average duration of `kernel`, from the summaries
+    under profiles/ -- or None for each when the GEMV source has changed
+    since they were taken."""
+    sha = gemv_source_sha()
+    traffic = prof_us = None
+    try:
+        with open(os.path.join(ROOT, "profiles", "gemv_ffn_up_hbm_traffic.md")) as fh:
+            for line in fh:
+                if line.strip().startswith("TRAFFIC "):
+                    rec = json.loads(line.strip()[len("TRAFFIC "):])
+                    if rec["kernel"] == kernel and rec["source_sha256"] == sha:
+                        traffic = int(rec["traffic_bytes"])
+        with open(os.path.join(ROOT, "profiles", "gemv_ffn_up_q8_0_q4_1_kernel_stats.md")) as fh:
+            text = fh.read()
+        if sha in text:
+            for line in text.splitlines():
+                if line.startswith("| " + kernel):
+                    prof_us = float(line.split("|")[3])
+    except (OSError, ValueError, KeyError):
+        pass
+    return traffic, prof_us
 
 
 def parse():
@@ -117,6 +156,8 @@ def main():
     alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
     achieved = alg / (avg_ms * 1e-3) / 1e9
 
+    traffic, prof_us = profiled("gemv_wave_kernel<8, 5, 2>")
+
     extra = None if args.no_extra else secondary(cq, gs, dev, stream)
 
     cpu = None
@@ -141,10 +182,12 @@ def main():
                    "n": n, "k": k, "batches": [1, B], "formats": ["q8_0", "q4_1"],
                    "weight_copies": {gs.NAMES[f]: len(copies[f]) for f in fmts}},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<Q8_0, B=5>",
+        "roofline": {"bound": "hbm", "kernel": "gemv_wave_kernel<8, 5, 2> (Q8_0, batch 5)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": alg},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": alg,
+                     "traffic_over_alg": round(traffic / alg, 3) if traffic else None,
+                     "rocprof_avg_kernel_us": prof_us},
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "wall_s": round(wall, 3),
