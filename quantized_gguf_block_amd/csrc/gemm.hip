@@ -98,33 +98,56 @@ __device__ __forceinline__ uint32_t half_at(const uint32_t* w, int off) {
 
 // ---- staging of one k step --------------------------------------------------
 // Two threads per row: thread t stages row t/2, blocks 2*(t%2) and
-// 2*(t%2)+1 of the step.  All global loads are 4-byte loads.
-template <int FMT, class S>
-__device__ __forceinline__ void stage_weights(S& s, const uint8_t* __restrict__ w, int64_t n,
-                                              int64_t rb, int64_t n0, int kstep) {
+// 2*(t%2)+1 of the step.  Staging is split into the global loads (into
+// registers) and the decode into LDS, so the loads of step ks+1 are in flight
+// while step ks is computed.  The loads are unconditional: a weight row past
+// n reads row n-1 and a tile row without an activation row reads row 0; the
+// outputs of such rows are never stored.  (A load under a branch is merged
+// with the other branch's value by a register copy, which waits for it at
+// once.)
+template <int FMT> struct WRaw {      // two 32-value blocks of one row
+    static constexpr int BS = (FMT == T_Q4_0) ? 18 : (FMT == T_Q4_1) ? 20 : 34;
+    uint32_t v[(2 * BS) / 4];
+};
+template <> struct WRaw<T_Q4_K> {     // super-block header + one 32-byte chunk
+    uint32_t hdr[4], q[8];
+};
+struct XRaw {                         // two Q8_0 activation blocks
+    uint32_t v[17];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_weights(WRaw<FMT>& r, const uint8_t* __restrict__ w, int64_t n,
+                                             int64_t rb, int64_t n0, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
-    const int64_t gn = n0 + row;
+    const int64_t gn = n0 + row < n ? n0 + row : n - 1;
     if constexpr (FMT == T_Q4_K) {
         // a 256-value super-block spans two k steps; this step holds nibble
         // chunks 2*(kstep&1) and +1, this thread chunk c (sub-blocks 2c, 2c+1)
         const int c = 2 * (kstep & 1) + half;
-        uint32_t hdr[4], q[8];
-        if (gn < n) {
-            const uint8_t* p = w + gn * rb + static_cast<int64_t>(kstep >> 1) * 144;
-            const uint4 hv = *reinterpret_cast<const uint4*>(p);
-            hdr[0] = hv.x; hdr[1] = hv.y; hdr[2] = hv.z; hdr[3] = hv.w;
-            const uint4 v0 = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
-            q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
-            q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
-        } else {
+        const uint8_t* p = w + gn * rb + static_cast<int64_t>(kstep >> 1) * 144;
+        const uint4 hv = *reinterpret_cast<const uint4*>(p);
+        r.hdr[0] = hv.x; r.hdr[1] = hv.y; r.hdr[2] = hv.z; r.hdr[3] = hv.w;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+        r.q[0] = v0.x; r.q[1] = v0.y; r.q[2] = v0.z; r.q[3] = v0.w;
+        r.q[4] = v1.x; r.q[5] = v1.y; r.q[6] = v1.z; r.q[7] = v1.w;
+    } else {
+        constexpr int BS = WRaw<FMT>::BS;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(
+            w + gn * rb + (static_cast<int64_t>(kstep) * KB + 2 * half) * BS);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hdr[i] = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = 0;
-        }
-        const float d = h2f(hdr[0] & 0xFFFFu), dmin = h2f(hdr[0] >> 16);
-        const uint32_t S0 = hdr[1], S1 = hdr[2], S2 = hdr[3];
+        for (int i = 0; i < (2 * BS) / 4; ++i) r.v[i] = p[i];
+    }
+}
+
+template <int FMT, class S>
+__device__ __forceinline__ void store_weights(S& s, const WRaw<FMT>& r, int kstep) {
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+    if constexpr (FMT == T_Q4_K) {
+        const int c = 2 * (kstep & 1) + half;
+        const float d = h2f(r.hdr[0] & 0xFFFFu), dmin = h2f(r.hdr[0] >> 16);
+        const uint32_t S0 = r.hdr[1], S1 = r.hdr[2], S2 = r.hdr[3];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {             // sub-block j = 2c + e -> local block 2*half + e
             const int j = 2 * c + e;
@@ -142,35 +165,24 @@ __device__ __forceinline__ void stage_weights(S& s, const uint8_t* __restrict__ 
             s.cw[b][row] = -(dmin * static_cast<float>(mn));
             uint32_t o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = e ? nib_hi(q[i]) : nib_lo(q[i]);
+            for (int i = 0; i < 8; ++i) o[i] = e ? nib_hi(r.q[i]) : nib_lo(r.q[i]);
             uint4* d4 = reinterpret_cast<uint4*>(s.w + row * ROW + 32 * b);
             d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
             d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
     } else {
-        constexpr int BS = (FMT == T_Q4_0) ? 18 : (FMT == T_Q4_1) ? 20 : 34;
-        constexpr int NW = (2 * BS) / 4;          // dwords of 2 blocks
-        uint32_t v[NW];
-        if (gn < n) {
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(
-                w + gn * rb + (static_cast<int64_t>(kstep) * KB + 2 * half) * BS);
-#pragma unroll
-            for (int i = 0; i < NW; ++i) v[i] = p[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < NW; ++i) v[i] = 0;
-        }
+        constexpr int BS = WRaw<FMT>::BS;
 #pragma unroll
         for (int bl = 0; bl < 2; ++bl) {
             const int b = 2 * half + bl;
             uint32_t o[8];
-            s.dw[b][row] = h2f(half_at(v, bl * BS));
+            s.dw[b][row] = h2f(half_at(r.v, bl * BS));
             if constexpr (FMT == T_Q8_0) {
-                extract<8>(v, bl * BS + 2, o);
+                extract<8>(r.v, bl * BS + 2, o);
             } else {
                 uint32_t q[4];
-                extract<4>(v, bl * BS + (FMT == T_Q4_0 ? 2 : 4), q);
-                if constexpr (FMT == T_Q4_1) s.cw[b][row] = h2f(half_at(v, bl * BS + 2));
+                extract<4>(r.v, bl * BS + (FMT == T_Q4_0 ? 2 : 4), q);
+                if constexpr (FMT == T_Q4_1) s.cw[b][row] = h2f(half_at(r.v, bl * BS + 2));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     o[i] = (FMT == T_Q4_0) ? nib_lo_s8(q[i]) : nib_lo(q[i]);
@@ -185,29 +197,29 @@ __device__ __forceinline__ void stage_weights(S& s, const uint8_t* __restrict__ 
 }
 
 // Activations: threads t < 2*BM stage tile row t/2 (activation row
-// s.xrow[t/2], -1 = zeros), blocks 2*(t%2) and +1 of the step.
-template <int FMT, int BM, class S>
-__device__ __forceinline__ void stage_acts(S& s, const uint8_t* __restrict__ xq, int64_t xrb,
-                                           int kstep) {
+// s.xrow[t/2]), blocks 2*(t%2) and +1 of the step.
+template <int BM, class S>
+__device__ __forceinline__ void load_acts(XRaw& r, const S& s, const uint8_t* __restrict__ xq,
+                                          int64_t xrb, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
-    if (row >= BM) return;
-    const int gm = s.xrow[row];
-    uint32_t v[17];  // 2 blocks x 34 bytes
-    if (gm >= 0) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(
-            xq + static_cast<int64_t>(gm) * xrb + (static_cast<int64_t>(kstep) * KB + 2 * half) * 34);
+    if (2 * BM < kThreads && row >= BM) return;
+    const int gm = s.xrow[row] < 0 ? 0 : s.xrow[row];
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(
+        xq + static_cast<int64_t>(gm) * xrb + (static_cast<int64_t>(kstep) * KB + 2 * half) * 34);
 #pragma unroll
-        for (int i = 0; i < 17; ++i) v[i] = p[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 17; ++i) v[i] = 0;
-    }
+    for (int i = 0; i < 17; ++i) r.v[i] = p[i];
+}
+
+template <int FMT, int BM, class S>
+__device__ __forceinline__ void store_acts(S& s, const XRaw& r) {
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+    if (2 * BM < kThreads && row >= BM) return;
 #pragma unroll
     for (int bl = 0; bl < 2; ++bl) {
         const int b = 2 * half + bl;
         uint32_t o[8];
-        extract<8>(v, bl * 34 + 2, o);
-        const float dx = h2f(half_at(v, bl * 34));
+        extract<8>(r.v, bl * 34 + 2, o);
+        const float dx = h2f(half_at(r.v, bl * 34));
         s.dx[b][row] = dx;
         if constexpr (kHasOffset<FMT>) {
             int sum = 0;
@@ -223,7 +235,7 @@ __device__ __forceinline__ void stage_acts(S& s, const uint8_t* __restrict__ xq,
 
 // One workgroup tile: y[yrow[r]][n0 + c] for tile rows r with xrow[r] >= 0,
 // over all of k.  Weights: rows n0.. of w (n rows, rb bytes per row).
-template <int FMT, int WMW, int WNW, int MI, int NI>
+template <int FMT, int WMW, int WNW, int MI, int NI, bool kAllLive = false>
 __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& s,
                                          const uint8_t* __restrict__ w, int64_t n, int64_t k,
                                          int64_t rb, int64_t n0, const uint8_t* __restrict__ xq,
@@ -251,11 +263,20 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
     for (int r = 0; r < 16; ++r) bias[r] = kBias;
 
     const int ksteps = static_cast<int>(k / (32 * KB));
+    WRaw<FMT> wr;
+    XRaw xr;
+    load_weights<FMT>(wr, w, n, rb, n0, 0);
+    __syncthreads();  // the row maps written by the caller are visible
+    load_acts<BM>(xr, s, xq, xrb, 0);
     for (int ks = 0; ks < ksteps; ++ks) {
+        __syncthreads();  // the previous step's reads of the tiles are done
+        store_weights<FMT>(s, wr, ks);
+        store_acts<FMT, BM>(s, xr);
         __syncthreads();
-        stage_weights<FMT>(s, w, n, rb, n0, ks);
-        stage_acts<FMT, BM>(s, xq, xrb, ks);
-        __syncthreads();
+        // next step's loads (the last step reloads itself: no branch)
+        const int kn = ks + 1 < ksteps ? ks + 1 : ks;
+        load_weights<FMT>(wr, w, n, rb, n0, kn);
+        load_acts<BM>(xr, s, xq, xrb, kn);
 #pragma unroll 2
         for (int b = 0; b < KB; ++b) {
             v4i A[NI], Bv[MI];
@@ -271,22 +292,52 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
                 dx[mi] = s.dx[b][(wm * MI + mi) * 32 + l32];
                 ndx[mi] = -kBiasF * dx[mi];
             }
+            if constexpr (kAllLive) {
+                // every (ni, mi) tile is live: the MFMA of the next tile is
+                // issued before the rescale of the current one, so the
+                // rescale does not wait for the MFMA it follows
+                constexpr int NT = NI * MI;
+                float dwv[NI][16];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                float dwv[16];
+                for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][(wn * NI + ni) * 32 + 8 * q + 4 * h]);
-                    dwv[4 * q] = d4.x; dwv[4 * q + 1] = d4.y; dwv[4 * q + 2] = d4.z; dwv[4 * q + 3] = d4.w;
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][(wn * NI + ni) * 32 + 8 * q + 4 * h]);
+                        dwv[ni][4 * q] = d4.x; dwv[ni][4 * q + 1] = d4.y;
+                        dwv[ni][4 * q + 2] = d4.z; dwv[ni][4 * q + 3] = d4.w;
+                    }
+                v16i D[2];
+                D[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], Bv[0], bias, 0, 0, 0);
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi) {
-                    if (mi >= mi_live) break;
-                    const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ni], Bv[mi], bias, 0, 0, 0);
+                for (int p = 0; p < NT; ++p) {
+                    const int ni = p / MI, mi = p % MI;
+                    if (p + 1 < NT)
+                        D[(p + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(p + 1) / MI], Bv[(p + 1) % MI],
+                                                                             bias, 0, 0, 0);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float tq = fmaf(__int_as_float(D[r]), dx[mi], ndx[mi]);
-                        acc[mi][ni][r] = fmaf(tq, dwv[r], acc[mi][ni][r]);
+                        const float tq = fmaf(__int_as_float(D[p & 1][r]), dx[mi], ndx[mi]);
+                        acc[mi][ni][r] = fmaf(tq, dwv[ni][r], acc[mi][ni][r]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    float dwv[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][(wn * NI + ni) * 32 + 8 * q + 4 * h]);
+                        dwv[4 * q] = d4.x; dwv[4 * q + 1] = d4.y; dwv[4 * q + 2] = d4.z; dwv[4 * q + 3] = d4.w;
+                    }
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi) {
+                        if (mi >= mi_live) break;
+                        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ni], Bv[mi], bias, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float tq = fmaf(__int_as_float(D[r]), dx[mi], ndx[mi]);
+                            acc[mi][ni][r] = fmaf(tq, dwv[r], acc[mi][ni][r]);
+                        }
                     }
                 }
             }
@@ -301,7 +352,7 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
                     const float a = s.cw[b2 + h][(wn * NI + ni) * 32 + l32];
 #pragma unroll
                     for (int mi = 0; mi < MI; ++mi) {
-                        if (mi >= mi_live) break;
+                        if (!kAllLive && mi >= mi_live) break;
                         const float bx = s.sx[b2 + h][(wm * MI + mi) * 32 + l32];
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bx, acc[mi][ni], 0, 0, 0);
                     }
@@ -353,7 +404,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         s.yrow[threadIdx.x] = static_cast<int>(gm);
     }
     const int rows = static_cast<int>(m - m0 < T::BM ? m - m0 : T::BM);
-    mma_tile<FMT, 2, 2, 2, 2>(s, w, n, k, rb, n0, xq, rows, y, ldy);
+    // every token sub-tile is computed (rows past m hold row 0's data and are
+    // not stored): straight-line MFMA code keeps the accumulators in place
+    mma_tile<FMT, 2, 2, 2, 2, true>(s, w, n, k, rb, n0, xq, rows, y, ldy);
 }
 
 // Grouped expert GEMM: workgroup (n tile, expert); 64 x 128 tiles, 1 x 4
