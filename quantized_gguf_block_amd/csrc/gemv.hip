@@ -1,27 +1,34 @@
 // gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K) for
 // 1..8 Q8_0 activation rows.
 //
-// Design (HBM-bound; the weights are read exactly once):
-//  * A workgroup owns row tiles of RT consecutive weight rows.  Because GGUF
-//    rows are stored back to back, a tile is one contiguous byte range; all
-//    threads stage it into LDS with fully coalesced 16-byte loads (a wave
-//    reads 1 KiB per instruction), whatever the 18/20/34/144-byte block
-//    size.  Blocks are then re-sliced out of LDS.
-//  * Each lane owns fixed "columns" of K (one 32-value block, or for Q4_K one
-//    32-byte nibble chunk = two 32-value sub-blocks) and keeps the Q8_0
-//    activation of its columns, for all batch rows, in registers for the
-//    workgroup's lifetime; a grid-stride loop over tiles amortizes that load.
+// Streaming kernel (HBM-bound; the weights are read exactly once):
+//  * A wave owns a contiguous range of rows.  Every row is loaded with
+//    coalesced, non-temporal 16-byte loads (one KiB per wave instruction)
+//    straight into registers, through a ring of P rows, so P rows are in
+//    flight while one is computed.  Because GGUF rows are stored back to
+//    back, a row is one contiguous byte range whatever the 18/20/34/144-byte
+//    block size; it is staged in a wave-private LDS buffer and each lane
+//    re-slices its own blocks out of it.
+//  * Each lane owns fixed "columns" of K (one or two 32-value blocks, or for
+//    Q4_K one 32-byte nibble chunk = two 32-value sub-blocks) and keeps the
+//    Q8_0 activation of its columns, for all batch rows, in registers.  The
+//    activations are copied once per workgroup into LDS with coalesced
+//    loads and unpacked from there.
 //  * Per block: nibble unpack in registers, v_dot4 integer dots against the
 //    activation quants, scales applied once per 32-value block in fp32
 //    (alice-llm 2.0.0 README, "Computation Path (Q4_K)").  Batch rows share
 //    the decoded weight registers (alice-llm 2.0.0 README, "Batch-4
 //    Speculative Decoding": one accumulator register per row).
-//  * Cross-lane sums are wave64 DPP reductions (alice-llm 2.0.0 README, "The
-//    GPU Optimization Journey", phase 2: subgroup reduction instead of a
-//    shared-memory tree); with more than one wave per row the per-wave sums
-//    meet in LDS and are added in wave order.
+//  * Cross-lane sums: P rows x batch values are reduced together, four at a
+//    time, with permlane swaps and DPP (alice-llm 2.0.0 README, "The GPU
+//    Optimization Journey", phase 2: subgroup reduction instead of a
+//    shared-memory tree), then stored with one instruction.
 //  * The column split depends only on (type, k), never on the batch size, so
 //    batch row b gives bitwise the batch-1 result.
+// Shapes the streaming kernel does not cover (more than two columns per
+// lane, rows that are not whole 16-byte pieces, unaligned activations) use
+// the general kernel: several waves per row, cooperative staging of row
+// tiles in LDS, per-wave sums added in wave order.
 #include "cq_device.h"
 #include "cq_internal.h"
 
@@ -79,19 +86,63 @@ __device__ __forceinline__ void load_q8(const uint8_t* p, uint32_t* q, float* dx
     *sum = acc;
 }
 
+// keep (1 or 0) multiplies the block scales: 0 turns the column into exact
+// zero contributions.
 template <int FMT>
-__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a) {
+__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a,
+                                         float keep = 1.0f) {
     int s;
     load_q8(xq_row + static_cast<int64_t>(col) * 34, a.q, &a.dx, &s);
+    a.dx *= keep;
     a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
     a.ndx = -kBiasF * a.dx;
     a.sdx = a.dx * static_cast<float>(s);
 }
 template <>
-__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a) {
+__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a,
+                                                 float keep) {
     int sa, sb;
     load_q8(xq_row + static_cast<int64_t>(2 * col) * 34, a.qa, &a.dxa, &sa);
     load_q8(xq_row + static_cast<int64_t>(2 * col + 1) * 34, a.qb, &a.dxb, &sb);
+    a.dxa *= keep;
+    a.dxb *= keep;
+    a.sa = a.dxa * static_cast<float>(sa);
+    a.sb = a.dxb * static_cast<float>(sb);
+    a.ndxa = -kBiasF * a.dxa;
+    a.ndxb = -kBiasF * a.dxb;
+}
+
+// The same, from a block already in registers: fp16 scale bits d16 and
+// the 32 quants q (Q4_K: two consecutive blocks).
+__device__ __forceinline__ void q8_from_regs(uint32_t d16, const uint32_t* qin, uint32_t* q,
+                                             float* dx, int* sum) {
+    *dx = h2f(d16);
+    int acc = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        q[t] = qin[t];
+        acc = sdot4(q[t], 0x01010101u, acc);
+    }
+    *sum = acc;
+}
+template <int FMT>
+__device__ __forceinline__ void act_from_raw(const uint32_t* d16, const uint32_t (*q)[8],
+                                             Act<FMT>& a, float keep) {
+    int sum;
+    q8_from_regs(d16[0], q[0], a.q, &a.dx, &sum);
+    a.dx *= keep;
+    a.start = (FMT == T_Q4_0) ? kBias - 8 * sum : kBias;
+    a.ndx = -kBiasF * a.dx;
+    a.sdx = a.dx * static_cast<float>(sum);
+}
+template <>
+__device__ __forceinline__ void act_from_raw<T_Q4_K>(const uint32_t* d16, const uint32_t (*q)[8],
+                                                     Act<T_Q4_K>& a, float keep) {
+    int sa, sb;
+    q8_from_regs(d16[0], q[0], a.qa, &a.dxa, &sa);
+    q8_from_regs(d16[1], q[1], a.qb, &a.dxb, &sb);
+    a.dxa *= keep;
+    a.dxb *= keep;
     a.sa = a.dxa * static_cast<float>(sa);
     a.sb = a.dxb * static_cast<float>(sb);
     a.ndxa = -kBiasF * a.dxa;
@@ -341,88 +392,6 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
     }
 }
 
-// ---- single-wave variant: one wave covers all of k (every lane owns its
-// columns), so waves never wait for each other.  Each wave streams its row
-// tiles HBM -> LDS with LDS-DMA (global_load_lds_dwordx4: 16 bytes per lane,
-// 1 KiB per instruction, no VGPRs) through a ring of kRing wave-private
-// buffers: while tile t is computed, tiles t+1 .. t+kRing-1 are in flight.
-// The weights are read once, so the DMA carries the non-temporal hint.
-//
-// Wait accounting: every tile is exactly kDmaVec DMA instructions, each with
-// at least one active lane (lanes past the tile are masked off; an
-// instruction wholly past it re-loads the tile's first KiB onto the buffer's
-// first KiB), and every processed tile issues exactly one global store, so
-// the number of vector-memory operations issued after a tile's DMA is a
-// compile-time constant and an explicit s_waitcnt vmcnt(N) suffices.  The
-// DMA is issued from inline assembly: the compiler then does not model it,
-// and places no waits of its own for it (its waits for its own loads can
-// only become more conservative); all waits for the DMA are the explicit
-// ones below.
-constexpr int kRing = 2;                           // buffers per wave
-constexpr int kTileCap = 9232;                     // tile bytes incl. up to 15 lead bytes
-constexpr int kDmaVec = (kTileCap + 1023) / 1024;  // 1-KiB DMA instructions per tile
-constexpr int kDmaBufBytes = kTileCap + 64;        // + read slack past the last block
-constexpr int kWavesPerCu = 8;                     // most waves per CU (kRing buffers each)
-// waves per CU launched: Q8_0's per-tile work (two unaligned 34-byte blocks
-// per lane and row) runs best with six, the others with eight
-template <int FMT> constexpr int kWaveGrid = FMT == T_Q8_0 ? 6 : kWavesPerCu;
-static_assert(kRing >= 2 && kRing <= 4, "ring depth");
-static_assert(kRing * kWavesPerCu * kDmaBufBytes <= 160 * 1024, "LDS per CU");
-static_assert(kDmaVec * 64 * 16 >= kTileCap && (kDmaVec - 1) * 1024 < kTileCap, "instruction count");
-
-template <int N>
-__device__ __forceinline__ void wait_vmem() {      // s_waitcnt vmcnt(N)
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// LDS byte offset of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-    typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
-}
-
-// One LDS-DMA instruction: each active lane copies the 16 bytes at gaddr (its
-// own) to LDS[lds_base + 16*lane]; lds_base must be wave-uniform.  M0 carries
-// the LDS base; it is saved and restored around the instruction, with one
-// wait state between the M0 write and the DMA that reads it.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off nt\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gaddr), "s"(lds_base)
-        : "memory");
-}
-
-// Stage bytes [a0, a0 + 16*nvec) of w (a0 16-aligned, 1 <= nvec,
-// 16*nvec <= kTileCap, a0 + 16*nvec <= size of w) into buf with exactly
-// kDmaVec DMA instructions.  Instruction u covers vectors 64u .. 64u+63 with
-// the lanes past nvec masked off; an instruction with 64u >= nvec instead
-// re-loads the tile's own first vectors (lanes < nvec) onto the same bytes of
-// the buffer, so every instruction has lane 0 active and none writes past
-// 16*nvec.
-__device__ __forceinline__ void dma_tile(const uint8_t* __restrict__ w, int64_t a0, int nvec,
-                                         uint8_t* buf, int lane) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(buf));
-#pragma unroll
-    for (int u = 0; u < kDmaVec; ++u) {
-        if (u * kWave < nvec) {               // wave-uniform
-            const int v = u * kWave + lane;
-            if (v < nvec) dma16(w + a0 + 16 * static_cast<int64_t>(v), base + u * kWave * 16);
-        } else {
-            // the tile's first vectors again, onto the same bytes (lanes past
-            // nvec masked as above, lane 0 always active)
-            if (lane < nvec) dma16(w + a0 + 16 * static_cast<int64_t>(lane), base);
-        }
-    }
-}
-
 // Sum each of the V = RT*B accumulators over the 64 lanes and store row r,
 // batch j to y[j*ldy + r0 + r] (r < rt) with one store instruction.
 // Groups of four values are transposed across the wave with
@@ -431,7 +400,8 @@ __device__ __forceinline__ void dma_tile(const uint8_t* __restrict__ w, int64_t 
 // order is the same for every value slot.
 template <int RT, int B>
 __device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_t r0,
-                                             float* __restrict__ y, int64_t ldy, int lane) {
+                                             float* __restrict__ y, int64_t ldy, int lane,
+                                             int64_t rs = 1) {
     constexpr int V = RT * B;
     constexpr int NG = (V + 3) / 4;
     static_assert(NG <= 16, "at most 64 values");
@@ -459,170 +429,420 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_
     const int row = lane >> 4, g = lane & 15;
     const int idx = 4 * g + (row == 1 ? 2 : (row == 2 ? 1 : row));
     const int r = idx / B, j = idx - (idx / B) * B;
-    if (g < NG && idx < V && r < rt) y[j * ldy + r0 + r] = out;
+    if (g < NG && idx < V && r < rt) y[j * ldy + r0 + r * rs] = out;
 }
 
-template <int FMT, int B, int RT>
-__global__ __launch_bounds__(kWave) void gemv_wave_kernel(
-        const uint8_t* __restrict__ w, int64_t n, int64_t rb, int ncols, int C,
+// ---- streaming kernel: one wave per workgroup, each wave owns a contiguous
+// range of rows; every lane loads its own blocks of each row straight from
+// HBM into registers (non-temporal 16-byte loads), through a ring of P row
+// buffers, so P rows are in flight while one is computed.  Each lane owns C
+// consecutive columns (32-value blocks; Q4_K: 32-byte nibble chunks) and
+// keeps their activations for all batch rows in registers.  Every P rows the
+// P*B sums are reduced across the wave together and stored.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Weight loads carry the non-temporal hint: every weight byte is read once.
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// the dword at (even) byte offset O of a dword window
+template <int O>
+__device__ __forceinline__ uint32_t dw_at(const uint32_t* w) {
+    if constexpr (O & 2) return __builtin_amdgcn_alignbit(w[(O >> 2) + 1], w[O >> 2], 16);
+    else return w[O >> 2];
+}
+template <int O>
+__device__ __forceinline__ uint32_t half_at(const uint32_t* w) {
+    return (w[O >> 2] >> ((O & 2) * 8)) & 0xFFFFu;
+}
+
+// Per-lane register window of one weight row.
+template <int FMT, int C> struct Win {
+    static constexpr int BS = Fmt<FMT>::BS;
+    static constexpr bool kMis = (C * BS) % 4 != 0;       // odd lanes start 2 bytes into a dword
+    static constexpr int NDW = kMis ? (C * BS + 2 + 3) / 4 : C * BS / 4;
+};
+template <int C> struct Win<T_Q4_K, C> {
+    static constexpr bool kMis = false;
+    static constexpr int NDW = 4 + 8 * C;                  // header + C nibble chunks
+};
+
+// acc[j] += block (32 values) at byte offset O of the window, batch row j
+template <int FMT, int B, int O>
+__device__ __forceinline__ void block_dot(const uint32_t* w, const Act<FMT>* a, float* acc) {
+    if constexpr (FMT == T_Q8_0) {
+        const float dw = h2f(half_at<O>(w));
+        uint32_t q[8];
+        q[0] = dw_at<O + 2>(w); q[1] = dw_at<O + 6>(w); q[2] = dw_at<O + 10>(w); q[3] = dw_at<O + 14>(w);
+        q[4] = dw_at<O + 18>(w); q[5] = dw_at<O + 22>(w); q[6] = dw_at<O + 26>(w); q[7] = dw_at<O + 30>(w);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = kBias, s1 = 0;
+            int& s2 = B == 1 ? s1 : s;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(q[t], a[j].q[t], s);
+                s2 = sdot4(q[4 + t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
+            acc[j] = fmaf(sx, dw, acc[j]);
+        }
+    } else if constexpr (FMT == T_Q4_0) {
+        const float dw = h2f(half_at<O>(w));
+        const uint32_t qq[4] = {dw_at<O + 2>(w), dw_at<O + 6>(w), dw_at<O + 10>(w), dw_at<O + 14>(w)};
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            lo[t] = qq[t] & 0x0F0F0F0Fu;
+            hi[t] = (qq[t] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = a[j].start, s1 = 0;
+            int& s2 = B == 1 ? s1 : s;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(lo[t], a[j].q[t], s);
+                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
+            acc[j] = fmaf(sx, dw, acc[j]);
+        }
+    } else {  // Q4_1, O a multiple of 4
+        const uint32_t dm = w[O >> 2];
+        const float dw = h2f(dm & 0xFFFFu), mw = h2f(dm >> 16);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t q = w[(O >> 2) + 1 + t];
+            lo[t] = q & 0x0F0F0F0Fu;
+            hi[t] = (q >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = kBias, s1 = 0;
+            int& s2 = B == 1 ? s1 : s;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                s = sdot4(lo[t], a[j].q[t], s);
+                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
+            }
+            if (B == 1) s += s1;
+            const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
+            acc[j] = fmaf(mw, a[j].sdx, fmaf(sx, dw, acc[j]));
+        }
+    }
+}
+
+// acc[j] += Q4_K nibble chunk c (sub-blocks 2c, 2c+1) of the super-block
+// whose 16-byte header is hdr, nibbles q[0..7], batch row j.  Branch-free in
+// c (c differs between the lanes of a wave).
+template <int B>
+__device__ __forceinline__ void chunk_dot_q4k(const uint32_t* hdr, const uint32_t* q, int c,
+                                              const Act<T_Q4_K>* a, float* acc) {
+    const float d = h2f(hdr[0] & 0xFFFFu), dmin = h2f(hdr[0] >> 16);
+    // scale/min bytes of sub-blocks 2c, 2c+1 as byte pairs (low byte: 2c)
+    const uint32_t sh = 16u * (c & 1);
+    const uint32_t lowsrc = (c < 2) ? hdr[1] : hdr[3];     // S[0..3] or S[8..11]
+    const uint32_t A = lowsrc >> sh, Bm = hdr[2] >> sh, V = hdr[1] >> sh;
+    const uint32_t sc_lo = A & 0x3F3Fu, m_lo = Bm & 0x3F3Fu;                        // c < 2
+    const uint32_t sc_hi = (A & 0x0F0Fu) | ((V >> 2) & 0x3030u);                     // c >= 2
+    const uint32_t m_hi = ((A >> 4) & 0x0F0Fu) | ((Bm >> 2) & 0x3030u);
+    const uint32_t scp = (c < 2) ? sc_lo : sc_hi, mp = (c < 2) ? m_lo : m_hi;
+    const float ds0 = d * static_cast<float>(scp & 0xFFu), ds1 = d * static_cast<float>((scp >> 8) & 0xFFu);
+    const float dm0 = dmin * static_cast<float>(mp & 0xFFu), dm1 = dmin * static_cast<float>((mp >> 8) & 0xFFu);
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        lo[t] = q[t] & 0x0F0F0F0Fu;
+        hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        int sa = kBias, sb = kBias, sa1 = 0, sb1 = 0;
+        int& sa2 = B == 1 ? sa1 : sa;
+        int& sb2 = B == 1 ? sb1 : sb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sa = sdot4(lo[t], a[j].qa[t], sa);
+            sb = sdot4(hi[t], a[j].qb[t], sb);
+            sa2 = sdot4(lo[4 + t], a[j].qa[4 + t], sa2);
+            sb2 = sdot4(hi[4 + t], a[j].qb[4 + t], sb2);
+        }
+        if (B == 1) {
+            sa += sa1;
+            sb += sb1;
+        }
+        const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
+        const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
+        float v = fmaf(xa, ds0, acc[j]);
+        v = fmaf(-dm0, a[j].sa, v);
+        v = fmaf(xb, ds1, v);
+        acc[j] = fmaf(-dm1, a[j].sb, v);
+    }
+}
+
+template <int FMT, int B, int C, int I = 0>
+__device__ __forceinline__ void row_dot(const uint32_t* w, const Act<FMT> (*act)[B], int c0,
+                                        float* acc) {
+    if constexpr (I < C) {
+        if constexpr (FMT == T_Q4_K) {
+            chunk_dot_q4k<B>(w, w + 4 + 8 * I, c0 + I, act[I], acc);
+        } else {
+            block_dot<FMT, B, I * Fmt<FMT>::BS>(w, act[I], acc);
+        }
+        row_dot<FMT, B, C, I + 1>(w, act, c0, acc);
+    }
+}
+
+template <bool V> struct Bool { static constexpr bool value = V; };
+
+// bytes of one lane column: a 32-value block, or a quarter super-block
+template <int FMT> constexpr int col_bytes() {
+    if constexpr (FMT == T_Q4_K) return 36;
+    else return Fmt<FMT>::BS;
+}
+
+constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per SIMD)
+
+// Largest activation bytes (all batch rows) one streaming workgroup stages.
+template <int FMT, int B, int C> constexpr int kActMax = B * (FMT == T_Q4_K ? 128 : 64) * C * 34;
+
+template <int FMT, int B, int C, int P>
+__global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
+        const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy) {
-    __shared__ __align__(16) uint8_t ring[kRing][kDmaBufBytes];
-    const int lane = threadIdx.x;
-
-    constexpr int CM = kCMax<FMT>;
-    int col[CM];
-    bool valid[CM];
-#pragma unroll
-    for (int i = 0; i < CM; ++i) {
-        col[i] = i * kWave + lane;
-        valid[i] = (i < C) && (col[i] < ncols);
+    using W = Win<FMT, C>;
+    // 16-byte pieces per lane and row: piece j of lane l is row bytes
+    // [1024 j + 16 l, +16), so every load instruction reads one contiguous KiB
+    constexpr int NJ = (kWave * C * col_bytes<FMT>() + 1023) / 1024;
+    constexpr int XMAX = kActMax<FMT, B, C>;
+    __shared__ __align__(16) uint8_t xs[XMAX + 16];              // activations, all rows
+    __shared__ __align__(16) uint8_t stage_all[kGW][NJ * 1024 + 16];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    uint8_t* stage = stage_all[wv];
+    // global wave g owns rows [rbeg, rend): rows_q each, one more for the
+    // first rows_r (possibly none)
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kGW + wv;
+    const int64_t rbeg = g * rows_q + (g < rows_r ? g : rows_r);
+    const int64_t rend = rbeg + rows_q + (g < rows_r ? 1 : 0);
+    const bool valid = C * lane < ncols;
+    // byte offsets of this lane's column data within a row
+    int off, qoff = 0, c0 = 0;
+    if constexpr (FMT == T_Q4_K) {
+        const int ch = valid ? C * lane : 0;
+        off = (ch >> 2) * 144;
+        c0 = ch & 3;
+        qoff = off + 16 + 32 * c0;
+    } else {
+        off = valid ? C * lane * Fmt<FMT>::BS : 0;
     }
-    Act<FMT> act[CM][B];  // loaded once the first tiles are in flight
-
-    const int64_t G = gridDim.x;
-    const int64_t ntiles = (n + RT - 1) / RT;
-    const int64_t nt = ntiles > blockIdx.x ? (ntiles - blockIdx.x + G - 1) / G : 0;
-    auto tile_of = [&](int64_t i) { return blockIdx.x + i * G; };
-    auto issue = [&](int64_t i, uint8_t* buf) {
-        const int64_t r0 = tile_of(i) * RT;
-        const int rt = static_cast<int>(n - r0 < RT ? n - r0 : RT);
-        const int64_t a0 = (r0 * rb) & ~static_cast<int64_t>(15);
-        const int nvec = (static_cast<int>(r0 * rb - a0) + rt * static_cast<int>(rb) + 15) >> 4;
-        wait_lds_all();  // earlier reads of this buffer have completed
-        dma_tile(w, a0, nvec, buf, lane);
+    const int aoff = off & ~3;
+    const uint32_t mis = static_cast<uint32_t>(off & 2) * 8;
+    // pieces at or past the row end re-read the row's first 16 bytes (staged
+    // past the row, never read back)
+    int poff[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int o = 1024 * j + 16 * lane;
+        poff[j] = o + 16 <= rb ? o : 0;
+    }
+    auto load_row = [&](int64_t r, u32x4* d) {
+        const uint8_t* base = w + (r < rend ? r : rend - 1) * rb;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) d[j] = ldg(reinterpret_cast<const u32x4*>(base + poff[j]));
     };
-    auto process = [&](int64_t i, const uint8_t* buf) {
-        const int64_t r0 = tile_of(i) * RT;
-        const int rt = static_cast<int>(n - r0 < RT ? n - r0 : RT);
-        const int delta = static_cast<int>(r0 * rb - ((r0 * rb) & ~static_cast<int64_t>(15)));
-        float acc[RT][B];
+
+    // Activations: the workgroup copies all batch rows (xact bytes, a whole
+    // number of 16-byte pieces at a 16-byte aligned address) into LDS with
+    // coalesced loads, issued before the first P rows of each wave; the
+    // copy only waits for its own loads (they are the oldest).
+    const int xact = static_cast<int>(B * xq_row_bytes);
+    constexpr int XPT = (XMAX / 16 + kWave * kGW - 1) / (kWave * kGW);  // pieces per thread
+    u32x4 xv[XPT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+    for (int t = 0; t < XPT; ++t) {
+        const int pc = threadIdx.x + t * kWave * kGW;
+        xv[t] = *reinterpret_cast<const u32x4*>(xq + (16 * pc < xact ? 16 * pc : 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool has_rows = rbeg < rend;
+    u32x4 buf[P][NJ];
+    if (has_rows) {
 #pragma unroll
-            for (int j = 0; j < B; ++j) acc[r][j] = 0.0f;
+        for (int j = 0; j < P; ++j) load_row(rbeg + j, buf[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            if (r < rt) {
-                const int row_base = delta + r * static_cast<int>(rb);
+    for (int t = 0; t < XPT; ++t) {
+        const int pc = threadIdx.x + t * kWave * kGW;
+        if (16 * pc < xact) *reinterpret_cast<u32x4*>(xs + 16 * pc) = xv[t];
+    }
+    __syncthreads();
+    if (!has_rows) return;
+    // this lane's activation blocks from LDS: fp16 scale bits and 32 quants
+    // (a lane past the columns reads column 0 with its scales forced to 0,
+    // so it adds exact zeros)
+    constexpr int NA = FMT == T_Q4_K ? 2 : 1;  // Q8_0 blocks per column
+    Act<FMT> act[C][B];
+    const float keep = valid ? 1.0f : 0.0f;
 #pragma unroll
-                for (int c = 0; c < CM; ++c)
-                    if (valid[c])
-                        column_dot<FMT, B>(buf, col_offset<FMT>(row_base, col[c]), act[c],
-                                           acc[r], col[c]);
+    for (int i = 0; i < C; ++i)
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            uint32_t ad[NA], aq[NA][8];
+#pragma unroll
+            for (int h = 0; h < NA; ++h) {
+                const int bo = j * static_cast<int>(xq_row_bytes) +
+                               (NA * (valid ? C * lane + i : 0) + h) * 34;
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(xs + (bo & ~3));
+                const uint32_t sh = static_cast<uint32_t>(bo & 2) * 8;
+                uint32_t wd[10];
+#pragma unroll
+                for (int t = 0; t < 10; ++t) wd[t] = p[t];
+                ad[h] = __builtin_amdgcn_alignbit(wd[1], wd[0], sh) & 0xFFFFu;
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    aq[h][t] = __builtin_amdgcn_alignbit(wd[t + 1 + (sh ? 1 : 0)], wd[t + (sh ? 1 : 0)], sh ? 0 : 16);
             }
+            act_from_raw<FMT>(ad, aq, act[i][j], keep);
         }
-        reduce_store<RT, B>(acc, rt, r0, y, ldy, lane);
+
+    // One group of P rows: stage each row in LDS, refill its registers with
+    // the row P further on (REFILL), compute, then reduce and store.  The
+    // last group does not refill, so rows are loaded once except the at most
+    // P-1 past the end in the second-to-last group's refills (re-reads of the
+    // last row, computed and not stored).
+    auto group = [&](int64_t r, auto refill) {
+        float acc[P][B];
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+#pragma unroll
+            for (int j = 0; j < B; ++j) acc[i][j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            // stage the row in LDS (one wave: LDS requests are served in
+            // order, so the reads below see these writes and the next
+            // row's writes come after these reads)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                *reinterpret_cast<u32x4*>(stage + 1024 * j + 16 * lane) = buf[i][j];
+            // The refill goes into the registers just staged, with no branch
+            // around it, so no register copy of an in-flight load (which
+            // would wait for it) is ever needed.
+            if constexpr (decltype(refill)::value) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_row(r + P + i, buf[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint32_t v[W::NDW];
+            if constexpr (FMT == T_Q4_K) {
+                const uint4 h = *reinterpret_cast<const uint4*>(stage + off);
+                v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
+#pragma unroll
+                for (int t = 0; t < 2 * C; ++t) {
+                    const uint4 q = *reinterpret_cast<const uint4*>(stage + qoff + 16 * t);
+                    v[4 + 4 * t] = q.x; v[5 + 4 * t] = q.y; v[6 + 4 * t] = q.z; v[7 + 4 * t] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < W::NDW; ++t)
+                    v[t] = *reinterpret_cast<const uint32_t*>(stage + aoff + 4 * t);
+                if constexpr (W::kMis) {
+#pragma unroll
+                    for (int t = 0; t + 1 < W::NDW; ++t) v[t] = __builtin_amdgcn_alignbit(v[t + 1], v[t], mis);
+                    v[W::NDW - 1] >>= mis;
+                }
+            }
+            row_dot<FMT, B, C>(v, act, c0, acc[i]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        const int rt = static_cast<int>(rend - r < P ? rend - r : P);
+        reduce_store<P, B>(acc, rt, r, y, ldy, lane);
     };
-    // Tile i lives in buffer i % kRing.  Step i issues tile i+kRing-1 (into
-    // the buffer computed in step i-1), waits for tile i, computes it and
-    // stores its outputs.  Vector-memory operations issued after tile i's DMA
-    // by the time of that wait: the DMAs of tiles i+1 .. i+kRing-1 and the
-    // stores of the min(i, kRing-1) steps before i.  Once no tile is left to
-    // issue, the wait drains everything.
-    constexpr int kAhead = (kRing - 1) * kDmaVec;
-    auto step = [&](int64_t i, const uint8_t* cur, uint8_t* nxt) {
-        if (i + kRing - 1 < nt) {
-            issue(i + kRing - 1, nxt);
-            const int64_t stores = i < kRing - 1 ? i : kRing - 1;
-            if (stores == 0) wait_vmem<kAhead>();
-            else if (stores == 1) wait_vmem<kAhead + 1>();
-            else if (stores == 2) wait_vmem<kAhead + 2>();
-            else wait_vmem<kAhead + 3>();
-        } else {
-            wait_vmem<0>();
-        }
-        process(i, cur);
-    };
-#pragma unroll
-    for (int d = 0; d < kRing - 1; ++d)
-        if (d < nt) issue(d, ring[d]);
-    // the activations are loaded after the first tiles are in flight, so the
-    // latencies overlap (their loads only add completed operations to the
-    // counts above, which stay upper bounds).  Unconditional loads (an
-    // unused column reads column 0 and is never consumed) keep all of them in
-    // flight together.
-#pragma unroll
-    for (int i = 0; i < CM; ++i)
-#pragma unroll
-        for (int j = 0; j < B; ++j)
-            load_act<FMT>(xq + j * xq_row_bytes, valid[i] ? col[i] : 0, act[i][j]);
-    for (int64_t i = 0; i < nt; i += kRing) {
-        step(i, ring[0], ring[kRing - 1]);
-        if (i + 1 >= nt) break;
-        step(i + 1, ring[1], ring[0]);
-        if constexpr (kRing > 2) {
-            if (i + 2 >= nt) break;
-            step(i + 2, ring[2], ring[1]);
-        }
-        if constexpr (kRing > 3) {
-            if (i + 3 >= nt) break;
-            step(i + 3, ring[3], ring[2]);
-        }
-    }
+    int64_t r = rbeg;
+    for (; r + P < rend; r += P) group(r, Bool<true>{});
+    group(r, Bool<false>{});
 }
 
 struct Plan {
     int ncols, C, nw, RT, tile_lds, red_bytes;
-    bool wave;  // single-wave LDS-DMA kernel
+    int SC;  // > 0: streaming kernel with SC columns per lane
 };
 
-// wave_ok: the single-wave LDS-DMA kernel may be used (the matrix is a whole
-// number of 16-byte vectors, so no tile ends inside a vector).
-Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool wave_ok) {
+constexpr int kRing = 4;  // rows in flight per wave in the streaming kernel
+
+// stream_ok: the streaming kernel may be used (the activations are 16-byte
+// aligned); it also needs weight and activation rows that are a whole number
+// of 16-byte pieces.
+Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
+    const int64_t xrb = k / 32 * 34;
     Plan p{};
     p.ncols = static_cast<int>(wt == T_Q4_K ? k / 64 : k / 32);
     p.C = (wt == T_Q4_K || p.ncols <= kWave) ? 1 : 2;
     p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
-    // rows per tile: about 16 KiB of weights per tile, at most 32 live
+    // general kernel: about 16 KiB of weights per tile, at most 32 live
     // accumulators per lane
     int rt = 8;
     while (rt > 1 && (rt * rb > 20480 || rt * batch > 32)) rt >>= 1;
     if (rt == 2) rt = 1;  // instantiated tiles: 1, 4, 8
-    if (p.nw == 1 && wave_ok) {  // single-wave kernel: tiles bounded by its LDS buffers
-        static constexpr int kRts[] = {8, 4, 3, 2, 1};
-        for (int cand : kRts) {
-            if (cand * rb + 15 <= kTileCap && cand * batch <= 32) {
-                rt = cand;
-                p.wave = true;
-                break;
-            }
-        }
-    }
     p.RT = rt;
     p.tile_lds = static_cast<int>((rt * rb + 32 + 15) & ~15);
     p.red_bytes = p.nw > 1 ? p.nw * rt * batch * 4 : 0;
+    // streaming kernel: one wave covers the row with 1 or 2 columns per lane
+    // (not Q4_K with two chunks per lane: its activations alone would need
+    // more than the register file at the larger batches, and every batch of
+    // one (type, k) must take the same kernel)
+    const int sc = (p.ncols + kWave - 1) / kWave;
+    if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
+        !(wt == T_Q4_K && sc == 2))
+        p.SC = sc;
     return p;
+}
+
+template <typename K>
+int resident_blocks_per_cu(K kernel, int threads) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1)
+        nb = 1;
+    return nb;
+}
+
+template <int FMT, int B, int SC>
+int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint8_t* xq,
+                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
+    auto kern = gemv_stream_kernel<FMT, B, SC, kRing>;
+    static const int occ = kGW * resident_blocks_per_cu(kern, kWave * kGW);
+    int per_cu = occ < 8 ? occ : 8;
+    // as many waves as fit, each with a whole number of P-row groups where
+    // possible: gpw groups per wave, then the fewest waves that cover n,
+    // rounded up to whole workgroups (spare waves get no rows)
+    const int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu;
+    const int64_t groups = (n + kRing - 1) / kRing;
+    const int64_t gpw = (groups + gmax - 1) / gmax;
+    const int64_t waves = (n + gpw * kRing - 1) / (gpw * kRing);
+    const int64_t wgs = (waves + kGW - 1) / kGW, nw = wgs * kGW;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(kWave * kGW), 0, stream, w,
+                       n / nw, static_cast<int>(n % nw), rb, ncols, xq, xrb, y, ldy);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
+    if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+    if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
-    if (p.wave) {
-        int64_t grid = static_cast<int64_t>(device_cu_count()) * kWaveGrid<FMT>;
-        if (grid > ntiles) grid = ntiles;
-        const dim3 g(static_cast<unsigned>(grid)), b(kWave);
-        switch (p.RT) {
-            case 8:
-                if constexpr (B <= 4) {
-                    hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 8>), g, b, 0, stream, w, n, rb,
-                                       p.ncols, p.C, xq, xrb, y, ldy);
-                    break;
-                } else {
-                    return -3;
-                }
-            case 4: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 4>), g, b, 0, stream, w, n, rb,
-                                       p.ncols, p.C, xq, xrb, y, ldy); break;
-            case 3: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 3>), g, b, 0, stream, w, n, rb,
-                                       p.ncols, p.C, xq, xrb, y, ldy); break;
-            case 2: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 2>), g, b, 0, stream, w, n, rb,
-                                       p.ncols, p.C, xq, xrb, y, ldy); break;
-            default: hipLaunchKernelGGL((gemv_wave_kernel<FMT, B, 1>), g, b, 0, stream, w, n, rb,
-                                        p.ncols, p.C, xq, xrb, y, ldy); break;
-        }
-        return hipGetLastError() == hipSuccess ? 0 : -6;
-    }
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
     if (grid > ntiles) grid = ntiles;
@@ -669,7 +889,7 @@ int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
     const int64_t qk = wt == T_Q4_K ? 256 : 32;
     const Plan p = make_plan(wt, k, k / qk * bs, static_cast<int>(batch), false);
     if (p.nw * kWave > kMaxThreads) return -3;
-    if (!p.wave && p.tile_lds + p.red_bytes > 65536) return -3;
+    if (p.tile_lds + p.red_bytes > 65536) return -3;
     return 0;
 }
 
@@ -679,7 +899,8 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
     const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
     const int64_t qk = wt == T_Q4_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
-    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch), (n * rb) % 16 == 0);
+    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch),
+                             (reinterpret_cast<uintptr_t>(xq) & 15) == 0);
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     const uint8_t* xp = static_cast<const uint8_t*>(xq);
     const int64_t xrb = k / 32 * 34;
