@@ -671,12 +671,13 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         xv[t] = *reinterpret_cast<const u32x4*>(xq + (16 * pc < xact ? 16 * pc : 0));
     }
     __builtin_amdgcn_sched_barrier(0);
+    // (no branch around these loads, even for a spare wave without rows,
+    // which re-reads the matrix's last row: with a branch, the wait for the
+    // activation copy below would also wait for these loads)
     const bool has_rows = rbeg < rend;
     u32x4 buf[P][NJ];
-    if (has_rows) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) load_row(rbeg + j, buf[j]);
-    }
+    for (int j = 0; j < P; ++j) load_row(rbeg + j, buf[j]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < XPT; ++t) {

@@ -60,8 +60,8 @@ def test_gemv_config_full(cq, orc, name):
 
 def test_gemv_lm_head_sampled(cq, orc):
     """Q4_K LM head 128256 x 4096 at batch 1 and 4: every output of the first
-    and last row tiles plus 4000 random outputs against the oracle, and the
-    batch-4 rows equal the batch-1 results bitwise."""
+    and last row tiles plus 4000 random outputs against the oracle (both
+    batches), and the batch-4 rows equal the batch-1 results bitwise."""
     name = "q4_k_gemv_lm_head"
     c, w, x = config_inputs(name)
     n, k = c["n"], c["k"]
@@ -77,24 +77,31 @@ def test_gemv_lm_head_sampled(cq, orc):
     bs = np.concatenate([np.arange(128) % 4, rng.integers(0, 4, 4000)])
     y_ref, s_ref = orc.matmul_sampled(c["fmt"], w, n, k, xq, 4, bs, rows)
     assert_close_to_oracle(y4[bs, rows], y_ref, s_ref, what="lm head b4")
+    b0 = bs == 0
+    assert_close_to_oracle(y1[0, rows[b0]], y_ref[b0], s_ref[b0], what="lm head b1")
     # each batch row separately equals a batch-1 call on that row
     for b in range(1, 4):
         yb = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd[b:b + 1], 1))
         assert np.array_equal(yb[0], y4[b])
 
 
+@pytest.mark.parametrize("k", [1024, 2048, 4096])
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
-def test_gemv_batch_rows_equal_single_rows(cq, orc, fmt):
-    n, k = 300, 4096
+def test_gemv_batch_rows_equal_single_rows(cq, orc, fmt, k):
+    """Row b of a verify batch is bitwise the batch-1 result on that row, for
+    every batch size (the column split depends only on the type and k)."""
+    if k % gs.BLOCK_ELEMS[fmt]:
+        pytest.skip("k not a whole number of blocks for this type")
+    n = 300
     w = gs.weights(fmt, n, k, cfg=300)
     xq = orc.quantize_q8_0(gs.activations(8, k, cfg=300))
     wd = to_dev(w)
-    note("gemv batch invariance", gs.NAMES[fmt])
-    for batch in (2, 5, 8):
+    note("gemv batch invariance", gs.NAMES[fmt], k)
+    y1 = [to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq[b:b + 1]), 1))[0] for b in range(8)]
+    for batch in (2, 3, 5, 8):
         yb = to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq[:batch]), batch))
         for b in range(batch):
-            y1 = to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq[b:b + 1]), 1))
-            assert np.array_equal(yb[b], y1[0]), (batch, b)
+            assert np.array_equal(yb[b], y1[b]), (batch, b)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
