@@ -10,10 +10,11 @@ the 256 MB Infinity Cache.
 
 Printed: one JSON line.  value = weight bytes streamed per step / step time
 (GB/s).  roofline: the Q8_0 batch-5 GEMV (the largest launch), algorithmic
-bytes (weights + activation blocks + outputs) over its average duration from
-HIP events recorded around each of its launches on the launch stream (these
-brackets also hold the kernel-boundary time, about 3 us, that the profiler's
-kernel duration leaves out; both are reported).  traffic: HBM bytes per launch
+bytes (weights + activation blocks + outputs) over its average launch
+duration from HIP events on the launch stream around a burst of back-to-back
+launches right after the timed steps; the average of events recorded around
+each of its launches inside the timed steps is reported beside it (those
+brackets also hold the kernel-boundary time, about 3 us).  traffic: HBM bytes per launch
 from the committed rocprofv3 counter summary, null once the GEMV source has
 changed since it was taken.
 cpu_baseline: the CPU oracle on the same step (fp64 reference, not a tuned
@@ -150,11 +151,26 @@ def main():
     step_bytes = 2 * sum(wbytes.values())
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: Q8_0 batch-5 GEMV
+    # dominant kernel: Q8_0 batch-5 GEMV.  Two live HIP-event figures on the
+    # launch stream: events around each of its launches inside the timed
+    # steps (they also hold the event packets and the dispatch/completion
+    # gap, ~3 us), and a burst of back-to-back launches on rotating copies
+    # right after the timed steps (per-launch duration without that gap,
+    # the figure the profiler's kernel duration corresponds to).
     durs = [a.elapsed_time(b) for a, b in ev_pairs]
     avg_ms = float(np.mean(durs))
+    reps = 100
+    torch.cuda.synchronize()
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(reps):
+        gemv(gs.Q8_0, B, False)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    burst_ms = b0.elapsed_time(b1) / reps
     alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
-    achieved = alg / (avg_ms * 1e-3) / 1e9
+    achieved = alg / (burst_ms * 1e-3) / 1e9
 
     traffic, prof_us = profiled("gemv_stream_kernel<8, 5, 2, 4>")
 
@@ -185,7 +201,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel<8, 5, 2, 4> (Q8_0, batch 5)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": alg,
+                     "avg_launch_us": round(burst_ms * 1e3, 3),
+                     "avg_launch_us_event_bracketed": round(avg_ms * 1e3, 3),
+                     "alg_bytes_per_launch": alg,
                      "traffic_over_alg": round(traffic / alg, 3) if traffic else None,
                      "rocprof_avg_kernel_us": prof_us},
         "cpu_baseline": cpu,
