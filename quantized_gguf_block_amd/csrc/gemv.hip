@@ -55,6 +55,13 @@ template <> struct Fmt<T_Q8_0> { static constexpr int BS = 34; };
 constexpr int kBias = 0x4B400000;
 constexpr float kBiasF = 12582912.0f;
 
+// kBias in a scalar register the compiler cannot see through.
+__device__ __forceinline__ int bias_sgpr() {
+    int r;
+    asm("s_mov_b32 %0, 0x4b400000" : "=s"(r));
+    return r;
+}
+
 template <int FMT> struct Act {
     uint32_t q[8];  // 32 int8 quants
     float dx;       // block scale
@@ -73,6 +80,47 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
 }
 
+// First dot of a chain in the three-operand form, its start value read from a
+// scalar register (S), a vector register (V) or zero (Z); the compiler's own
+// choice, the accumulate-in-place form, would first copy the start value into
+// the result register.
+__device__ __forceinline__ int sdot4_s(uint32_t a, uint32_t b, int c) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
+__device__ __forceinline__ int sdot4_v(uint32_t a, uint32_t b, int c) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ int sdot4_z(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// start + sum over t < 8 of the 4-byte dot w[t].x[t] (exact in int32); start
+// is wave-uniform (in a scalar register) when UNIFORM.  TWO: two chains of
+// four for more independent work (batch 1).
+template <bool TWO, bool UNIFORM>
+__device__ __forceinline__ int dot8(const uint32_t* w, const uint32_t* x, int start) {
+    int s = UNIFORM ? sdot4_s(w[0], x[0], start) : sdot4_v(w[0], x[0], start);
+    if constexpr (TWO) {
+        int s1 = sdot4_z(w[4], x[4]);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) {
+            s = sdot4(w[t], x[t], s);
+            s1 = sdot4(w[4 + t], x[4 + t], s1);
+        }
+        return s + s1;
+    } else {
+#pragma unroll
+        for (int t = 1; t < 8; ++t) s = sdot4(w[t], x[t], s);
+        return s;
+    }
+}
+
 // Load one 34-byte Q8_0 activation block (2-byte aligned) from global memory.
 __device__ __forceinline__ void load_q8(const uint8_t* p, uint32_t* q, float* dx, int* sum) {
     const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
@@ -86,63 +134,19 @@ __device__ __forceinline__ void load_q8(const uint8_t* p, uint32_t* q, float* dx
     *sum = acc;
 }
 
-// keep (1 or 0) multiplies the block scales: 0 turns the column into exact
-// zero contributions.
 template <int FMT>
-__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a,
-                                         float keep = 1.0f) {
+__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a) {
     int s;
     load_q8(xq_row + static_cast<int64_t>(col) * 34, a.q, &a.dx, &s);
-    a.dx *= keep;
     a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
     a.ndx = -kBiasF * a.dx;
     a.sdx = a.dx * static_cast<float>(s);
 }
 template <>
-__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a,
-                                                 float keep) {
+__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a) {
     int sa, sb;
     load_q8(xq_row + static_cast<int64_t>(2 * col) * 34, a.qa, &a.dxa, &sa);
     load_q8(xq_row + static_cast<int64_t>(2 * col + 1) * 34, a.qb, &a.dxb, &sb);
-    a.dxa *= keep;
-    a.dxb *= keep;
-    a.sa = a.dxa * static_cast<float>(sa);
-    a.sb = a.dxb * static_cast<float>(sb);
-    a.ndxa = -kBiasF * a.dxa;
-    a.ndxb = -kBiasF * a.dxb;
-}
-
-// The same, from a block already in registers: fp16 scale bits d16 and
-// the 32 quants q (Q4_K: two consecutive blocks).
-__device__ __forceinline__ void q8_from_regs(uint32_t d16, const uint32_t* qin, uint32_t* q,
-                                             float* dx, int* sum) {
-    *dx = h2f(d16);
-    int acc = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        q[t] = qin[t];
-        acc = sdot4(q[t], 0x01010101u, acc);
-    }
-    *sum = acc;
-}
-template <int FMT>
-__device__ __forceinline__ void act_from_raw(const uint32_t* d16, const uint32_t (*q)[8],
-                                             Act<FMT>& a, float keep) {
-    int sum;
-    q8_from_regs(d16[0], q[0], a.q, &a.dx, &sum);
-    a.dx *= keep;
-    a.start = (FMT == T_Q4_0) ? kBias - 8 * sum : kBias;
-    a.ndx = -kBiasF * a.dx;
-    a.sdx = a.dx * static_cast<float>(sum);
-}
-template <>
-__device__ __forceinline__ void act_from_raw<T_Q4_K>(const uint32_t* d16, const uint32_t (*q)[8],
-                                                     Act<T_Q4_K>& a, float keep) {
-    int sa, sb;
-    q8_from_regs(d16[0], q[0], a.qa, &a.dxa, &sa);
-    q8_from_regs(d16[1], q[1], a.qb, &a.dxb, &sb);
-    a.dxa *= keep;
-    a.dxb *= keep;
     a.sa = a.dxa * static_cast<float>(sa);
     a.sb = a.dxb * static_cast<float>(sb);
     a.ndxa = -kBiasF * a.dxa;
@@ -441,10 +445,15 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_
 // P*B sums are reduced across the wave together and stored.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Weight loads carry the non-temporal hint: every weight byte is read once.
-template <typename T>
-__device__ __forceinline__ T ldg(const T* p) {
-    return __builtin_nontemporal_load(p);
+// Weight rows are read through buffer descriptors: the row base and its
+// length live in scalar registers, each lane adds a 32-bit offset, and the
+// hardware returns zeros for bytes at or past the length without touching
+// memory.  The loads carry the non-temporal hint (every weight byte is read
+// once).
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit dwords
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufWord3);
 }
 
 // the dword at (even) byte offset O of a dword window
@@ -477,61 +486,42 @@ __device__ __forceinline__ void block_dot(const uint32_t* w, const Act<FMT>* a, 
         uint32_t q[8];
         q[0] = dw_at<O + 2>(w); q[1] = dw_at<O + 6>(w); q[2] = dw_at<O + 10>(w); q[3] = dw_at<O + 14>(w);
         q[4] = dw_at<O + 18>(w); q[5] = dw_at<O + 22>(w); q[6] = dw_at<O + 26>(w); q[7] = dw_at<O + 30>(w);
+        const int bias = bias_sgpr();
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = kBias, s1 = 0;
-            int& s2 = B == 1 ? s1 : s;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                s = sdot4(q[t], a[j].q[t], s);
-                s2 = sdot4(q[4 + t], a[j].q[4 + t], s2);
-            }
-            if (B == 1) s += s1;
+            const int s = dot8<B == 1, true>(q, a[j].q, bias);
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(sx, dw, acc[j]);
         }
     } else if constexpr (FMT == T_Q4_0) {
         const float dw = h2f(half_at<O>(w));
         const uint32_t qq[4] = {dw_at<O + 2>(w), dw_at<O + 6>(w), dw_at<O + 10>(w), dw_at<O + 14>(w)};
-        uint32_t lo[4], hi[4];
+        uint32_t nib[8];  // low nibbles (values 0..15), then high nibbles (16..31)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            lo[t] = qq[t] & 0x0F0F0F0Fu;
-            hi[t] = (qq[t] >> 4) & 0x0F0F0F0Fu;
+            nib[t] = qq[t] & 0x0F0F0F0Fu;
+            nib[4 + t] = (qq[t] >> 4) & 0x0F0F0F0Fu;
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = a[j].start, s1 = 0;
-            int& s2 = B == 1 ? s1 : s;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                s = sdot4(lo[t], a[j].q[t], s);
-                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
-            }
-            if (B == 1) s += s1;
+            const int s = dot8<B == 1, false>(nib, a[j].q, a[j].start);
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(sx, dw, acc[j]);
         }
     } else {  // Q4_1, O a multiple of 4
         const uint32_t dm = w[O >> 2];
         const float dw = h2f(dm & 0xFFFFu), mw = h2f(dm >> 16);
-        uint32_t lo[4], hi[4];
+        uint32_t nib[8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t q = w[(O >> 2) + 1 + t];
-            lo[t] = q & 0x0F0F0F0Fu;
-            hi[t] = (q >> 4) & 0x0F0F0F0Fu;
+            nib[t] = q & 0x0F0F0F0Fu;
+            nib[4 + t] = (q >> 4) & 0x0F0F0F0Fu;
         }
+        const int bias = bias_sgpr();
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = kBias, s1 = 0;
-            int& s2 = B == 1 ? s1 : s;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                s = sdot4(lo[t], a[j].q[t], s);
-                s2 = sdot4(hi[t], a[j].q[4 + t], s2);
-            }
-            if (B == 1) s += s1;
+            const int s = dot8<B == 1, true>(nib, a[j].q, bias);
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(mw, a[j].sdx, fmaf(sx, dw, acc[j]));
         }
@@ -561,22 +551,11 @@ __device__ __forceinline__ void chunk_dot_q4k(const uint32_t* hdr, const uint32_
         lo[t] = q[t] & 0x0F0F0F0Fu;
         hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
     }
+    const int bias = bias_sgpr();
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-        int sa = kBias, sb = kBias, sa1 = 0, sb1 = 0;
-        int& sa2 = B == 1 ? sa1 : sa;
-        int& sb2 = B == 1 ? sb1 : sb;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            sa = sdot4(lo[t], a[j].qa[t], sa);
-            sb = sdot4(hi[t], a[j].qb[t], sb);
-            sa2 = sdot4(lo[4 + t], a[j].qa[4 + t], sa2);
-            sb2 = sdot4(hi[4 + t], a[j].qb[4 + t], sb2);
-        }
-        if (B == 1) {
-            sa += sa1;
-            sb += sb1;
-        }
+        const int sa = dot8<B == 1, true>(lo, a[j].qa, bias);
+        const int sb = dot8<B == 1, true>(hi, a[j].qb, bias);
         const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
         const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
         float v = fmaf(xa, ds0, acc[j]);
@@ -622,10 +601,26 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // [1024 j + 16 l, +16), so every load instruction reads one contiguous KiB
     constexpr int NJ = (kWave * C * col_bytes<FMT>() + 1023) / 1024;
     constexpr int XMAX = kActMax<FMT, B, C>;
-    __shared__ __align__(16) uint8_t xs[XMAX + 16];              // activations, all rows
-    __shared__ __align__(16) uint8_t stage_all[kGW][NJ * 1024 + 16];
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    uint8_t* stage = stage_all[wv];
+    constexpr int NBMAX = XMAX / 34;                             // activation blocks, all rows
+    constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
+    constexpr int RAW = (XMAX + 16 > kGW * STG) ? XMAX + 16 : kGW * STG;
+    // raw activation copy first, the waves' row staging buffers afterwards
+    __shared__ __align__(16) uint8_t raw[RAW];
+    // Converted activation blocks in lane order: block h of column C*l + i of
+    // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
+    // read consecutive words (no bank conflicts).
+    constexpr int NS = FMT == T_Q4_K ? 2 : 1;  // Q8_0 blocks per column
+    constexpr int NP = kWave * C;              // column positions per row
+    __shared__ __align__(16) u32x4 xq0[NBMAX];  // quants 0..15
+    __shared__ __align__(16) u32x4 xq1[NBMAX];  // quants 16..31
+    __shared__ float xda[NBMAX];                // dx
+    __shared__ float xau[NBMAX];                // dx*sum(q) (Q4_0: the integer sum)
+    // (the wave index is read from lane 0 so the compiler keeps every
+    // per-wave row quantity in scalar registers)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint8_t* xs = raw;
+    uint8_t* stage = raw + wv * STG;
     // global wave g owns rows [rbeg, rend): rows_q each, one more for the
     // first rows_r (possibly none)
     const int64_t g = static_cast<int64_t>(blockIdx.x) * kGW + wv;
@@ -644,18 +639,15 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     }
     const int aoff = off & ~3;
     const uint32_t mis = static_cast<uint32_t>(off & 2) * 8;
-    // pieces at or past the row end re-read the row's first 16 bytes (staged
-    // past the row, never read back)
-    int poff[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int o = 1024 * j + 16 * lane;
-        poff[j] = o + 16 <= rb ? o : 0;
-    }
+    // Pieces past the row end, and every piece of a row past rend (the ring
+    // runs up to P-1 rows ahead of the wave's last row), read as zeros
+    // without memory traffic; they are staged or computed and never stored.
     auto load_row = [&](int64_t r, u32x4* d) {
-        const uint8_t* base = w + (r < rend ? r : rend - 1) * rb;
+        const bool in = r < rend;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(w + (in ? r : 0) * rb, in ? static_cast<int>(rb) : 0);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) d[j] = ldg(reinterpret_cast<const u32x4*>(base + poff[j]));
+        for (int j = 0; j < NJ; ++j)
+            d[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 * j + 16 * lane, 0, kNonTemporal);
     };
 
     // Activations: the workgroup copies all batch rows (xact bytes, a whole
@@ -672,8 +664,8 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     // (no branch around these loads, even for a spare wave without rows,
-    // which re-reads the matrix's last row: with a branch, the wait for the
-    // activation copy below would also wait for these loads)
+    // whose loads read zeros: with a branch, the wait for the activation
+    // copy below would also wait for these loads)
     const bool has_rows = rbeg < rend;
     u32x4 buf[P][NJ];
 #pragma unroll
@@ -685,40 +677,86 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         if (16 * pc < xact) *reinterpret_cast<u32x4*>(xs + 16 * pc) = xv[t];
     }
     __syncthreads();
+    // Each activation block is converted once per workgroup: 32 quants (two
+    // 16-byte words), dx, and dx*sum(q) (Q4_0: the integer sum); positions
+    // past the columns get zeros, so lanes without a column add exact zeros.
+    {
+        const int nbr = static_cast<int>(xq_row_bytes / 34);
+        constexpr int NG = B * NS * NP;
+#pragma unroll
+        for (int t0 = 0; t0 < NG; t0 += kWave * kGW) {
+            const int gi = t0 + static_cast<int>(threadIdx.x);
+            if (gi < NG) {
+                const int j = gi / (NS * NP), h = (gi / NP) % NS, pp = gi % NP;
+                const int blk = (C * (pp % kWave) + pp / kWave) * NS + h;
+                uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                float dx = 0.0f;
+                if (blk < nbr) {
+                    const int bo = j * static_cast<int>(xq_row_bytes) + blk * 34;
+                    const int qb = bo + 2;
+                    const uint32_t* pq = reinterpret_cast<const uint32_t*>(xs + (qb & ~3));
+                    const uint32_t sh = static_cast<uint32_t>(qb & 2) * 8;
+                    uint32_t wd[9];
+#pragma unroll
+                    for (int u = 0; u < 9; ++u) wd[u] = pq[u];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) q[u] = __builtin_amdgcn_alignbit(wd[u + 1], wd[u], sh);
+                    dx = h2f(*reinterpret_cast<const uint16_t*>(xs + bo));
+                }
+                xq0[gi] = u32x4{q[0], q[1], q[2], q[3]};
+                xq1[gi] = u32x4{q[4], q[5], q[6], q[7]};
+                xda[gi] = dx;
+                if constexpr (FMT != T_Q8_0) {
+                    int sum = 0;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) sum = sdot4(q[u], 0x01010101u, sum);
+                    xau[gi] = FMT == T_Q4_0 ? __int_as_float(sum) : dx * static_cast<float>(sum);
+                }
+            }
+        }
+    }
+    __syncthreads();  // converted; the raw copy's space now serves as row staging
     if (!has_rows) return;
-    // this lane's activation blocks from LDS: fp16 scale bits and 32 quants
-    // (a lane past the columns reads column 0 with its scales forced to 0,
-    // so it adds exact zeros)
-    constexpr int NA = FMT == T_Q4_K ? 2 : 1;  // Q8_0 blocks per column
     Act<FMT> act[C][B];
-    const float keep = valid ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < C; ++i)
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            uint32_t ad[NA], aq[NA][8];
-#pragma unroll
-            for (int h = 0; h < NA; ++h) {
-                const int bo = j * static_cast<int>(xq_row_bytes) +
-                               (NA * (valid ? C * lane + i : 0) + h) * 34;
-                const uint32_t* p = reinterpret_cast<const uint32_t*>(xs + (bo & ~3));
-                const uint32_t sh = static_cast<uint32_t>(bo & 2) * 8;
-                uint32_t wd[10];
-#pragma unroll
-                for (int t = 0; t < 10; ++t) wd[t] = p[t];
-                ad[h] = __builtin_amdgcn_alignbit(wd[1], wd[0], sh) & 0xFFFFu;
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    aq[h][t] = __builtin_amdgcn_alignbit(wd[t + 1 + (sh ? 1 : 0)], wd[t + (sh ? 1 : 0)], sh ? 0 : 16);
+            if constexpr (FMT == T_Q4_K) {
+                Act<T_Q4_K>& a = act[i][j];
+                const int ga = 2 * j * NP + lane, gb = ga + NP;
+                const u32x4 a0 = xq0[ga], a1 = xq1[ga], b0 = xq0[gb], b1 = xq1[gb];
+                a.qa[0] = a0.x; a.qa[1] = a0.y; a.qa[2] = a0.z; a.qa[3] = a0.w;
+                a.qa[4] = a1.x; a.qa[5] = a1.y; a.qa[6] = a1.z; a.qa[7] = a1.w;
+                a.qb[0] = b0.x; a.qb[1] = b0.y; a.qb[2] = b0.z; a.qb[3] = b0.w;
+                a.qb[4] = b1.x; a.qb[5] = b1.y; a.qb[6] = b1.z; a.qb[7] = b1.w;
+                a.dxa = xda[ga];
+                a.dxb = xda[gb];
+                a.sa = xau[ga];
+                a.sb = xau[gb];
+                a.ndxa = -kBiasF * a.dxa;
+                a.ndxb = -kBiasF * a.dxb;
+            } else {
+                Act<FMT>& a = act[i][j];
+                const int g = j * NP + kWave * i + lane;
+                const u32x4 q0 = xq0[g], q1 = xq1[g];
+                a.q[0] = q0.x; a.q[1] = q0.y; a.q[2] = q0.z; a.q[3] = q0.w;
+                a.q[4] = q1.x; a.q[5] = q1.y; a.q[6] = q1.z; a.q[7] = q1.w;
+                a.dx = xda[g];
+                a.ndx = -kBiasF * a.dx;
+                if constexpr (FMT == T_Q4_0) {
+                    a.start = kBias - 8 * __float_as_int(xau[g]);
+                } else {
+                    a.start = kBias;
+                    if constexpr (FMT == T_Q4_1) a.sdx = xau[g];
+                }
             }
-            act_from_raw<FMT>(ad, aq, act[i][j], keep);
         }
 
     // One group of P rows: stage each row in LDS, refill its registers with
     // the row P further on (REFILL), compute, then reduce and store.  The
-    // last group does not refill, so rows are loaded once except the at most
-    // P-1 past the end in the second-to-last group's refills (re-reads of the
-    // last row, computed and not stored).
+    // last group does not refill, so every row is loaded once (refills past
+    // rend read zeros, computed and not stored).
     auto group = [&](int64_t r, auto refill) {
         float acc[P][B];
 #pragma unroll
