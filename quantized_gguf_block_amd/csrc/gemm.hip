@@ -494,14 +494,15 @@ struct WRegs {            // one lane's share of one Q4_K super-block
 };
 
 // Load activation blocks 2q, 2q+1 of super-block sb for tile row r (thread
-// t: r = t/4, q = t%4).  Unconditional: a row that holds no pair reads token
-// row 0 instead, and its outputs are never stored.  (A load under a branch is
-// merged with the other branch's value by a register copy, which waits for
-// the load at once.)
+// t: r = t/4, q = t%4).  Unconditional: a row that holds no pair reads the
+// pass's first token row instead (loaded anyway, and not one row shared by
+// every workgroup), and its outputs are never stored.  (A load under a
+// branch is merged with the other branch's value by a register copy, which
+// waits for the load at once.)
 __device__ __forceinline__ void issue_acts(const StreamSmem& s, const uint8_t* __restrict__ xq,
                                            int64_t xrb, int sb, ARegs& a) {
     const int t = threadIdx.x, r = t >> 2, q = t & 3;
-    const int gm = s.xrow[r];
+    const int gm = s.xrow[r] >= 0 ? s.xrow[r] : s.xrow[0];
     const uint32_t* p = reinterpret_cast<const uint32_t*>(
         xq + static_cast<int64_t>(gm < 0 ? 0 : gm) * xrb + (static_cast<int64_t>(sb) * 8 + 2 * q) * 34);
 #pragma unroll
