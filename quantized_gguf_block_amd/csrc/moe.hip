@@ -23,7 +23,6 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
         const int32_t* __restrict__ ids, int np, int n_experts, int32_t* __restrict__ offsets,
         int32_t* __restrict__ pairs) {
     __shared__ int fill[kMaxExperts];
-    __shared__ int scan[kGroupThreads];
     __shared__ uint16_t wcnt[kGroupWaves][kMaxExperts];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
 
@@ -34,21 +33,27 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
         if (e >= 0 && e < n_experts) atomicAdd(&fill[e], 1);
     }
     __syncthreads();
-    // inclusive Hillis-Steele scan of the counts (n_experts <= 1024 = threads)
-    scan[t] = (t < n_experts) ? fill[t] : 0;
-    __syncthreads();
-    for (int d = 1; d < kGroupThreads; d <<= 1) {
-        const int v = (t >= d) ? scan[t - d] : 0;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
+    // exclusive scan of the counts by wave 0, 64 experts at a time (a
+    // wave-level inclusive scan plus the running carry)
+    if (wv == 0) {
+        int carry = 0;
+        for (int e0 = 0; e0 < n_experts; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = e < n_experts ? fill[e] : 0;
+            int v = c;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(v, d, 64);
+                if (lane >= d) v += o;
+            }
+            if (e < n_experts) {
+                offsets[e] = carry + v - c;
+                fill[e] = carry + v - c;  // running fill pointer
+            }
+            carry += __shfl(v, 63, 64);
+        }
+        if (lane == 0) offsets[n_experts] = carry;
     }
-    if (t < n_experts) {
-        const int excl = scan[t] - fill[t];
-        offsets[t] = excl;
-        fill[t] = excl;  // running fill pointer
-    }
-    if (t == 0) offsets[n_experts] = scan[n_experts - 1];
     for (int i = t; i < kGroupWaves * n_experts; i += kGroupThreads)
         wcnt[i / n_experts][i % n_experts] = 0;
     __syncthreads();
@@ -98,31 +103,47 @@ int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_
 }
 
 // ---- combine: y[t] = sum_s w[t,s] * d[t*k+s] in slot order ---------------
+// Workgroup (column chunk, tokens blockIdx.y, + gridDim.y, ...): each thread
+// four consecutive columns, with 16-byte loads and stores when d and y allow
+// them; the route weights of a token are wave-uniform.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ d,
                                                           const float* __restrict__ rw,
                                                           int64_t n_tokens, int top_k, int64_t n,
                                                           float* __restrict__ y, int64_t ldy) {
-    const int64_t total = n_tokens * n;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t t = i / n, c = i - t * n;
-        float acc = 0.0f;
-        for (int s = 0; s < top_k; ++s) {
-            const int64_t p = t * top_k + s;
-            acc = fmaf(rw[p], d[p * n + c], acc);
+    const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (c >= n) return;
+    const bool vec = (n & 3) == 0 && (ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(d) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    for (int64_t t = blockIdx.y; t < n_tokens; t += gridDim.y) {
+        const float* dp = d + t * top_k * n;
+        if (vec) {
+            float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int s = 0; s < top_k; ++s) {
+                const float wgt = rw[t * top_k + s];
+                const float4 v = *reinterpret_cast<const float4*>(dp + s * n + c);
+                acc.x = fmaf(wgt, v.x, acc.x);
+                acc.y = fmaf(wgt, v.y, acc.y);
+                acc.z = fmaf(wgt, v.z, acc.z);
+                acc.w = fmaf(wgt, v.w, acc.w);
+            }
+            *reinterpret_cast<float4*>(y + t * ldy + c) = acc;
+        } else {
+            for (int64_t cc = c; cc < c + 4 && cc < n; ++cc) {
+                float acc = 0.0f;
+                for (int s = 0; s < top_k; ++s) acc = fmaf(rw[t * top_k + s], dp[s * n + cc], acc);
+                y[t * ldy + cc] = acc;
+            }
         }
-        y[t * ldy + c] = acc;
     }
 }
 
 int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
                        int64_t n, float* y, int64_t ldy, hipStream_t stream) {
-    const int64_t total = n_tokens * n;
-    int64_t grid = (total + 255) / 256;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-    if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
-                       d, route_w, n_tokens, static_cast<int>(top_k), n, y, ldy);
+    const int64_t gx = (n + 1023) / 1024;
+    const int64_t gy = n_tokens < 4096 ? n_tokens : 4096;
+    if (gx > 0x7FFFFFFF) return -3;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+                       dim3(256), 0, stream, d, route_w, n_tokens, static_cast<int>(top_k), n, y, ldy);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

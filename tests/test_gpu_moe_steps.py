@@ -48,3 +48,21 @@ def test_moe_combine(cq, orc):
     y_ref, s_ref = orc.moe_combine(d.astype(np.float64), np.abs(d).astype(np.float64), rw)
     # four fp32 products summed in slot order: within 4 ulp-ish of the sum of |terms|
     assert np.all(np.abs(y - y_ref) <= 4 * 2.0 ** -24 * s_ref + 1e-30)
+
+
+@pytest.mark.parametrize("T,K,n", [(5000, 2, 36), (7, 4, 1001), (3, 8, 4096)])
+def test_moe_combine_shapes(cq, orc, T, K, n):
+    """Token counts past one grid row of workgroups, column counts that are
+    not a multiple of four (scalar path) and a strided output."""
+    import torch
+    note("moe combine shapes", T, K, n)
+    rng = np.random.default_rng(10 + n)
+    d = rng.standard_normal((T * K, n)).astype(np.float32)
+    rw = rng.random((T, K)).astype(np.float32)
+    ldy = n + 5
+    y = torch.full((T, ldy), -3.0, device="cuda")
+    cq.cq_moe_combine(to_dev(d), to_dev(rw), y=y[:, :n])
+    yh = to_host(y)
+    y_ref, s_ref = orc.moe_combine(d.astype(np.float64), np.abs(d).astype(np.float64), rw)
+    assert np.all(np.abs(yh[:, :n] - y_ref) <= 4 * 2.0 ** -24 * s_ref + 1e-30)
+    assert np.all(yh[:, n:] == -3.0)
