@@ -548,17 +548,6 @@ __device__ __forceinline__ void store_acts(ActTile& at, const ARegs& a) {
     }
 }
 
-__device__ __forceinline__ void q4k_scale_min(const u32x4& hdr, int j, int& sc, int& mn) {
-    if (j < 4) {
-        sc = (hdr.y >> (8 * j)) & 63;
-        mn = (hdr.z >> (8 * j)) & 63;
-    } else {
-        const int sh = 8 * (j - 4);
-        sc = ((hdr.w >> sh) & 0xF) | ((((hdr.y >> sh) >> 6) & 3) << 4);
-        mn = (((hdr.w >> sh) >> 4) & 0xF) | ((((hdr.z >> sh) >> 6) & 3) << 4);
-    }
-}
-
 constexpr int kStreamThreads = 256;    // 4 waves x 16 weight rows; 4 stagers per token row
 static_assert(kStreamThreads == 4 * kSbTok, "every thread stages two activation blocks");
 
@@ -574,6 +563,12 @@ template <int MT>
 __device__ __forceinline__ void stream_sb(const ActTile& at, const WRegs& cur, const StreamLane& L,
                                           const v4i& bias, v4f (&acc)[MT]) {
     const float d = h2f(cur.hdr.x & 0xFFFFu), dmin = h2f(cur.hdr.x >> 16);
+    // the eight 6-bit scales (bytes of sc03, sc47) and this lane's mins of
+    // sub-blocks g and 4 + g, unpacked a dword at a time
+    const uint32_t sc03 = cur.hdr.y & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (cur.hdr.w & 0x0F0F0F0Fu) | ((cur.hdr.y >> 2) & 0x30303030u);
+    const uint32_t mn03 = cur.hdr.z & 0x3F3F3F3Fu;
+    const uint32_t mn47 = ((cur.hdr.w >> 4) & 0x0F0F0F0Fu) | ((cur.hdr.z >> 2) & 0x30303030u);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const u32x2 qv = cur.q[c];
@@ -583,9 +578,8 @@ __device__ __forceinline__ void stream_sb(const ActTile& at, const WRegs& cur, c
             const long Bw = static_cast<long>(
                 (static_cast<uint64_t>(((e2 ? qv.y >> 4 : qv.y) & 0x0F0F0F0Fu)) << 32) |
                 ((e2 ? qv.x >> 4 : qv.x) & 0x0F0F0F0Fu));
-            int sc, mn;
-            q4k_scale_min(cur.hdr, j, sc, mn);
-            const float dwj = d * static_cast<float>(sc);
+            const uint32_t scw = j < 4 ? sc03 : sc47;
+            const float dwj = d * static_cast<float>((scw >> (8 * (j & 3))) & 0xFFu);
             const float ndwj = -kBiasF * dwj;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -603,9 +597,8 @@ __device__ __forceinline__ void stream_sb(const ActTile& at, const WRegs& cur, c
     // B = -dmin*m [4 sub-blocks][weight rows]
 #pragma unroll
     for (int j4 = 0; j4 < 8; j4 += 4) {
-        int sc, mn;
-        q4k_scale_min(cur.hdr, j4 + L.g, sc, mn);      // sub-block j4 + g of this lane's row
-        const float bm = -(dmin * static_cast<float>(mn));
+        const uint32_t mw = j4 == 0 ? mn03 : mn47;      // sub-block j4 + g of this lane's row
+        const float bm = -(dmin * static_cast<float>(__builtin_amdgcn_ubfe(mw, 8 * L.g, 8)));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const float ax = at.sx[j4 + L.g][16 * mt + L.j16];
