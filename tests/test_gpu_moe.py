@@ -170,3 +170,22 @@ def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
                                    to_dev(offs), to_dev(pairs), n_tokens, top_k))
         y_ref, s_ref = orc.moe_matmul(FMT, w, n_experts, n, k, xq, x_per_pair, ids)
         assert_close_to_oracle(y, y_ref, s_ref, what="moe shape")
+
+
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0], ids=lambda f: gs.NAMES[f])
+@pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(40, 6, 2, 200, 512), (130, 3, 3, 70, 256)])
+def test_moe_gemm_other_formats(cq, orc, fmt, n_tokens, n_experts, top_k, n, k):
+    """Grouped GEMM over the 32-value formats (the dense tile engine over
+    gathered rows): experts with more than one 64-token tile, n not a
+    multiple of 128, per-token and per-pair activation rows."""
+    w = gs.expert_weights(fmt, n_experts, n, k, cfg=720 + n_tokens, which=0)
+    ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=720 + n_tokens)
+    offs, pairs = orc.moe_group(ids, n_experts)
+    for x_per_pair in (False, True):
+        rows = n_tokens * top_k if x_per_pair else n_tokens
+        xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=721))
+        note("moe gemm", gs.NAMES[fmt], n_tokens, n_experts, top_k, n, k, x_per_pair)
+        y = to_host(cq.cq_moe_gemm(fmt, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
+                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
+        assert_close_to_oracle(y, y_ref, s_ref, what=f"moe {gs.NAMES[fmt]}")
