@@ -7,7 +7,8 @@ draws into block fields (fp16 scale fields at their byte offsets, uniformly
 random bytes for packed quants).  Uniform random bytes give uniform 4-bit
 quants and, for Q4_K, uniform independent 6-bit scales and mins, because
 the 12 scale bytes carry each of their 96 bits in exactly one of the 16
-six-bit fields.
+six-bit fields; for Q6_K, uniform 6-bit quants (every bit of ql and qh
+belongs to exactly one quant) and uniform signed 8-bit scales.
 
 Streams: numpy.random.default_rng([20261202, cfg, tensor]) with tensor ids
 0 = scales, 1 = quants, 2 = activations, 3 = expert ids, 4 = router logits,
@@ -17,15 +18,16 @@ import numpy as np
 
 SEED = 20261202
 
-Q4_0, Q4_1, Q8_0, Q4_K = 2, 3, 8, 12
-FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K}
+Q4_0, Q4_1, Q8_0, Q4_K, Q6_K = 2, 3, 8, 12, 14
+FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
 NAMES = {v: k for k, v in FORMATS.items()}
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144}
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q6_K: 210}
 
 # scale distributions (fp64 uniform draws, rounded to fp16 by numpy)
 D_RANGE = (1e-3, 2e-2)
 M_RANGE = (-0.16, 0.0)  # Q4_1 block offset m
+D6_RANGE = (1e-5, 2e-4)  # Q6_K super-block d (its 8-bit scales carry the rest)
 
 
 def rng(cfg, tensor):
@@ -63,6 +65,11 @@ def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
         out[:, 0:2] = _f16_field(gs, nblk, *d_range)   # d
         out[:, 2:4] = _f16_field(gs, nblk, *d_range)   # dmin
         out[:, 4:144] = gq.integers(0, 256, size=(nblk, 140), dtype=np.uint8)
+    elif fmt == Q6_K:
+        # ql[128], qh[64], 16 signed scale bytes: uniform random bytes;
+        # d (fp16) last
+        out[:, 0:208] = gq.integers(0, 256, size=(nblk, 208), dtype=np.uint8)
+        out[:, 208:210] = _f16_field(gs, nblk, *(D6_RANGE if d_range is D_RANGE else d_range))
     else:
         raise ValueError(f"unknown format {fmt}")
     return out.reshape(n, row_bytes(fmt, k))

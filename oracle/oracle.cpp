@@ -81,7 +81,7 @@ uint16_t rd16(const uint8_t* p) {   /* little-endian 16-bit field */
 int64_t elems_of(int type) {
     switch (type) {
         case ORACLE_Q4_0: case ORACLE_Q4_1: case ORACLE_Q8_0: return 32;
-        case ORACLE_Q4_K: return 256;
+        case ORACLE_Q4_K: case ORACLE_Q6_K: return 256;
         default: return -1;
     }
 }
@@ -92,6 +92,7 @@ int64_t bytes_of(int type) {
         case ORACLE_Q4_1: return 20;   /* fp16 d + fp16 m + 16 bytes      */
         case ORACLE_Q8_0: return 34;   /* fp16 d + 32 int8 [alice-QBS]    */
         case ORACLE_Q4_K: return 144;  /* 2 + 2 + 12 + 128 [alice-QBS]    */
+        case ORACLE_Q6_K: return 210;  /* 128 + 64 + 16 + 2 [alice-Q6K]   */
         default: return -1;
     }
 }
@@ -108,6 +109,20 @@ void q4k_scale_min(const uint8_t* S, int j, int* sc, int* mn) {
         *sc = (S[j + 4] & 0x0F) | ((S[j - 4] >> 6) << 4);
         *mn = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
     }
+}
+
+/* Q6_K: 6-bit quant (0..63) and signed scale of element e (0..255) of the
+ * super-block at b, per the reading in oracle.h. */
+void q6k_element(const uint8_t* b, int e, int* q, int* scale) {
+    const uint8_t* ql = b;
+    const uint8_t* qh = b + 128;
+    const int8_t* sc = reinterpret_cast<const int8_t*>(b + 192);
+    const int h = e / 128, r = e % 128, g = r / 32, l = r % 32;
+    const uint8_t lbyte = ql[64 * h + l + (g % 2 == 1 ? 32 : 0)];
+    const int low = (g < 2) ? (lbyte & 0x0F) : (lbyte >> 4);
+    const int high = (qh[32 * h + l] >> (2 * g)) & 3;
+    *q = low | (high << 4);
+    *scale = sc[8 * h + 2 * g + l / 16];
 }
 
 /* Decode one block to its elems_of(type) exact fp64 values. */
@@ -148,6 +163,15 @@ void decode_block(int type, const uint8_t* b, double* out) {
                     out[64 * c + i]      = d * sc_lo * (Q[32 * c + i] & 0x0F) - dmin * m_lo;
                     out[64 * c + 32 + i] = d * sc_hi * (Q[32 * c + i] >> 4) - dmin * m_hi;
                 }
+            }
+            break;
+        }
+        case ORACLE_Q6_K: {
+            const double d = half_value(rd16(b + 208));
+            for (int e = 0; e < 256; ++e) {
+                int q, sc;
+                q6k_element(b, e, &q, &sc);
+                out[e] = d * sc * (q - 32);
             }
             break;
         }
@@ -258,6 +282,29 @@ double factored_dot(int type, const uint8_t* wrow, const uint8_t* xrow, int64_t 
                 /* d*dx*sc*sum(q*qx) - dmin*dx*m*sum(qx) [alice-Q4K] */
                 acc += d * dx * sc * static_cast<double>(idot32(q, xq)) -
                        dmin * dx * mn * static_cast<double>(isum32(xq));
+            }
+        }
+        return acc;
+    }
+    if (type == ORACLE_Q6_K) {
+        /* per 16-element scale group: d*dx*scale*(sum q*qx - 32*sum qx) */
+        for (int64_t sb = 0; sb < k / 256; ++sb) {
+            const uint8_t* b = wrow + sb * 210;
+            const double d = half_value(rd16(b + 208));
+            for (int grp = 0; grp < 16; ++grp) {
+                const int e0 = 16 * grp;
+                const uint8_t* xb = xrow + (sb * 8 + e0 / 32) * 34;
+                const double dx = half_value(rd16(xb));
+                const int8_t* xq = reinterpret_cast<const int8_t*>(xb + 2) + e0 % 32;
+                int64_t sq = 0, sx = 0;
+                int sc = 0;
+                for (int i = 0; i < 16; ++i) {
+                    int q;
+                    q6k_element(b, e0 + i, &q, &sc);  /* one scale per group */
+                    sq += static_cast<int64_t>(q) * xq[i];
+                    sx += xq[i];
+                }
+                acc += d * dx * sc * static_cast<double>(sq - 32 * sx);
             }
         }
         return acc;

@@ -30,6 +30,12 @@
  *                 by expert is the stated follow-up.
  *   [alice-GPU]   alice-llm 2.0.0 README, "The GPU Optimization Journey",
  *                 phase 4: fused SwiGLU (gate + up + silu x mul).
+ *   [alice-Q6K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
+ *                 a Q6_K super-block is 210 bytes for 256 values, fields
+ *                 ql[128], qh[64], scales[16], d (fp16); and the NEON matvec
+ *                 design notes: the two high bits of each quant come from qh
+ *                 through the shift-masks (qh<<4)&0x30, (qh<<2)&0x30,
+ *                 qh&0x30 and (qh>>2)&0x30, one per quadrant.
  *
  * Readings where the pages are silent (all listed in the design notes):
  *   - Q4_0 block: fp16 d, then 16 bytes; byte i holds element i in its low
@@ -40,6 +46,14 @@
  *     (see oracle_q4k_scale_min); qs chunk c (32 bytes) holds sub-block 2c
  *     in low nibbles and sub-block 2c+1 in high nibbles.  Value
  *     d*sc*q - dmin*m.
+ *   - Q6_K: each 128-value half h uses ql[64h..64h+63], qh[32h..32h+31]
+ *     and scales[8h..8h+7].  For l in 0..31 the 6-bit quants of elements
+ *     l, l+32, l+64, l+96 of the half are the low nibble of ql[l], the low
+ *     nibble of ql[l+32], the high nibble of ql[l], the high nibble of
+ *     ql[l+32], each joined with bit pair 0-1, 2-3, 4-5, 6-7 of qh[l] as bits
+ *     4-5 (the four shift-masks above); element l + 32*g takes the signed
+ *     scale byte scales[8h + 2g + l/16]; value d*scale*(q-32).  This is the
+ *     GGUF layout, so real GGUF tensors decode as stored.
  *   - fp16 is IEEE-754 binary16, little-endian, subnormals honoured.
  *   - Q8_0 quantization: see oracle_quantize_q8_0.
  *   - SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z)), evaluated
@@ -60,7 +74,8 @@ enum {
     ORACLE_Q4_0 = 2,
     ORACLE_Q4_1 = 3,
     ORACLE_Q8_0 = 8,
-    ORACLE_Q4_K = 12
+    ORACLE_Q4_K = 12,
+    ORACLE_Q6_K = 14
 };
 
 int oracle_abi_version(void);
@@ -102,10 +117,10 @@ int oracle_matmul_sampled(int type, const uint8_t* w, int64_t n, int64_t k,
                           const int64_t* act_rows, const int64_t* w_rows, int64_t count,
                           double* y, double* s, int n_threads);
 
-/* Second, independent formulation of oracle_matmul: per 32-element block an
- * exact integer sum of quant products, then the fp64 scale factors, as in
- * [alice-Q4K] with the Q8_0 activation scale of each 32-block in place of
- * the Q8_K one. */
+/* Second, independent formulation of oracle_matmul: per 32-element block
+ * (Q6_K: per 16-element scale group) an exact integer sum of quant products,
+ * then the fp64 scale factors, as in [alice-Q4K] with the Q8_0 activation
+ * scale of each 32-block in place of the Q8_K one. */
 int oracle_matmul_factored(int type, const uint8_t* w, int64_t n, int64_t k,
                            const uint8_t* xq, int64_t m, double* y, int n_threads);
 

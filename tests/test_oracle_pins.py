@@ -39,6 +39,10 @@ def test_block_sizes_match_pages(orc):
     assert (orc.block_elems(orc.Q4_1), orc.block_bytes(orc.Q4_1)) == (32, 20)
     # bits per weight printed on the same table: 8.5 (Q8_0), 4.5 (Q4_K)
     assert 34 * 8 / 32 == 8.5 and 144 * 8 / 256 == 4.5
+    # Q6_K: 256 values in 210 bytes (ql[128] + qh[64] + scales[16] + fp16 d),
+    # 6.5625 bits per weight, same table
+    assert (orc.block_elems(orc.Q6_K), orc.block_bytes(orc.Q6_K)) == (256, 210)
+    assert 128 + 64 + 16 + 2 == 210 and 210 * 8 / 256 == 6.5625
     assert orc.block_bytes(99) == -1
 
 
@@ -308,7 +312,7 @@ def test_q4k_subblock_equals_q4_1(orc):
     assert np.array_equal(yk, y1)
 
 
-@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K])
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q6_K])
 def test_two_formulations_agree(orc, fmt):
     n, m, k = 33, 5, 1024
     w = gs.weights(fmt, n, k, cfg=914)
@@ -323,7 +327,7 @@ def test_two_formulations_agree(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt,k", [(gs.Q4_0, 32), (gs.Q4_1, 64), (gs.Q8_0, 96), (gs.Q4_K, 256),
-                                   (gs.Q4_K, 512)])
+                                   (gs.Q4_K, 512), (gs.Q6_K, 256)])
 def test_exact_rational_brute_force(orc, fmt, k):
     """Tiny shapes in exact rational arithmetic: the fp64 sums must agree
     with the exact value to within the fp64 summation bound."""
@@ -416,3 +420,122 @@ def test_moe_combine_vs_numpy(orc):
     assert np.allclose(y, ref, rtol=1e-15, atol=1e-15)
     assert np.allclose(s, np.einsum("tk,tkn->tn", np.abs(rw.astype(np.float64)),
                                     np.abs(d).reshape(T, K, n)), rtol=1e-15)
+
+
+# ------------------------------------------------------------------- Q6_K
+# alice-llm 2.0.0 README, Quantization Block Specs: Q6_K = ql[128] + qh[64]
+# + scales[16] + d(f16), 210 bytes for 256 values.  NEON matvec design notes:
+# the four quadrants take their high bits from qh through (qh<<4)&0x30,
+# (qh<<2)&0x30, qh&0x30 and (qh>>2)&0x30.  Reading (GGUF): in half h, element
+# l + 32g (l < 32) takes a nibble of ql[64h + l] (g = 0, 2: low, high) or
+# ql[64h + 32 + l] (g = 1, 3), scale byte 8h + 2g + l/16 (signed), value
+# d*scale*(q-32).
+
+def _q6k_block(d=1.0, ql=None, qh=None, scales=None):
+    b = np.zeros(210, np.uint8)
+    if ql is not None:
+        b[0:128] = ql
+    if qh is not None:
+        b[128:192] = qh
+    if scales is not None:
+        b[192:208] = np.asarray(scales, np.int8).view(np.uint8)
+    b[208:210] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+    return b
+
+
+def test_q6k_field_offsets(orc):
+    """d sits in the last two bytes, the signed scales in bytes 192..207:
+    with all quants 33 (ql low nibbles 1, qh bit pairs 2 -> q-32 = 1 in
+    quadrants 0 and 1), each element equals d times its group's scale."""
+    ql = np.full(128, 0x01, np.uint8)          # low nibble 1, high nibble 0
+    qh = np.full(64, 0b0000_1010, np.uint8)    # quadrants 0, 1: high bits 2 -> q = 33
+    scales = np.arange(-8, 8)
+    v = orc.dequantize(gs.Q6_K, _q6k_block(0.5, ql, qh, scales), 256)
+    for h in range(2):
+        for g in range(2):                     # quadrants with q = 33
+            for l in range(32):
+                assert v[128 * h + 32 * g + l] == 0.5 * scales[8 * h + 2 * g + l // 16]
+        for g in range(2, 4):                  # high nibble 0, high bits 0: q = 0
+            for l in range(32):
+                assert v[128 * h + 32 * g + l] == 0.5 * scales[8 * h + 2 * g + l // 16] * -32
+
+
+@pytest.mark.parametrize("quad", range(4))
+def test_q6k_high_bits_follow_the_page_shift_masks(orc, quad):
+    """qh byte l carries quadrant 0..3's high bit pairs in bits 0-1, 2-3,
+    4-5, 6-7: the page's four shift-masks place them at bits 4-5 of q."""
+    shift_mask = [lambda x: (x << 4) & 0x30, lambda x: (x << 2) & 0x30,
+                  lambda x: x & 0x30, lambda x: (x >> 2) & 0x30][quad]
+    qh = np.zeros(64, np.uint8)
+    qh[5] = 0b11 << (2 * quad)                 # half 0, l = 5: high bits 3
+    ql = np.zeros(128, np.uint8)
+    v = orc.dequantize(gs.Q6_K, _q6k_block(1.0, ql, qh, np.ones(16)), 256)
+    q = v + 32                                 # d = 1, every scale 1
+    assert shift_mask(int(qh[5])) == 0x30
+    assert q[32 * quad + 5] == 0x30            # bits 4-5 set, nibble 0
+    q[32 * quad + 5] = 0
+    assert not q.any()                         # no other element moved
+
+
+def test_q6k_nibble_quadrants(orc):
+    """ql[l] low/high nibble -> quadrants 0/2, ql[32 + l] -> quadrants 1/3, in
+    each half; qh all zero, d = 1, scales 1."""
+    ql = np.zeros(128, np.uint8)
+    ql[3] = 0x5A           # half 0: l = 3, quadrant 0 gets 0xA, quadrant 2 gets 0x5
+    ql[32 + 7] = 0xC3      # half 0: l = 7, quadrant 1 gets 0x3, quadrant 3 gets 0xC
+    ql[64 + 31] = 0x1F     # half 1: l = 31, quadrant 0 gets 0xF, quadrant 2 gets 0x1
+    v = orc.dequantize(gs.Q6_K, _q6k_block(1.0, ql, None, np.ones(16)), 256) + 32
+    exp = np.zeros(256)
+    exp[0 + 3], exp[64 + 3] = 0xA, 0x5
+    exp[32 + 7], exp[96 + 7] = 0x3, 0xC
+    exp[128 + 31], exp[128 + 64 + 31] = 0xF, 0x1
+    assert np.array_equal(v, exp)
+
+
+def test_q6k_equals_q8_0(orc):
+    """A Q6_K row whose d*scale is exact in fp16 equals the Q8_0 row with
+    block scale d*scale per 16-value group (each Q8_0 block split in two
+    groups of equal scale) and quants q-32: built here from the bit fields
+    directly, not through the decoder."""
+    k, n = 512, 3
+    w6 = gs.weights(gs.Q6_K, n, k, cfg=915).reshape(-1, 210)
+    # equal scales within each 32-value quadrant (both 16-groups), d = 2^-10
+    sc = w6[:, 192:208].view(np.int8).copy()
+    sc[:, 1::2] = sc[:, 0::2]
+    w6[:, 192:208] = sc.view(np.uint8)
+    w6[:, 208:210] = np.frombuffer(np.float16(2.0 ** -10).tobytes(), np.uint8)
+    w8 = np.zeros((w6.shape[0], 8, 34), np.uint8)
+    for r in range(w6.shape[0]):
+        ql, qh = w6[r, 0:128].astype(np.int32), w6[r, 128:192].astype(np.int32)
+        for h in range(2):
+            for g in range(4):
+                lb = ql[64 * h + (32 if g % 2 else 0): 64 * h + (32 if g % 2 else 0) + 32]
+                low = (lb & 0x0F) if g < 2 else (lb >> 4)
+                high = (qh[32 * h: 32 * h + 32] >> (2 * g)) & 3
+                q = (low | (high << 4)) - 32
+                s_ = int(sc[r, 8 * h + 2 * g])
+                w8[r, 4 * h + g, 0:2] = np.frombuffer(np.float16(2.0 ** -10 * s_).tobytes(), np.uint8)
+                w8[r, 4 * h + g, 2:] = q.astype(np.int8).view(np.uint8)
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=915))
+    y6, _ = orc.matmul(gs.Q6_K, w6.reshape(n, -1), n, k, xq, 2)
+    y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
+    assert np.array_equal(y6, y8)
+
+
+def test_q6k_scale_sign_and_d(orc):
+    """Negating every scale byte negates the row; doubling d doubles it."""
+    k, n = 512, 4
+    w = gs.weights(gs.Q6_K, n, k, cfg=916).reshape(-1, 210)
+    sc = w[:, 192:208].view(np.int8)
+    keep = sc != -128                       # -(-128) does not fit in int8
+    sc[~keep] = 0
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=916))
+    y0, _ = orc.matmul(gs.Q6_K, w.reshape(n, -1), n, k, xq, 2)
+    wn = w.copy(); wn[:, 192:208] = (-sc).view(np.uint8)
+    yn, _ = orc.matmul(gs.Q6_K, wn.reshape(n, -1), n, k, xq, 2)
+    assert np.array_equal(yn, -y0)
+    w2 = w.copy()
+    d = w2[:, 208:210].copy().view(np.float16)
+    w2[:, 208:210] = (d * np.float16(2)).view(np.uint8)
+    y2, _ = orc.matmul(gs.Q6_K, w2.reshape(n, -1), n, k, xq, 2)
+    assert np.array_equal(y2, 2 * y0)
