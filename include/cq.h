@@ -5,7 +5,8 @@
  * What is computed (pages cited by title and section):
  *   - Weights stay in GGUF block form as stored: Q4_0, Q4_1, Q8_0, Q4_K
  *     (Cera README, "Quantization"; alice-llm 2.0.0 README, "Quantization
- *     Block Specs").  The LM head runs on the weight as stored, not on a
+ *     Block Specs"), and for the decode GEMV also Q6_K, the type of the
+ *     tied-embedding LM head (same table; Cera README, "Performance").  The LM head runs on the weight as stored, not on a
  *     dequantized copy (Cera README, "Performance").
  *   - Activations are quantized on the fly to Q8_0 blocks of 32 (Cera
  *     README, "Quantization"; alice-llm 2.0.0 README, "The CPU Optimization
@@ -32,6 +33,11 @@
  *   Q4_K  256 values, 144 B: d, dmin, 12 bytes of six-bit sub-block scales
  *         and mins, 128 bytes of nibbles (32-byte chunk c: low nibbles =
  *         sub-block 2c, high nibbles = sub-block 2c+1); value d*sc*q - dmin*m.
+ *   Q6_K  256 values, 210 B: ql[128], qh[64], 16 signed 8-bit scales, d.
+ *         In half h (128 values), element l + 32g (l < 32, quadrant g) takes
+ *         a nibble of ql[64h + l] (g = 0 low, g = 2 high) or ql[64h + 32 + l]
+ *         (g = 1 low, g = 3 high), bit pair g of qh[32h + l] as bits 4-5,
+ *         and scale 8h + 2g + l/16; value d*scale*(q-32).
  *   A weight matrix [n][k] is n rows of k/qk consecutive blocks, row-major,
  *   no padding.  MoE expert weights are n_experts such matrices back to back.
  *
@@ -67,7 +73,7 @@ typedef struct ihipStream_t* cq_stream_t;
 typedef enum {
     CQ_OK = 0,
     CQ_ERR_INVALID_ARG = -1,      /* null pointer, negative size, bad flag   */
-    CQ_ERR_UNSUPPORTED_TYPE = -2, /* weight type other than the four below   */
+    CQ_ERR_UNSUPPORTED_TYPE = -2, /* weight type not supported by the call   */
     CQ_ERR_SHAPE = -3,            /* k not a multiple of the block, too big  */
     CQ_ERR_ALIGNMENT = -4,        /* pointer or leading dim misaligned       */
     CQ_ERR_WORKSPACE = -5,        /* reserved                                */
@@ -76,7 +82,7 @@ typedef enum {
 } cq_status;
 
 /* Weight types, numbered as the GGUF tensor type ids. */
-typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12 } cq_type;
+typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q6_K = 14 } cq_type;
 
 #define CQ_ABI_VERSION 1
 #define CQ_GEMV_MAX_BATCH 8
@@ -114,13 +120,13 @@ int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k,
 /*
  * cq_gemv -- decode GEMV for 1..8 activation rows (speculative verify
  * rows included): y[b*ldy + i] = sum_j w_hat[i][j] * x_hat[b][j].
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q6_K.
  *   w      [n][k/qk] blocks, 16-byte aligned.
  *   xq     [batch][k/32] Q8_0 blocks (as written by cq_quantize_q8_0),
  *          2-byte aligned.
  *   batch  1..CQ_GEMV_MAX_BATCH.
  *   y      fp32, row b at y + b*ldy, ldy >= n, 4-byte aligned.
- *   k      multiple of 32 (of 256 for Q4_K), k <= CQ_MAX_K.
+ *   k      multiple of 32 (of 256 for Q4_K and Q6_K), k <= CQ_MAX_K.
  * Each row b of a batched call is bitwise equal to the batch-1 call on that
  * row alone.  Accuracy: |y - y_exact| <= 2e-5 * sum_j |w_hat*x_hat|.
  */
@@ -133,7 +139,9 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  *     y[r*ldy + i] = sum_j w_hat[i][j] * x_hat[r][j]
  * computed as int8 MFMA products of each 32-value block with the two block
  * scales applied per block in fp32.
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K (CQ_Q6_K returns
+ *          CQ_ERR_UNSUPPORTED_TYPE: its 16-value scale groups do not fit the
+ *          32-value MFMA block step).
  *   w      [n][k/qk] blocks, 16-byte aligned; xq [m][k/32] Q8_0 blocks,
  *          4-byte aligned; y fp32 [m][ldy], ldy >= n, 4-byte aligned.
  *   k      multiple of 256, k <= CQ_MAX_K.
@@ -168,7 +176,7 @@ int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
  * where row = p / top_k (x_per_pair = 0: gate/up read the token row) or
  * row = p (x_per_pair = 1: down reads the pair row).  Each expert's weight
  * matrix is streamed once for all of its pairs.
- *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K.
+ *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K (CQ_Q6_K: as cq_gemm).
  *   w_experts  n_experts matrices [n][k/qk], back to back, 16-B aligned.
  *   xq         Q8_0 rows of k/32 blocks (n_tokens or n_tokens*top_k rows).
  *   offsets, pairs  as written by cq_moe_group.

@@ -1,5 +1,5 @@
-// gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K) for
-// 1..8 Q8_0 activation rows.
+// gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K, Q6_K)
+// for 1..8 Q8_0 activation rows.
 //
 // Streaming kernel (HBM-bound; the weights are read exactly once):
 //  * A wave owns a contiguous range of rows.  Every row is loaded with
@@ -35,10 +35,10 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
 
-// columns per lane: a Q4_K column already spans 64 values
-template <int FMT> constexpr int kCMax = (FMT == T_Q4_K) ? 1 : 2;
+// columns per lane: a Q4_K or Q6_K column already spans 64 values
+template <int FMT> constexpr int kCMax = (FMT == T_Q4_K || FMT == T_Q6_K) ? 1 : 2;
 constexpr int kMaxThreads = 512;    // 8 waves
 
 // bytes per block of the 32-value formats
@@ -74,6 +74,16 @@ template <> struct Act<T_Q4_K> {
     float dxa, dxb;
     float ndxa, ndxb;       // -12582912 * dx
     float sa, sb;           // dx * sum(q) of each block
+};
+
+// Q6_K column (64 values): half h of super-block sb, l in [16 i, 16 i + 16)
+// of each of the four 32-value quadrants g; quadrant g of the half is Q8_0
+// activation block 8 sb + 4 h + g, values [16 i, 16 i + 16) of it.
+template <> struct Act<T_Q6_K> {
+    uint32_t q[4][4];  // 16 int8 quants per quadrant
+    float dx[4];
+    float ndx[4];      // -12582912 * dx
+    int start[4];      // kBias - 32 * sum(q): start of the dot with the 6-bit quants
 };
 
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
@@ -153,12 +163,76 @@ __device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col,
     a.ndxb = -kBiasF * a.dxb;
 }
 
+template <>
+__device__ __forceinline__ void load_act<T_Q6_K>(const uint8_t* xq_row, int col, Act<T_Q6_K>& a) {
+    const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(
+            xq_row + static_cast<int64_t>(8 * sb + 4 * h + g) * 34);
+        a.dx[g] = h2f(p[0]);
+        int sum = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int o = 1 + 8 * i + 2 * t;  // 16-bit word of byte 2 + 16 i + 4 t
+            a.q[g][t] = static_cast<uint32_t>(p[o]) | (static_cast<uint32_t>(p[o + 1]) << 16);
+            sum = sdot4(a.q[g][t], 0x01010101u, sum);
+        }
+        a.start[g] = kBias - 32 * sum;
+        a.ndx[g] = -kBiasF * a.dx[g];
+    }
+}
+
 // Byte offset, inside the staged tile, of the block that holds column col
 // of tile row r.
 template <int FMT>
 __device__ __forceinline__ int col_offset(int row_base, int col) {
     if constexpr (FMT == T_Q4_K) return row_base + (col >> 2) * 144;
+    else if constexpr (FMT == T_Q6_K) return row_base + (col >> 2) * 210;
     else return row_base + col * Fmt<FMT>::BS;
+}
+
+// Q6_K 6-bit quants of quadrant g (0..3) from 4 dwords of ql (the low
+// nibbles of ql[l] for g = 0, of ql[l + 32] for g = 1, their high nibbles for
+// g = 2, 3) and 4 dwords of qh (bit pair g of qh[l] goes to bits 4-5).
+__device__ __forceinline__ uint32_t q6k_quant4(uint32_t lqa, uint32_t lqb, uint32_t hq, int g) {
+    const uint32_t l = (g & 1) ? lqb : lqa;
+    const uint32_t nib = (g < 2) ? (l & 0x0F0F0F0Fu) : ((l >> 4) & 0x0F0F0F0Fu);
+    return nib | (((hq >> (2 * g)) & 0x03030303u) << 4);
+}
+
+// acc[j] += one Q6_K column (see Act<T_Q6_K>) of the super-block at LDS byte
+// offset off (2-byte aligned): per quadrant g an integer dot of the 16 6-bit
+// quants with the activation quants from kBias - 32 * sum(qx), then
+// dx * d * scale.
+template <int B>
+__device__ __forceinline__ void q6k_column_dot(const uint8_t* lds, int off, int col,
+                                               const Act<T_Q6_K>* a, float* acc) {
+    const int h = (col >> 1) & 1, i = col & 1;
+    uint32_t qla[4], qlb[4], qh[4], scw[2];
+    lds_dwords_a2<4>(lds, off + 64 * h + 16 * i, qla);
+    lds_dwords_a2<4>(lds, off + 64 * h + 32 + 16 * i, qlb);
+    lds_dwords_a2<4>(lds, off + 128 + 32 * h + 16 * i, qh);
+    lds_dwords_a2<2>(lds, off + 192 + 8 * h, scw);
+    const float d = h2f(lds_u16(lds, off + 208));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        // signed scale byte 2 g + i of the half
+        const int b = 2 * g + i;
+        const int sc = static_cast<int8_t>((scw[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+        const float dsc = d * static_cast<float>(sc);
+        uint32_t q[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = q6k_quant4(qla[t], qlb[t], qh[t], g);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            int s = a[j].start[g];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s = sdot4(q[t], a[j].q[g][t], s);
+            const float sx = fmaf(__int_as_float(s), a[j].dx[g], a[j].ndx[g]);
+            acc[j] = fmaf(sx, dsc, acc[j]);
+        }
+    }
 }
 
 // acc[j] += dot of one column of one weight row with activation row j.
@@ -232,6 +306,8 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
             const float sx = fmaf(__int_as_float(s), a[j].dx, a[j].ndx);
             acc[j] = fmaf(sx, dw, acc[j]);
         }
+    } else if constexpr (FMT == T_Q6_K) {
+        q6k_column_dot<B>(lds, off, col, a, acc);
     } else {  // Q4_K: column = nibble chunk c of super-block at off
         const int c = col & 3;
         const uint4 hdr = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
@@ -827,8 +903,8 @@ constexpr int kRing = 4;  // rows in flight per wave in the streaming kernel
 Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     const int64_t xrb = k / 32 * 34;
     Plan p{};
-    p.ncols = static_cast<int>(wt == T_Q4_K ? k / 64 : k / 32);
-    p.C = (wt == T_Q4_K || p.ncols <= kWave) ? 1 : 2;
+    p.ncols = static_cast<int>(wt == T_Q4_K || wt == T_Q6_K ? k / 64 : k / 32);
+    p.C = (wt == T_Q4_K || wt == T_Q6_K || p.ncols <= kWave) ? 1 : 2;
     p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
     // general kernel: about 16 KiB of weights per tile, at most 32 live
     // accumulators per lane
@@ -844,7 +920,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     // one (type, k) must take the same kernel)
     const int sc = (p.ncols + kWave - 1) / kWave;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !(wt == T_Q4_K && sc == 2))
+        !(wt == T_Q4_K && sc == 2) && wt != T_Q6_K)
         p.SC = sc;
     return p;
 }
@@ -879,8 +955,10 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
 template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
-    if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
-    if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+    if constexpr (FMT != T_Q6_K) {
+        if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+        if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+    }
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
@@ -920,12 +998,17 @@ int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb
     }
 }
 
+int64_t block_bytes_of(int wt) {
+    return wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 210;
+}
+int64_t block_elems_of(int wt) { return wt == T_Q4_K || wt == T_Q6_K ? 256 : 32; }
+
 }  // namespace
 
 // Returns 0, -3 (shape the kernel cannot tile) or -6 (launch failure).
 int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
-    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t bs = block_bytes_of(wt);
+    const int64_t qk = block_elems_of(wt);
     const Plan p = make_plan(wt, k, k / qk * bs, static_cast<int>(batch), false);
     if (p.nw * kWave > kMaxThreads) return -3;
     if (p.tile_lds + p.red_bytes > 65536) return -3;
@@ -935,8 +1018,8 @@ int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
 int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
                 float* y, int64_t ldy, hipStream_t stream) {
     if (gemv_shape_ok(wt, k, batch) != 0) return -3;
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
-    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t bs = block_bytes_of(wt);
+    const int64_t qk = block_elems_of(wt);
     const int64_t rb = k / qk * bs;
     const Plan p = make_plan(wt, k, rb, static_cast<int>(batch),
                              (reinterpret_cast<uintptr_t>(xq) & 15) == 0);
@@ -949,6 +1032,7 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_1: return launch_fmt<T_Q4_1>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q8_0: return launch_fmt<T_Q8_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q4_K: return launch_fmt<T_Q4_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q6_K: return launch_fmt<T_Q6_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         default: return -2;
     }
 }

@@ -43,8 +43,9 @@ def test_version_and_status_strings(lib):
 
 
 def test_block_geometry(lib):
-    assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12)] == [32, 32, 32, 256]
-    assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12)] == [18, 20, 34, 144]
+    assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12, 14)] == [32, 32, 32, 256, 256]
+    assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12, 14)] == [18, 20, 34, 144, 210]
+    assert lib.cq_row_bytes(14, 4096) == 3360
     assert lib.cq_row_bytes(12, 4096) == 2304
     assert lib.cq_row_bytes(8, 4096) == 4352
     assert lib.cq_row_bytes(12, 4000) == -1
@@ -70,6 +71,7 @@ def test_gemv_validation(lib):
     f = lib.cq_gemv
     assert f(7, P(FAKE), 8, 256, P(FAKE), 1, P(FAKE), 8, None) == UNSUPPORTED
     assert f(12, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q4_K needs 256
+    assert f(14, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q6_K needs 256
     assert f(2, P(FAKE), 8, 48, P(FAKE), 1, P(FAKE), 8, None) == SHAPE
     assert f(2, P(FAKE), 8, 256, P(FAKE), 0, P(FAKE), 8, None) == INVALID  # batch 0
     assert f(2, P(FAKE), 8, 256, P(FAKE), 9, P(FAKE), 8, None) == INVALID  # batch 9
@@ -88,6 +90,7 @@ def test_gemm_validation(lib):
     assert f(2, P(FAKE), 8, 256, P(FAKE), -1, P(FAKE), 8, None) == INVALID
     assert f(2, P(FAKE), 8, 256, None, 0, None, 8, None) == OK             # m == 0
     assert f(5, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
+    assert f(14, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED  # Q6_K: GEMV only
 
 
 def test_moe_validation(lib):
@@ -103,6 +106,8 @@ def test_moe_validation(lib):
              None) == SHAPE
     assert m(12, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 0, 4, P(FAKE), 64,
              None) == OK                                                     # no tokens
+    assert m(14, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
+             None) == UNSUPPORTED                                            # Q6_K: GEMV only
     s = lib.cq_swiglu_quantize_q8_0
     assert s(P(FAKE), P(FAKE), 64, 2, 48, None, P(FAKE), None) == SHAPE
     assert s(P(FAKE), P(FAKE + 4), 64, 2, 64, None, P(FAKE), None) == ALIGN

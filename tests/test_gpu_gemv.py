@@ -13,7 +13,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q6_K]
 
 
 def run_gemv(cq, fmt, w, n, k, xq, batch):
@@ -58,16 +58,17 @@ def test_gemv_config_full(cq, orc, name):
         print(f"{name} batch {batch}: max |err|/S = {r:.3e}")
 
 
-def test_gemv_lm_head_sampled(cq, orc):
-    """Q4_K LM head 128256 x 4096 at batch 1 and 4: every output of the first
-    and last row tiles plus 4000 random outputs against the oracle (both
-    batches), and the batch-4 rows equal the batch-1 results bitwise."""
-    name = "q4_k_gemv_lm_head"
+@pytest.mark.parametrize("name", ["q4_k_gemv_lm_head", "q6_k_gemv_lm_head"])
+def test_gemv_lm_head_sampled(cq, orc, name):
+    """LM head 128256 x 4096 (Q4_K; Q6_K, the tied-embedding type) at batch 1
+    and 4: every output of the first and last row tiles plus 4000 random
+    outputs against the oracle (both batches), and the batch-4 rows equal the
+    batch-1 results bitwise."""
     c, w, x = config_inputs(name)
     n, k = c["n"], c["k"]
     xq = orc.quantize_q8_0(x)
     wd, xd = to_dev(w), to_dev(xq)
-    note("gemv lm head b4")
+    note("gemv lm head b4", name)
     y4 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 4))
     note("gemv lm head b1")
     y1 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 1))
@@ -115,10 +116,10 @@ def test_gemv_deterministic_and_scaling(cq, orc, fmt):
     assert np.array_equal(y0, y1)
     # doubling every weight scale (d, and m or dmin) doubles y bitwise
     w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[fmt])
-    nf = 2 if fmt in (gs.Q4_1, gs.Q4_K) else 1
-    for f in range(nf):
-        h = w2[:, 2 * f:2 * f + 2].copy().view(np.float16)
-        w2[:, 2 * f:2 * f + 2] = (h * np.float16(2)).view(np.uint8)
+    offs = [208] if fmt == gs.Q6_K else [0, 2] if fmt in (gs.Q4_1, gs.Q4_K) else [0]
+    for o in offs:
+        h = w2[:, o:o + 2].copy().view(np.float16)
+        w2[:, o:o + 2] = (h * np.float16(2)).view(np.uint8)
     y2 = run_gemv(cq, fmt, w2.reshape(n, -1), n, k, xq, 3)
     assert np.array_equal(y2, 2 * y0)
     # permuting weight rows permutes y
