@@ -237,7 +237,8 @@ def _burst_us(fn, reps, stream):
 def secondary(cq, gs, dev, stream):
     """The other workloads, each timed as a burst of back-to-back launches
     (weights rotated through >= 512 MB of copies where they would fit the
-    Infinity Cache): the 128K-vocabulary Q4_K LM head at batch 1 and 4, the
+    Infinity Cache): the 128K-vocabulary LM head (Q4_K, and Q6_K as for a
+    tied embedding) at batch 1 and 4, the
     2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens, and
     the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
@@ -249,17 +250,19 @@ def secondary(cq, gs, dev, stream):
         ncopy = max(2, -(-min_bytes // host.nbytes) + 1)
         return [base] + [base.clone() for _ in range(ncopy - 1)]
 
-    # LM head
+    # LM head, Q4_K and the tied-embedding Q6_K
     n, k = 128256, 4096
-    wl = copies(gs.weights(gs.Q4_K, n, k, cfg=2))
     xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(4, k, cfg=2)).to(dev))
     y = torch.empty((4, n), dtype=torch.float32, device=dev)
-    for b in (1, 4):
-        us = _burst_us(lambda i: cq.cq_gemv(gs.Q4_K, wl[i % len(wl)], n, k, xq, b, y=y), 50, stream)
-        gbs = wl[0].numel() / us / 1e3
-        out[f"q4_k_lm_head_128256x4096_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
-                                                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
-    del wl
+    for fmt, cfg in ((gs.Q4_K, 2), (gs.Q6_K, 22)):
+        wl = copies(gs.weights(fmt, n, k, cfg=cfg))
+        for b in (1, 4):
+            us = _burst_us(lambda i: cq.cq_gemv(fmt, wl[i % len(wl)], n, k, xq, b, y=y), 50, stream)
+            gbs = wl[0].numel() / us / 1e3
+            out[f"{gs.NAMES[fmt]}_lm_head_128256x4096_b{b}"] = {
+                "us": round(us, 2), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+        del wl
     # 2048 x 2048 Q4_0 GEMV (2.36 MB per call: launch-latency bound)
     n, k = 2048, 2048
     w0 = copies(gs.weights(gs.Q4_0, n, k, cfg=0))

@@ -553,6 +553,10 @@ template <int C> struct Win<T_Q4_K, C> {
     static constexpr bool kMis = false;
     static constexpr int NDW = 4 + 8 * C;                  // header + C nibble chunks
 };
+template <int C> struct Win<T_Q6_K, C> {                 // (reads LDS directly)
+    static constexpr bool kMis = false;
+    static constexpr int NDW = 1;
+};
 
 // acc[j] += block (32 values) at byte offset O of the window, batch row j
 template <int FMT, int B, int O>
@@ -657,15 +661,18 @@ __device__ __forceinline__ void row_dot(const uint32_t* w, const Act<FMT> (*act)
 template <bool V> struct Bool { static constexpr bool value = V; };
 
 // bytes of one lane column: a 32-value block, or a quarter super-block
+// (Q6_K: 210 / 4, rounded up)
 template <int FMT> constexpr int col_bytes() {
     if constexpr (FMT == T_Q4_K) return 36;
+    else if constexpr (FMT == T_Q6_K) return 53;
     else return Fmt<FMT>::BS;
 }
 
 constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per SIMD)
 
 // Largest activation bytes (all batch rows) one streaming workgroup stages.
-template <int FMT, int B, int C> constexpr int kActMax = B * (FMT == T_Q4_K ? 128 : 64) * C * 34;
+template <int FMT, int B, int C>
+constexpr int kActMax = B * (FMT == T_Q4_K || FMT == T_Q6_K ? 128 : 64) * C * 34;
 
 template <int FMT, int B, int C, int P>
 __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
@@ -677,20 +684,21 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // [1024 j + 16 l, +16), so every load instruction reads one contiguous KiB
     constexpr int NJ = (kWave * C * col_bytes<FMT>() + 1023) / 1024;
     constexpr int XMAX = kActMax<FMT, B, C>;
-    constexpr int NBMAX = XMAX / 34;                             // activation blocks, all rows
+    // Converted activation blocks in lane order: slot h of column C*l + i of
+    // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
+    // read consecutive words (no bank conflicts).  A slot is one Q8_0 block
+    // (Q6_K: the 16 values of one quadrant that the column covers).
+    constexpr int NS = FMT == T_Q4_K ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
+    constexpr int NP = kWave * C;                                  // column positions per row
+    constexpr int NBMAX = B * NS * NP;                             // slots, all rows
     constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
     constexpr int RAW = (XMAX + 16 > kGW * STG) ? XMAX + 16 : kGW * STG;
     // raw activation copy first, the waves' row staging buffers afterwards
     __shared__ __align__(16) uint8_t raw[RAW];
-    // Converted activation blocks in lane order: block h of column C*l + i of
-    // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
-    // read consecutive words (no bank conflicts).
-    constexpr int NS = FMT == T_Q4_K ? 2 : 1;  // Q8_0 blocks per column
-    constexpr int NP = kWave * C;              // column positions per row
-    __shared__ __align__(16) u32x4 xq0[NBMAX];  // quants 0..15
+    __shared__ __align__(16) u32x4 xq0[NBMAX];  // quants 0..15 (Q6_K: the slot's 16)
     __shared__ __align__(16) u32x4 xq1[NBMAX];  // quants 16..31
     __shared__ float xda[NBMAX];                // dx
-    __shared__ float xau[NBMAX];                // dx*sum(q) (Q4_0: the integer sum)
+    __shared__ float xau[NBMAX];                // dx*sum(q) (Q4_0, Q6_K: the integer sum)
     // (the wave index is read from lane 0 so the compiler keeps every
     // per-wave row quantity in scalar registers)
     const int lane = threadIdx.x & (kWave - 1);
@@ -710,6 +718,9 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         off = (ch >> 2) * 144;
         c0 = ch & 3;
         qoff = off + 16 + 32 * c0;
+    } else if constexpr (FMT == T_Q6_K) {
+        c0 = valid ? C * lane : 0;               // the column
+        off = (c0 >> 2) * 210;
     } else {
         off = valid ? C * lane * Fmt<FMT>::BS : 0;
     }
@@ -764,12 +775,15 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             const int gi = t0 + static_cast<int>(threadIdx.x);
             if (gi < NG) {
                 const int j = gi / (NS * NP), h = (gi / NP) % NS, pp = gi % NP;
-                const int blk = (C * (pp % kWave) + pp / kWave) * NS + h;
+                const int col = C * (pp % kWave) + pp / kWave;
+                // Q6_K: quadrant h of the column's half, values [16 i, +16)
+                const int blk = FMT == T_Q6_K ? 8 * (col >> 2) + 4 * ((col >> 1) & 1) + h : col * NS + h;
+                const int qofs = FMT == T_Q6_K ? 16 * (col & 1) : 0;
                 uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 float dx = 0.0f;
                 if (blk < nbr) {
                     const int bo = j * static_cast<int>(xq_row_bytes) + blk * 34;
-                    const int qb = bo + 2;
+                    const int qb = bo + 2 + qofs;
                     const uint32_t* pq = reinterpret_cast<const uint32_t*>(xs + (qb & ~3));
                     const uint32_t sh = static_cast<uint32_t>(qb & 2) * 8;
                     uint32_t wd[9];
@@ -782,7 +796,12 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                 xq0[gi] = u32x4{q[0], q[1], q[2], q[3]};
                 xq1[gi] = u32x4{q[4], q[5], q[6], q[7]};
                 xda[gi] = dx;
-                if constexpr (FMT != T_Q8_0) {
+                if constexpr (FMT == T_Q6_K) {
+                    int sum = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sum = sdot4(q[u], 0x01010101u, sum);
+                    xau[gi] = __int_as_float(sum);
+                } else if constexpr (FMT != T_Q8_0) {
                     int sum = 0;
 #pragma unroll
                     for (int u = 0; u < 8; ++u) sum = sdot4(q[u], 0x01010101u, sum);
@@ -798,7 +817,18 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     for (int i = 0; i < C; ++i)
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            if constexpr (FMT == T_Q4_K) {
+            if constexpr (FMT == T_Q6_K) {
+                Act<T_Q6_K>& a = act[i][j];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int gi = (j * NS + g) * NP + kWave * i + lane;
+                    const u32x4 q0 = xq0[gi];
+                    a.q[g][0] = q0.x; a.q[g][1] = q0.y; a.q[g][2] = q0.z; a.q[g][3] = q0.w;
+                    a.dx[g] = xda[gi];
+                    a.ndx[g] = -kBiasF * a.dx[g];
+                    a.start[g] = kBias - 32 * __float_as_int(xau[gi]);
+                }
+            } else if constexpr (FMT == T_Q4_K) {
                 Act<T_Q4_K>& a = act[i][j];
                 const int ga = 2 * j * NP + lane, gb = ga + NP;
                 const u32x4 a0 = xq0[ga], a1 = xq1[ga], b0 = xq0[gb], b1 = xq1[gb];
@@ -859,7 +889,10 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             uint32_t v[W::NDW];
-            if constexpr (FMT == T_Q4_K) {
+            if constexpr (FMT == T_Q6_K) {
+                static_assert(C == 1, "one Q6_K column per lane");
+                q6k_column_dot<B>(stage, off, c0, act[0], acc[i]);
+            } else if constexpr (FMT == T_Q4_K) {
                 const uint4 h = *reinterpret_cast<const uint4*>(stage + off);
                 v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
 #pragma unroll
@@ -877,7 +910,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     v[W::NDW - 1] >>= mis;
                 }
             }
-            row_dot<FMT, B, C>(v, act, c0, acc[i]);
+            if constexpr (FMT != T_Q6_K) row_dot<FMT, B, C>(v, act, c0, acc[i]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -920,7 +953,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     // one (type, k) must take the same kernel)
     const int sc = (p.ncols + kWave - 1) / kWave;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !(wt == T_Q4_K && sc == 2) && wt != T_Q6_K)
+        !((wt == T_Q4_K || wt == T_Q6_K) && sc == 2))
         p.SC = sc;
     return p;
 }
@@ -955,10 +988,9 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
 template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
-    if constexpr (FMT != T_Q6_K) {
-        if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+    if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+    if constexpr (FMT != T_Q4_K && FMT != T_Q6_K)  // (one column per lane for these)
         if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
-    }
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
