@@ -7,7 +7,8 @@ draws into block fields (fp16 scale fields at their byte offsets, uniformly
 random bytes for packed quants).  Uniform random bytes give uniform 4-bit
 quants and, for Q4_K, uniform independent 6-bit scales and mins, because
 the 12 scale bytes carry each of their 96 bits in exactly one of the 16
-six-bit fields; for Q6_K, uniform 6-bit quants (every bit of ql and qh
+six-bit fields; for Q5_K the same plus uniform 5-bit quants (each qh bit
+is the top bit of exactly one quant); for Q6_K, uniform 6-bit quants (every bit of ql and qh
 belongs to exactly one quant) and uniform signed 8-bit scales.
 
 Streams: numpy.random.default_rng([20261202, cfg, tensor]) with tensor ids
@@ -18,11 +19,11 @@ import numpy as np
 
 SEED = 20261202
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q6_K = 2, 3, 8, 12, 14
-FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q6_k": Q6_K}
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K = 2, 3, 8, 12, 13, 14
+FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 NAMES = {v: k for k, v in FORMATS.items()}
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 # scale distributions (fp64 uniform draws, rounded to fp16 by numpy)
 D_RANGE = (1e-3, 2e-2)
@@ -65,6 +66,10 @@ def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
         out[:, 0:2] = _f16_field(gs, nblk, *d_range)   # d
         out[:, 2:4] = _f16_field(gs, nblk, *d_range)   # dmin
         out[:, 4:144] = gq.integers(0, 256, size=(nblk, 140), dtype=np.uint8)
+    elif fmt == Q5_K:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)   # d
+        out[:, 2:4] = _f16_field(gs, nblk, *d_range)   # dmin
+        out[:, 4:176] = gq.integers(0, 256, size=(nblk, 172), dtype=np.uint8)  # scales, qh, qs
     elif fmt == Q6_K:
         # ql[128], qh[64], 16 signed scale bytes: uniform random bytes;
         # d (fp16) last
@@ -108,6 +113,9 @@ CONFIGS = {
     "q4_k_gemv_lm_head": dict(cfg=2, kind="gemv", fmt=Q4_K, n=128256, k=4096, batches=(1, 4)),
     # the tied-embedding LM head in Q6_K (a "next" type: GEMV only)
     "q6_k_gemv_lm_head": dict(cfg=22, kind="gemv", fmt=Q6_K, n=128256, k=4096, batches=(1, 4)),
+    # Q5_K (the FFN type of Q5_K_M models): decode GEMV and prefill GEMM
+    "q5_k_gemv_ffn_up": dict(cfg=15, kind="gemv", fmt=Q5_K, n=14336, k=4096, batches=(1, 5)),
+    "q5_k_gemm_prefill_512": dict(cfg=25, kind="gemm", fmt=Q5_K, n=14336, k=4096, m=512),
     "q4_0_gemm_prefill_512": dict(cfg=3, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=512),
     "q4_0_gemm_prefill_2048": dict(cfg=13, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=2048),
     "q4_k_moe_ffn": dict(cfg=4, kind="moe", fmt=Q4_K, n_tokens=256, hidden=2048, ffn=1536,

@@ -81,7 +81,7 @@ uint16_t rd16(const uint8_t* p) {   /* little-endian 16-bit field */
 int64_t elems_of(int type) {
     switch (type) {
         case ORACLE_Q4_0: case ORACLE_Q4_1: case ORACLE_Q8_0: return 32;
-        case ORACLE_Q4_K: case ORACLE_Q6_K: return 256;
+        case ORACLE_Q4_K: case ORACLE_Q5_K: case ORACLE_Q6_K: return 256;
         default: return -1;
     }
 }
@@ -92,6 +92,7 @@ int64_t bytes_of(int type) {
         case ORACLE_Q4_1: return 20;   /* fp16 d + fp16 m + 16 bytes      */
         case ORACLE_Q8_0: return 34;   /* fp16 d + 32 int8 [alice-QBS]    */
         case ORACLE_Q4_K: return 144;  /* 2 + 2 + 12 + 128 [alice-QBS]    */
+        case ORACLE_Q5_K: return 176;  /* 2 + 2 + 12 + 32 + 128 [alice-Q5K] */
         case ORACLE_Q6_K: return 210;  /* 128 + 64 + 16 + 2 [alice-Q6K]   */
         default: return -1;
     }
@@ -109,6 +110,18 @@ void q4k_scale_min(const uint8_t* S, int j, int* sc, int* mn) {
         *sc = (S[j + 4] & 0x0F) | ((S[j - 4] >> 6) << 4);
         *mn = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
     }
+}
+
+/* Q5_K: 5-bit quant (0..31) of element e (0..255) of the super-block at b,
+ * per the reading in oracle.h: low four bits from the qs nibble, bit 4 from
+ * bit (sub-block) of qh[e % 32]. */
+int q5k_quant(const uint8_t* b, int e) {
+    const uint8_t* qh = b + 16;
+    const uint8_t* qs = b + 48;
+    const int j = e / 32, l = e % 32, c = j / 2;
+    const uint8_t byte = qs[32 * c + l];
+    const int low = (j % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return low | (((qh[l] >> j) & 1) << 4);
 }
 
 /* Q6_K: 6-bit quant (0..63) and signed scale of element e (0..255) of the
@@ -163,6 +176,16 @@ void decode_block(int type, const uint8_t* b, double* out) {
                     out[64 * c + i]      = d * sc_lo * (Q[32 * c + i] & 0x0F) - dmin * m_lo;
                     out[64 * c + 32 + i] = d * sc_hi * (Q[32 * c + i] >> 4) - dmin * m_hi;
                 }
+            }
+            break;
+        }
+        case ORACLE_Q5_K: {
+            const double d = half_value(rd16(b));
+            const double dmin = half_value(rd16(b + 2));
+            for (int e = 0; e < 256; ++e) {
+                int sc, mn;
+                q4k_scale_min(b + 4, e / 32, &sc, &mn);
+                out[e] = d * sc * q5k_quant(b, e) - dmin * mn;
             }
             break;
         }
@@ -280,6 +303,25 @@ double factored_dot(int type, const uint8_t* wrow, const uint8_t* xrow, int64_t 
                 const double dx = half_value(rd16(xb));
                 const int8_t* xq = reinterpret_cast<const int8_t*>(xb + 2);
                 /* d*dx*sc*sum(q*qx) - dmin*dx*m*sum(qx) [alice-Q4K] */
+                acc += d * dx * sc * static_cast<double>(idot32(q, xq)) -
+                       dmin * dx * mn * static_cast<double>(isum32(xq));
+            }
+        }
+        return acc;
+    }
+    if (type == ORACLE_Q5_K) {
+        /* as Q4_K per 32-element sub-block, with 5-bit quants [alice-Q5K] */
+        for (int64_t sb = 0; sb < k / 256; ++sb) {
+            const uint8_t* b = wrow + sb * 176;
+            const double d = half_value(rd16(b)), dmin = half_value(rd16(b + 2));
+            for (int j = 0; j < 8; ++j) {
+                int sc, mn;
+                q4k_scale_min(b + 4, j, &sc, &mn);
+                int q[32];
+                for (int i = 0; i < 32; ++i) q[i] = q5k_quant(b, 32 * j + i);
+                const uint8_t* xb = xrow + (sb * 8 + j) * 34;
+                const double dx = half_value(rd16(xb));
+                const int8_t* xq = reinterpret_cast<const int8_t*>(xb + 2);
                 acc += d * dx * sc * static_cast<double>(idot32(q, xq)) -
                        dmin * dx * mn * static_cast<double>(isum32(xq));
             }

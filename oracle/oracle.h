@@ -30,6 +30,9 @@
  *                 by expert is the stated follow-up.
  *   [alice-GPU]   alice-llm 2.0.0 README, "The GPU Optimization Journey",
  *                 phase 4: fused SwiGLU (gate + up + silu x mul).
+ *   [alice-Q5K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
+ *                 a Q5_K super-block is 176 bytes for 256 values (5.5 bpw),
+ *                 fields d (fp16), dmin (fp16), scales[12], qh[32], qs[128].
  *   [alice-Q6K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
  *                 a Q6_K super-block is 210 bytes for 256 values, fields
  *                 ql[128], qh[64], scales[16], d (fp16); and the NEON matvec
@@ -46,6 +49,12 @@
  *     (see oracle_q4k_scale_min); qs chunk c (32 bytes) holds sub-block 2c
  *     in low nibbles and sub-block 2c+1 in high nibbles.  Value
  *     d*sc*q - dmin*m.
+ *   - Q5_K: d, dmin and the 12 scale bytes as in Q4_K (same six-bit
+ *     scale/min packing); qs chunk c (32 bytes) holds the low four bits of
+ *     sub-block 2c in low nibbles and of sub-block 2c+1 in high nibbles, as
+ *     in Q4_K; bit j of qh[l] (l in 0..31) is bit 4 of element l of
+ *     sub-block j.  Quants 0..31, value d*sc*q - dmin*m.  This is the GGUF
+ *     layout (the pages give only the fields and their sizes).
  *   - Q6_K: each 128-value half h uses ql[64h..64h+63], qh[32h..32h+31]
  *     and scales[8h..8h+7].  For l in 0..31 the 6-bit quants of elements
  *     l, l+32, l+64, l+96 of the half are the low nibble of ql[l], the low
@@ -75,6 +84,7 @@ enum {
     ORACLE_Q4_1 = 3,
     ORACLE_Q8_0 = 8,
     ORACLE_Q4_K = 12,
+    ORACLE_Q5_K = 13,
     ORACLE_Q6_K = 14
 };
 

@@ -43,6 +43,10 @@ def test_block_sizes_match_pages(orc):
     # 6.5625 bits per weight, same table
     assert (orc.block_elems(orc.Q6_K), orc.block_bytes(orc.Q6_K)) == (256, 210)
     assert 128 + 64 + 16 + 2 == 210 and 210 * 8 / 256 == 6.5625
+    # Q5_K: 256 values in 176 bytes (d + dmin + scales[12] + qh[32] + qs[128]),
+    # 5.5 bits per weight, same table
+    assert (orc.block_elems(orc.Q5_K), orc.block_bytes(orc.Q5_K)) == (256, 176)
+    assert 2 + 2 + 12 + 32 + 128 == 176 and 176 * 8 / 256 == 5.5
     assert orc.block_bytes(99) == -1
 
 
@@ -312,7 +316,7 @@ def test_q4k_subblock_equals_q4_1(orc):
     assert np.array_equal(yk, y1)
 
 
-@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q6_K])
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K])
 def test_two_formulations_agree(orc, fmt):
     n, m, k = 33, 5, 1024
     w = gs.weights(fmt, n, k, cfg=914)
@@ -327,7 +331,7 @@ def test_two_formulations_agree(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt,k", [(gs.Q4_0, 32), (gs.Q4_1, 64), (gs.Q8_0, 96), (gs.Q4_K, 256),
-                                   (gs.Q4_K, 512), (gs.Q6_K, 256)])
+                                   (gs.Q4_K, 512), (gs.Q5_K, 256), (gs.Q6_K, 256)])
 def test_exact_rational_brute_force(orc, fmt, k):
     """Tiny shapes in exact rational arithmetic: the fp64 sums must agree
     with the exact value to within the fp64 summation bound."""
@@ -539,3 +543,82 @@ def test_q6k_scale_sign_and_d(orc):
     w2[:, 208:210] = (d * np.float16(2)).view(np.uint8)
     y2, _ = orc.matmul(gs.Q6_K, w2.reshape(n, -1), n, k, xq, 2)
     assert np.array_equal(y2, 2 * y0)
+
+
+# ------------------------------------------------------------------- Q5_K
+# alice-llm 2.0.0 README, Quantization Block Specs: Q5_K = d (fp16) + dmin
+# (fp16) + scales[12] + qh[32] + qs[128], 176 bytes for 256 values.  Reading:
+# d, dmin, scales and the qs nibbles as in Q4_K; bit j of qh[l] is bit 4 of
+# element l of sub-block j; value d*sc*q - dmin*m with q in 0..31.
+
+def _q5k_from_q4k(wk, qh=None):
+    """Q5_K blocks carrying the fields of Q4_K blocks wk ([nb][144]) and the
+    given qh bytes ([nb][32], default zeros)."""
+    nb = wk.shape[0]
+    w5 = np.zeros((nb, 176), np.uint8)
+    w5[:, 0:16] = wk[:, 0:16]
+    w5[:, 16:48] = 0 if qh is None else qh
+    w5[:, 48:176] = wk[:, 16:144]
+    return w5
+
+
+def test_q5k_without_high_bits_is_q4k(orc):
+    """With qh all zero every element decodes exactly as the Q4_K block with
+    the same d, dmin, scales and qs: pins the offsets of d, dmin, the scale
+    bytes and qs (byte 48) against the pinned Q4_K decode."""
+    wk = gs.weights(gs.Q4_K, 1, 2048, cfg=920).reshape(-1, 144)
+    w5 = _q5k_from_q4k(wk)
+    for b in range(wk.shape[0]):
+        assert np.array_equal(orc.dequantize(gs.Q5_K, w5[b], 256), orc.dequantize(gs.Q4_K, wk[b], 256))
+
+
+@pytest.mark.parametrize("j", range(8))
+def test_q5k_high_bit_one_hot(orc, j):
+    """Setting bit j of qh[l] raises exactly element 32*j + l, by 16*d*sc_j
+    (the fifth bit of that quant), and nothing else."""
+    wk = gs.weights(gs.Q4_K, 1, 256, cfg=921 + j).reshape(-1, 144)
+    d = float(np.frombuffer(wk[0, 0:2].tobytes(), np.float16)[0])
+    sc, _ = orc.q4k_scale_min(wk[0, 4:16], j)
+    base = orc.dequantize(gs.Q5_K, _q5k_from_q4k(wk)[0], 256)
+    for l in (0, 1, 7, 16, 30, 31):
+        qh = np.zeros((1, 32), np.uint8)
+        qh[0, l] = 1 << j
+        v = orc.dequantize(gs.Q5_K, _q5k_from_q4k(wk, qh)[0], 256)
+        diff = v - base
+        assert np.count_nonzero(diff) == (1 if sc else 0)
+        assert diff[32 * j + l] == 16 * d * sc
+
+
+def test_q5k_high_bits_add(orc):
+    """The high bits of all elements act independently: with every qh bit
+    set, each element is its Q4_K value plus 16*d*sc of its sub-block."""
+    wk = gs.weights(gs.Q4_K, 1, 512, cfg=930).reshape(-1, 144)
+    for b in range(wk.shape[0]):
+        d = float(np.frombuffer(wk[b, 0:2].tobytes(), np.float16)[0])
+        v4 = orc.dequantize(gs.Q4_K, wk[b], 256)
+        v5 = orc.dequantize(gs.Q5_K, _q5k_from_q4k(wk[b:b + 1], np.full((1, 32), 255, np.uint8))[0], 256)
+        for j in range(8):
+            sc, _ = orc.q4k_scale_min(wk[b, 4:16], j)
+            assert np.array_equal(v5[32 * j: 32 * j + 32], v4[32 * j: 32 * j + 32] + 16 * d * sc)
+
+
+def test_q5k_matmul_equals_q4k_plus_high_part(orc):
+    """y over a Q5_K row = y over its Q4_K part + y over the Q8_0 row whose
+    quants are 16 at the set qh bits, scale d*sc (exact: d = 2^-8, dmin
+    any), built block by block from the qh bits alone."""
+    n, k = 3, 512
+    wk = gs.weights(gs.Q4_K, n, k, cfg=931).reshape(-1, 144)
+    wk[:, 0:2] = np.frombuffer(np.float16(2.0 ** -8).tobytes(), np.uint8)
+    qh = gs.rng(931, 5).integers(0, 256, size=(wk.shape[0], 32), dtype=np.uint8)
+    w5 = _q5k_from_q4k(wk, qh)
+    w8 = np.zeros((wk.shape[0] * 8, 34), np.uint8)
+    for b in range(wk.shape[0]):
+        for j in range(8):
+            sc, _ = orc.q4k_scale_min(wk[b, 4:16], j)
+            w8[8 * b + j, 0:2] = np.frombuffer(np.float16(2.0 ** -8 * sc).tobytes(), np.uint8)
+            w8[8 * b + j, 2:34] = ((qh[b] >> j) & 1) * 16
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=931))
+    y5, _ = orc.matmul(gs.Q5_K, w5.reshape(n, -1), n, k, xq, 2)
+    y4, _ = orc.matmul(gs.Q4_K, wk.reshape(n, -1), n, k, xq, 2)
+    y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
+    assert np.allclose(y5, y4 + y8, rtol=0, atol=1e-12 * np.abs(y5).max())
