@@ -5,9 +5,11 @@
  * What is computed (pages cited by title and section):
  *   - Weights stay in GGUF block form as stored: Q4_0, Q4_1, Q8_0, Q4_K
  *     (Cera README, "Quantization"; alice-llm 2.0.0 README, "Quantization
- *     Block Specs"), and for the decode GEMV also Q6_K, the type of the
- *     tied-embedding LM head (same table; Cera README, "Performance").  The LM head runs on the weight as stored, not on a
- *     dequantized copy (Cera README, "Performance").
+ *     Block Specs"), Q5_K (same table; Cera README, "Quantization"), and
+ *     for the decode GEMV also Q6_K, the type of the tied-embedding LM head
+ *     (same table; Cera README, "Performance").  The LM head runs on the
+ *     weight as stored, not on a dequantized copy (Cera README,
+ *     "Performance").
  *   - Activations are quantized on the fly to Q8_0 blocks of 32 (Cera
  *     README, "Quantization"; alice-llm 2.0.0 README, "The CPU Optimization
  *     Journey", Phase 4).
@@ -33,6 +35,9 @@
  *   Q4_K  256 values, 144 B: d, dmin, 12 bytes of six-bit sub-block scales
  *         and mins, 128 bytes of nibbles (32-byte chunk c: low nibbles =
  *         sub-block 2c, high nibbles = sub-block 2c+1); value d*sc*q - dmin*m.
+ *   Q5_K  256 values, 176 B: d, dmin, 12 scale bytes as Q4_K, qh[32], then
+ *         128 bytes of nibbles as Q4_K; bit j of qh[l] is bit 4 of element l
+ *         of sub-block j (quants 0..31); value d*sc*q - dmin*m.
  *   Q6_K  256 values, 210 B: ql[128], qh[64], 16 signed 8-bit scales, d.
  *         In half h (128 values), element l + 32g (l < 32, quadrant g) takes
  *         a nibble of ql[64h + l] (g = 0 low, g = 2 high) or ql[64h + 32 + l]
@@ -82,7 +87,8 @@ typedef enum {
 } cq_status;
 
 /* Weight types, numbered as the GGUF tensor type ids. */
-typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q6_K = 14 } cq_type;
+typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q5_K = 13,
+               CQ_Q6_K = 14 } cq_type;
 
 #define CQ_ABI_VERSION 1
 #define CQ_GEMV_MAX_BATCH 8
@@ -120,13 +126,13 @@ int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k,
 /*
  * cq_gemv -- decode GEMV for 1..8 activation rows (speculative verify
  * rows included): y[b*ldy + i] = sum_j w_hat[i][j] * x_hat[b][j].
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q6_K.
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K.
  *   w      [n][k/qk] blocks, 16-byte aligned.
  *   xq     [batch][k/32] Q8_0 blocks (as written by cq_quantize_q8_0),
  *          2-byte aligned.
  *   batch  1..CQ_GEMV_MAX_BATCH.
  *   y      fp32, row b at y + b*ldy, ldy >= n, 4-byte aligned.
- *   k      multiple of 32 (of 256 for Q4_K and Q6_K), k <= CQ_MAX_K.
+ *   k      multiple of 32 (of 256 for Q4_K, Q5_K and Q6_K), k <= CQ_MAX_K.
  * Each row b of a batched call is bitwise equal to the batch-1 call on that
  * row alone.  Accuracy: |y - y_exact| <= 2e-5 * sum_j |w_hat*x_hat|.
  */
@@ -139,7 +145,7 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  *     y[r*ldy + i] = sum_j w_hat[i][j] * x_hat[r][j]
  * computed as int8 MFMA products of each 32-value block with the two block
  * scales applied per block in fp32.
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K (CQ_Q6_K returns
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K (CQ_Q6_K returns
  *          CQ_ERR_UNSUPPORTED_TYPE: its 16-value scale groups do not fit the
  *          32-value MFMA block step).
  *   w      [n][k/qk] blocks, 16-byte aligned; xq [m][k/32] Q8_0 blocks,
@@ -176,7 +182,8 @@ int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
  * where row = p / top_k (x_per_pair = 0: gate/up read the token row) or
  * row = p (x_per_pair = 1: down reads the pair row).  Each expert's weight
  * matrix is streamed once for all of its pairs.
- *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K (CQ_Q6_K: as cq_gemm).
+ *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K (CQ_Q6_K: as
+ *              cq_gemm).
  *   w_experts  n_experts matrices [n][k/qk], back to back, 16-B aligned.
  *   xq         Q8_0 rows of k/32 blocks (n_tokens or n_tokens*top_k rows).
  *   offsets, pairs  as written by cq_moe_group.

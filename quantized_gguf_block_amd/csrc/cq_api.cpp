@@ -27,7 +27,7 @@ std::atomic<int> g_cu_count[kMaxDevices];
 int64_t elems(int t) {
     switch (t) {
         case CQ_Q4_0: case CQ_Q4_1: case CQ_Q8_0: return 32;
-        case CQ_Q4_K: case CQ_Q6_K: return 256;
+        case CQ_Q4_K: case CQ_Q5_K: case CQ_Q6_K: return 256;
         default: return -1;
     }
 }
@@ -37,6 +37,7 @@ int64_t bytes(int t) {
         case CQ_Q4_1: return 20;
         case CQ_Q8_0: return 34;
         case CQ_Q4_K: return 144;
+        case CQ_Q5_K: return 176;
         case CQ_Q6_K: return 210;
         default: return -1;
     }
@@ -88,7 +89,7 @@ const char* cq_status_string(int status) {
     switch (status) {
         case CQ_OK: return "CQ_OK";
         case CQ_ERR_INVALID_ARG: return "CQ_ERR_INVALID_ARG: null pointer, negative size or bad flag";
-        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K everywhere; Q6_K in cq_gemv)";
+        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K everywhere; Q6_K in cq_gemv)";
         case CQ_ERR_SHAPE: return "CQ_ERR_SHAPE: k is not a whole number of blocks or exceeds the kernel's limit";
         case CQ_ERR_ALIGNMENT: return "CQ_ERR_ALIGNMENT: pointer or leading dimension misaligned";
         case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE";

@@ -33,7 +33,11 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13 };
+
+// Q4_K and Q5_K share the super-block header and nibble chunks (Q5_K adds a
+// high bit per value from qh[32])
+template <int FMT> constexpr bool kK45 = (FMT == T_Q4_K || FMT == T_Q5_K);
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -45,7 +49,7 @@ constexpr int kThreads = 256;
 constexpr int kBias = 0x4B400000;
 constexpr float kBiasF = 12582912.0f;
 
-template <int FMT> constexpr bool kHasOffset = (FMT == T_Q4_1 || FMT == T_Q4_K);
+template <int FMT> constexpr bool kHasOffset = (FMT == T_Q4_1 || kK45<FMT>);
 
 // Workgroup tile of BM tokens x BN weight rows: 4 waves arranged WMW x WNW,
 // each wave MI x NI tiles of 32 x 32.
@@ -112,6 +116,9 @@ template <int FMT> struct WRaw {      // two 32-value blocks of one row
 template <> struct WRaw<T_Q4_K> {     // super-block header + one 32-byte chunk
     uint32_t hdr[4], q[8];
 };
+template <> struct WRaw<T_Q5_K> {     // header, the 32 qh bytes, one 32-byte chunk
+    uint32_t hdr[4], qh[8], q[8];
+};
 struct XRaw {                         // two Q8_0 activation blocks
     uint32_t v[17];
 };
@@ -121,15 +128,22 @@ __device__ __forceinline__ void load_weights(WRaw<FMT>& r, const uint8_t* __rest
                                              int64_t rb, int64_t n0, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
     const int64_t gn = n0 + row < n ? n0 + row : n - 1;
-    if constexpr (FMT == T_Q4_K) {
+    if constexpr (kK45<FMT>) {
         // a 256-value super-block spans two k steps; this step holds nibble
         // chunks 2*(kstep&1) and +1, this thread chunk c (sub-blocks 2c, 2c+1)
+        constexpr int SB = FMT == T_Q4_K ? 144 : 176, QS = FMT == T_Q4_K ? 16 : 48;
         const int c = 2 * (kstep & 1) + half;
-        const uint8_t* p = w + gn * rb + static_cast<int64_t>(kstep >> 1) * 144;
+        const uint8_t* p = w + gn * rb + static_cast<int64_t>(kstep >> 1) * SB;
         const uint4 hv = *reinterpret_cast<const uint4*>(p);
         r.hdr[0] = hv.x; r.hdr[1] = hv.y; r.hdr[2] = hv.z; r.hdr[3] = hv.w;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+        if constexpr (FMT == T_Q5_K) {
+            const uint4 h0 = *reinterpret_cast<const uint4*>(p + 16);
+            const uint4 h1 = *reinterpret_cast<const uint4*>(p + 32);
+            r.qh[0] = h0.x; r.qh[1] = h0.y; r.qh[2] = h0.z; r.qh[3] = h0.w;
+            r.qh[4] = h1.x; r.qh[5] = h1.y; r.qh[6] = h1.z; r.qh[7] = h1.w;
+        }
+        const uint4 v0 = *reinterpret_cast<const uint4*>(p + QS + 32 * c);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(p + QS + 16 + 32 * c);
         r.q[0] = v0.x; r.q[1] = v0.y; r.q[2] = v0.z; r.q[3] = v0.w;
         r.q[4] = v1.x; r.q[5] = v1.y; r.q[6] = v1.z; r.q[7] = v1.w;
     } else {
@@ -144,7 +158,7 @@ __device__ __forceinline__ void load_weights(WRaw<FMT>& r, const uint8_t* __rest
 template <int FMT, class S>
 __device__ __forceinline__ void store_weights(S& s, const WRaw<FMT>& r, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
-    if constexpr (FMT == T_Q4_K) {
+    if constexpr (kK45<FMT>) {
         const int c = 2 * (kstep & 1) + half;
         const float d = h2f(r.hdr[0] & 0xFFFFu), dmin = h2f(r.hdr[0] >> 16);
         const uint32_t S0 = r.hdr[1], S1 = r.hdr[2], S2 = r.hdr[3];
@@ -165,7 +179,11 @@ __device__ __forceinline__ void store_weights(S& s, const WRaw<FMT>& r, int kste
             s.cw[b][row] = -(dmin * static_cast<float>(mn));
             uint32_t o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = e ? nib_hi(r.q[i]) : nib_lo(r.q[i]);
+            for (int i = 0; i < 8; ++i) {
+                o[i] = e ? nib_hi(r.q[i]) : nib_lo(r.q[i]);
+                // Q5_K: bit j of qh byte l is bit 4 of value l of sub-block j
+                if constexpr (FMT == T_Q5_K) o[i] |= ((r.qh[i] >> j) & 0x01010101u) << 4;
+            }
             uint4* d4 = reinterpret_cast<uint4*>(s.w + row * ROW + 32 * b);
             d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
             d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -721,8 +739,8 @@ int gemm_shape_ok(int wt, int64_t k) {
 
 int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,
                 int64_t ldy, hipStream_t stream) {
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
-    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 176;
+    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
     const int64_t tiles_m = (m + 127) / 128, tiles_n = (n + 127) / 128;
     const int64_t tiles = tiles_m * tiles_n;
@@ -736,6 +754,7 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_1: hipLaunchKernelGGL(gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q8_0: hipLaunchKernelGGL(gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q4_K: hipLaunchKernelGGL(gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
+        case T_Q5_K: hipLaunchKernelGGL(gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         default: return -2;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;
@@ -751,8 +770,8 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
                     const void* xq, int x_per_pair, const int32_t* offsets,
                     const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
                     int64_t ldy, hipStream_t stream) {
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : 144;
-    const int64_t qk = wt == T_Q4_K ? 256 : 32;
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 176;
+    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
     const int64_t tiles_n = (n + 127) / 128;
     const int64_t np = n_tokens * top_k;
@@ -765,6 +784,7 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
         case T_Q4_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q4_1: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q8_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q5_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q4_K: {
             const dim3 gs(static_cast<unsigned>((n + kSbRows - 1) / kSbRows), static_cast<unsigned>(n_experts));
             hipLaunchKernelGGL(moe_stream_q4k_kernel, gs, dim3(kStreamThreads), 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);

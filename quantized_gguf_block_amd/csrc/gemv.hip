@@ -35,10 +35,16 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14 };
 
-// columns per lane: a Q4_K or Q6_K column already spans 64 values
-template <int FMT> constexpr int kCMax = (FMT == T_Q4_K || FMT == T_Q6_K) ? 1 : 2;
+// Q4_K and Q5_K share the super-block header (d, dmin, 6-bit scales and
+// mins) and the nibble chunks; Q5_K adds one high bit per value from qh.
+template <int FMT> constexpr bool kK45 = (FMT == T_Q4_K || FMT == T_Q5_K);
+// super-block formats: a lane column spans 64 values
+template <int FMT> constexpr bool kSuper = kK45<FMT> || FMT == T_Q6_K;
+
+// columns per lane: a super-block column already spans 64 values
+template <int FMT> constexpr int kCMax = kSuper<FMT> ? 1 : 2;
 constexpr int kMaxThreads = 512;    // 8 waves
 
 // bytes per block of the 32-value formats
@@ -75,6 +81,7 @@ template <> struct Act<T_Q4_K> {
     float ndxa, ndxb;       // -12582912 * dx
     float sa, sb;           // dx * sum(q) of each block
 };
+template <> struct Act<T_Q5_K> : Act<T_Q4_K> {};
 
 // Q6_K column (64 values): half h of super-block sb, l in [16 i, 16 i + 16)
 // of each of the four 32-value quadrants g; quadrant g of the half is Q8_0
@@ -162,6 +169,10 @@ __device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col,
     a.ndxa = -kBiasF * a.dxa;
     a.ndxb = -kBiasF * a.dxb;
 }
+template <>
+__device__ __forceinline__ void load_act<T_Q5_K>(const uint8_t* xq_row, int col, Act<T_Q5_K>& a) {
+    load_act<T_Q4_K>(xq_row, col, a);
+}
 
 template <>
 __device__ __forceinline__ void load_act<T_Q6_K>(const uint8_t* xq_row, int col, Act<T_Q6_K>& a) {
@@ -188,6 +199,7 @@ __device__ __forceinline__ void load_act<T_Q6_K>(const uint8_t* xq_row, int col,
 template <int FMT>
 __device__ __forceinline__ int col_offset(int row_base, int col) {
     if constexpr (FMT == T_Q4_K) return row_base + (col >> 2) * 144;
+    else if constexpr (FMT == T_Q5_K) return row_base + (col >> 2) * 176;
     else if constexpr (FMT == T_Q6_K) return row_base + (col >> 2) * 210;
     else return row_base + col * Fmt<FMT>::BS;
 }
@@ -232,6 +244,51 @@ __device__ __forceinline__ void q6k_column_dot(const uint8_t* lds, int off, int 
             const float sx = fmaf(__int_as_float(s), a[j].dx[g], a[j].ndx[g]);
             acc[j] = fmaf(sx, dsc, acc[j]);
         }
+    }
+}
+
+// acc[j] += Q4_K / Q5_K chunk c (sub-blocks 2c, 2c+1) of the super-block
+// whose 16-byte header is hdr, nibbles q[0..7] (Q5_K: the 32 qh bytes
+// qh[0..7], bit j of byte l being bit 4 of value l of sub-block j), batch
+// row j.  Branch-free in c (c differs between the lanes of a wave).
+template <int FMT, int B>
+__device__ __forceinline__ void chunk_dot_k45(const uint32_t* hdr, const uint32_t* qh, const uint32_t* q,
+                                              int c, const Act<FMT>* a, float* acc) {
+    const float d = h2f(hdr[0] & 0xFFFFu), dmin = h2f(hdr[0] >> 16);
+    // scale/min bytes of sub-blocks 2c, 2c+1 as byte pairs (low byte: 2c)
+    const uint32_t sh = 16u * (c & 1);
+    const uint32_t lowsrc = (c < 2) ? hdr[1] : hdr[3];     // S[0..3] or S[8..11]
+    const uint32_t A = lowsrc >> sh, Bm = hdr[2] >> sh, V = hdr[1] >> sh;
+    const uint32_t sc_lo = A & 0x3F3Fu, m_lo = Bm & 0x3F3Fu;                        // c < 2
+    const uint32_t sc_hi = (A & 0x0F0Fu) | ((V >> 2) & 0x3030u);                     // c >= 2
+    const uint32_t m_hi = ((A >> 4) & 0x0F0Fu) | ((Bm >> 2) & 0x3030u);
+    const uint32_t scp = (c < 2) ? sc_lo : sc_hi, mp = (c < 2) ? m_lo : m_hi;
+    const float ds0 = d * static_cast<float>(scp & 0xFFu), ds1 = d * static_cast<float>((scp >> 8) & 0xFFu);
+    const float dm0 = dmin * static_cast<float>(mp & 0xFFu), dm1 = dmin * static_cast<float>((mp >> 8) & 0xFFu);
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        lo[t] = q[t] & 0x0F0F0F0Fu;
+        hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+        if constexpr (FMT == T_Q5_K) {
+            // bits 2c and 2c+1 of each qh byte become bit 4 of the low and
+            // high values
+            const uint32_t u = qh[t] >> (2 * c);
+            lo[t] |= (u << 4) & 0x10101010u;
+            hi[t] |= (u << 3) & 0x10101010u;
+        }
+    }
+    const int bias = bias_sgpr();
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const int sa = dot8<B == 1, true>(lo, a[j].qa, bias);
+        const int sb = dot8<B == 1, true>(hi, a[j].qb, bias);
+        const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
+        const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
+        float v = fmaf(xa, ds0, acc[j]);
+        v = fmaf(-dm0, a[j].sa, v);
+        v = fmaf(xb, ds1, v);
+        acc[j] = fmaf(-dm1, a[j].sb, v);
     }
 }
 
@@ -308,6 +365,17 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
     } else if constexpr (FMT == T_Q6_K) {
         q6k_column_dot<B>(lds, off, col, a, acc);
+    } else if constexpr (FMT == T_Q5_K) {  // chunk c, its 32 qh bytes at off + 16
+        const int c = col & 3;
+        const uint4 h4 = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
+        const uint4 qh0 = *reinterpret_cast<const uint4*>(lds + off + 16);
+        const uint4 qh1 = *reinterpret_cast<const uint4*>(lds + off + 32);
+        const uint4 q0 = *reinterpret_cast<const uint4*>(lds + off + 48 + 32 * c);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(lds + off + 64 + 32 * c);
+        const uint32_t hdr[4] = {h4.x, h4.y, h4.z, h4.w};
+        const uint32_t qh[8] = {qh0.x, qh0.y, qh0.z, qh0.w, qh1.x, qh1.y, qh1.z, qh1.w};
+        const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        chunk_dot_k45<T_Q5_K, B>(hdr, qh, q, c, a, acc);
     } else {  // Q4_K: column = nibble chunk c of super-block at off
         const int c = col & 3;
         const uint4 hdr = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
@@ -553,6 +621,10 @@ template <int C> struct Win<T_Q4_K, C> {
     static constexpr bool kMis = false;
     static constexpr int NDW = 4 + 8 * C;                  // header + C nibble chunks
 };
+template <int C> struct Win<T_Q5_K, C> {
+    static constexpr bool kMis = false;
+    static constexpr int NDW = 12 + 8 * C;                 // header + qh + C nibble chunks
+};
 template <int C> struct Win<T_Q6_K, C> {                 // (reads LDS directly)
     static constexpr bool kMis = false;
     static constexpr int NDW = 1;
@@ -608,49 +680,14 @@ __device__ __forceinline__ void block_dot(const uint32_t* w, const Act<FMT>* a, 
     }
 }
 
-// acc[j] += Q4_K nibble chunk c (sub-blocks 2c, 2c+1) of the super-block
-// whose 16-byte header is hdr, nibbles q[0..7], batch row j.  Branch-free in
-// c (c differs between the lanes of a wave).
-template <int B>
-__device__ __forceinline__ void chunk_dot_q4k(const uint32_t* hdr, const uint32_t* q, int c,
-                                              const Act<T_Q4_K>* a, float* acc) {
-    const float d = h2f(hdr[0] & 0xFFFFu), dmin = h2f(hdr[0] >> 16);
-    // scale/min bytes of sub-blocks 2c, 2c+1 as byte pairs (low byte: 2c)
-    const uint32_t sh = 16u * (c & 1);
-    const uint32_t lowsrc = (c < 2) ? hdr[1] : hdr[3];     // S[0..3] or S[8..11]
-    const uint32_t A = lowsrc >> sh, Bm = hdr[2] >> sh, V = hdr[1] >> sh;
-    const uint32_t sc_lo = A & 0x3F3Fu, m_lo = Bm & 0x3F3Fu;                        // c < 2
-    const uint32_t sc_hi = (A & 0x0F0Fu) | ((V >> 2) & 0x3030u);                     // c >= 2
-    const uint32_t m_hi = ((A >> 4) & 0x0F0Fu) | ((Bm >> 2) & 0x3030u);
-    const uint32_t scp = (c < 2) ? sc_lo : sc_hi, mp = (c < 2) ? m_lo : m_hi;
-    const float ds0 = d * static_cast<float>(scp & 0xFFu), ds1 = d * static_cast<float>((scp >> 8) & 0xFFu);
-    const float dm0 = dmin * static_cast<float>(mp & 0xFFu), dm1 = dmin * static_cast<float>((mp >> 8) & 0xFFu);
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        lo[t] = q[t] & 0x0F0F0F0Fu;
-        hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
-    }
-    const int bias = bias_sgpr();
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-        const int sa = dot8<B == 1, true>(lo, a[j].qa, bias);
-        const int sb = dot8<B == 1, true>(hi, a[j].qb, bias);
-        const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
-        const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
-        float v = fmaf(xa, ds0, acc[j]);
-        v = fmaf(-dm0, a[j].sa, v);
-        v = fmaf(xb, ds1, v);
-        acc[j] = fmaf(-dm1, a[j].sb, v);
-    }
-}
-
 template <int FMT, int B, int C, int I = 0>
 __device__ __forceinline__ void row_dot(const uint32_t* w, const Act<FMT> (*act)[B], int c0,
                                         float* acc) {
     if constexpr (I < C) {
         if constexpr (FMT == T_Q4_K) {
-            chunk_dot_q4k<B>(w, w + 4 + 8 * I, c0 + I, act[I], acc);
+            chunk_dot_k45<T_Q4_K, B>(w, nullptr, w + 4 + 8 * I, c0 + I, act[I], acc);
+        } else if constexpr (FMT == T_Q5_K) {  // header, 32 qh bytes, chunk
+            chunk_dot_k45<T_Q5_K, B>(w, w + 4, w + 12 + 8 * I, c0 + I, act[I], acc);
         } else {
             block_dot<FMT, B, I * Fmt<FMT>::BS>(w, act[I], acc);
         }
@@ -664,6 +701,7 @@ template <bool V> struct Bool { static constexpr bool value = V; };
 // (Q6_K: 210 / 4, rounded up)
 template <int FMT> constexpr int col_bytes() {
     if constexpr (FMT == T_Q4_K) return 36;
+    else if constexpr (FMT == T_Q5_K) return 44;
     else if constexpr (FMT == T_Q6_K) return 53;
     else return Fmt<FMT>::BS;
 }
@@ -672,7 +710,7 @@ constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per 
 
 // Largest activation bytes (all batch rows) one streaming workgroup stages.
 template <int FMT, int B, int C>
-constexpr int kActMax = B * (FMT == T_Q4_K || FMT == T_Q6_K ? 128 : 64) * C * 34;
+constexpr int kActMax = B * (kSuper<FMT> ? 128 : 64) * C * 34;
 
 template <int FMT, int B, int C, int P>
 __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
@@ -688,7 +726,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
     // read consecutive words (no bank conflicts).  A slot is one Q8_0 block
     // (Q6_K: the 16 values of one quadrant that the column covers).
-    constexpr int NS = FMT == T_Q4_K ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
+    constexpr int NS = kK45<FMT> ? 2 : FMT == T_Q6_K ? 4 : 1;      // slots per column
     constexpr int NP = kWave * C;                                  // column positions per row
     constexpr int NBMAX = B * NS * NP;                             // slots, all rows
     constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
@@ -713,11 +751,11 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     const bool valid = C * lane < ncols;
     // byte offsets of this lane's column data within a row
     int off, qoff = 0, c0 = 0;
-    if constexpr (FMT == T_Q4_K) {
+    if constexpr (kK45<FMT>) {
         const int ch = valid ? C * lane : 0;
-        off = (ch >> 2) * 144;
+        off = (ch >> 2) * (FMT == T_Q4_K ? 144 : 176);
         c0 = ch & 3;
-        qoff = off + 16 + 32 * c0;
+        qoff = off + (FMT == T_Q4_K ? 16 : 48) + 32 * c0;
     } else if constexpr (FMT == T_Q6_K) {
         c0 = valid ? C * lane : 0;               // the column
         off = (c0 >> 2) * 210;
@@ -828,8 +866,8 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     a.ndx[g] = -kBiasF * a.dx[g];
                     a.start[g] = kBias - 32 * __float_as_int(xau[gi]);
                 }
-            } else if constexpr (FMT == T_Q4_K) {
-                Act<T_Q4_K>& a = act[i][j];
+            } else if constexpr (kK45<FMT>) {
+                Act<FMT>& a = act[i][j];
                 const int ga = 2 * j * NP + lane, gb = ga + NP;
                 const u32x4 a0 = xq0[ga], a1 = xq1[ga], b0 = xq0[gb], b1 = xq1[gb];
                 a.qa[0] = a0.x; a.qa[1] = a0.y; a.qa[2] = a0.z; a.qa[3] = a0.w;
@@ -892,13 +930,19 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             if constexpr (FMT == T_Q6_K) {
                 static_assert(C == 1, "one Q6_K column per lane");
                 q6k_column_dot<B>(stage, off, c0, act[0], acc[i]);
-            } else if constexpr (FMT == T_Q4_K) {
-                const uint4 h = *reinterpret_cast<const uint4*>(stage + off);
-                v[0] = h.x; v[1] = h.y; v[2] = h.z; v[3] = h.w;
+            } else if constexpr (kK45<FMT>) {
+                // header (and Q5_K's 32 qh bytes), then the C nibble chunks
+                constexpr int NH = FMT == T_Q4_K ? 1 : 3;
+#pragma unroll
+                for (int t = 0; t < NH; ++t) {
+                    const uint4 h = *reinterpret_cast<const uint4*>(stage + off + 16 * t);
+                    v[4 * t] = h.x; v[4 * t + 1] = h.y; v[4 * t + 2] = h.z; v[4 * t + 3] = h.w;
+                }
 #pragma unroll
                 for (int t = 0; t < 2 * C; ++t) {
                     const uint4 q = *reinterpret_cast<const uint4*>(stage + qoff + 16 * t);
-                    v[4 + 4 * t] = q.x; v[5 + 4 * t] = q.y; v[6 + 4 * t] = q.z; v[7 + 4 * t] = q.w;
+                    v[4 * NH + 4 * t] = q.x; v[4 * NH + 1 + 4 * t] = q.y;
+                    v[4 * NH + 2 + 4 * t] = q.z; v[4 * NH + 3 + 4 * t] = q.w;
                 }
             } else {
 #pragma unroll
@@ -936,8 +980,9 @@ constexpr int kRing = 4;  // rows in flight per wave in the streaming kernel
 Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     const int64_t xrb = k / 32 * 34;
     Plan p{};
-    p.ncols = static_cast<int>(wt == T_Q4_K || wt == T_Q6_K ? k / 64 : k / 32);
-    p.C = (wt == T_Q4_K || wt == T_Q6_K || p.ncols <= kWave) ? 1 : 2;
+    const bool super = wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K;
+    p.ncols = static_cast<int>(super ? k / 64 : k / 32);
+    p.C = (super || p.ncols <= kWave) ? 1 : 2;
     p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
     // general kernel: about 16 KiB of weights per tile, at most 32 live
     // accumulators per lane
@@ -953,7 +998,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     // one (type, k) must take the same kernel)
     const int sc = (p.ncols + kWave - 1) / kWave;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !((wt == T_Q4_K || wt == T_Q6_K) && sc == 2))
+        !(super && sc == 2))
         p.SC = sc;
     return p;
 }
@@ -989,7 +1034,7 @@ template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
     if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
-    if constexpr (FMT != T_Q4_K && FMT != T_Q6_K)  // (one column per lane for these)
+    if constexpr (!kSuper<FMT>)  // (one column per lane for the super-block formats)
         if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
@@ -1031,9 +1076,10 @@ int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb
 }
 
 int64_t block_bytes_of(int wt) {
-    return wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 210;
+    return wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144
+           : wt == T_Q5_K ? 176 : 210;
 }
-int64_t block_elems_of(int wt) { return wt == T_Q4_K || wt == T_Q6_K ? 256 : 32; }
+int64_t block_elems_of(int wt) { return wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : 32; }
 
 }  // namespace
 
@@ -1064,6 +1110,7 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_1: return launch_fmt<T_Q4_1>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q8_0: return launch_fmt<T_Q8_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q4_K: return launch_fmt<T_Q4_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q5_K: return launch_fmt<T_Q5_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q6_K: return launch_fmt<T_Q6_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         default: return -2;
     }

@@ -43,8 +43,9 @@ def test_version_and_status_strings(lib):
 
 
 def test_block_geometry(lib):
-    assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12, 14)] == [32, 32, 32, 256, 256]
-    assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12, 14)] == [18, 20, 34, 144, 210]
+    assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12, 13, 14)] == [32, 32, 32, 256, 256, 256]
+    assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12, 13, 14)] == [18, 20, 34, 144, 176, 210]
+    assert lib.cq_row_bytes(13, 4096) == 2816
     assert lib.cq_row_bytes(14, 4096) == 3360
     assert lib.cq_row_bytes(12, 4096) == 2304
     assert lib.cq_row_bytes(8, 4096) == 4352
@@ -72,6 +73,7 @@ def test_gemv_validation(lib):
     assert f(7, P(FAKE), 8, 256, P(FAKE), 1, P(FAKE), 8, None) == UNSUPPORTED
     assert f(12, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q4_K needs 256
     assert f(14, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q6_K needs 256
+    assert f(13, P(FAKE), 8, 288, P(FAKE), 1, P(FAKE), 8, None) == SHAPE   # Q5_K needs 256
     assert f(2, P(FAKE), 8, 48, P(FAKE), 1, P(FAKE), 8, None) == SHAPE
     assert f(2, P(FAKE), 8, 256, P(FAKE), 0, P(FAKE), 8, None) == INVALID  # batch 0
     assert f(2, P(FAKE), 8, 256, P(FAKE), 9, P(FAKE), 8, None) == INVALID  # batch 9

@@ -11,7 +11,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
@@ -42,13 +42,14 @@ def test_gemm_prefill_512_full(cq, orc):
     print(f"prefill 512: max |err|/S = {r:.3e}")
 
 
-def test_gemm_prefill_2048_sampled(cq, orc):
-    c = gs.CONFIGS["q4_0_gemm_prefill_2048"]
+@pytest.mark.parametrize("name", ["q4_0_gemm_prefill_2048", "q5_k_gemm_prefill_512"])
+def test_gemm_prefill_sampled(cq, orc, name):
+    c = gs.CONFIGS[name]
     n, k, m = c["n"], c["k"], c["m"]
     w = gs.weights(c["fmt"], n, k, cfg=c["cfg"])
     x = gs.activations(m, k, cfg=c["cfg"])
     xq = orc.quantize_q8_0(x)
-    note("gemm prefill 2048")
+    note("gemm prefill sampled", name)
     y = to_host(cq.cq_gemm(c["fmt"], to_dev(w), n, k, to_dev(xq), m))
     rng = np.random.default_rng(12)
     # every output of the first and last 128 x 128 tiles, plus random ones
@@ -57,7 +58,7 @@ def test_gemm_prefill_2048_sampled(cq, orc):
     ni = np.concatenate([np.tile([0, 63, 64, 127], 128), np.tile([n - 128, n - 65, n - 64, n - 1], 128),
                          rng.integers(0, n, 6000)])
     y_ref, s_ref = orc.matmul_sampled(c["fmt"], w, n, k, xq, m, mi, ni)
-    assert_close_to_oracle(y[mi, ni], y_ref, s_ref, what="prefill 2048 sampled")
+    assert_close_to_oracle(y[mi, ni], y_ref, s_ref, what=f"{name} sampled")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
@@ -72,7 +73,7 @@ def test_gemm_invariants(cq, orc, fmt):
     assert np.array_equal(y0, y1)
     # doubling every weight scale doubles y bitwise
     w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[fmt])
-    nf = 2 if fmt in (gs.Q4_1, gs.Q4_K) else 1
+    nf = 2 if fmt in (gs.Q4_1, gs.Q4_K, gs.Q5_K) else 1
     for f in range(nf):
         h = w2[:, 2 * f:2 * f + 2].copy().view(np.float16)
         w2[:, 2 * f:2 * f + 2] = (h * np.float16(2)).view(np.uint8)

@@ -13,7 +13,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q6_K]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K]
 
 
 def run_gemv(cq, fmt, w, n, k, xq, batch):
@@ -44,7 +44,8 @@ def config_inputs(name):
     return c, w, x
 
 
-@pytest.mark.parametrize("name", ["q4_0_gemv_2048", "q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up"])
+@pytest.mark.parametrize("name", ["q4_0_gemv_2048", "q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up",
+                                  "q5_k_gemv_ffn_up"])
 def test_gemv_config_full(cq, orc, name):
     c, w, x = config_inputs(name)
     xq = orc.quantize_q8_0(x)
@@ -116,7 +117,7 @@ def test_gemv_deterministic_and_scaling(cq, orc, fmt):
     assert np.array_equal(y0, y1)
     # doubling every weight scale (d, and m or dmin) doubles y bitwise
     w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[fmt])
-    offs = [208] if fmt == gs.Q6_K else [0, 2] if fmt in (gs.Q4_1, gs.Q4_K) else [0]
+    offs = [208] if fmt == gs.Q6_K else [0, 2] if fmt in (gs.Q4_1, gs.Q4_K, gs.Q5_K) else [0]
     for o in offs:
         h = w2[:, o:o + 2].copy().view(np.float16)
         w2[:, o:o + 2] = (h * np.float16(2)).view(np.uint8)
