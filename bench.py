@@ -238,9 +238,9 @@ def secondary(cq, gs, dev, stream):
     """The other workloads, each timed as a burst of back-to-back launches
     (weights rotated through >= 512 MB of copies where they would fit the
     Infinity Cache): the 128K-vocabulary LM head (Q4_K, and Q6_K as for a
-    tied embedding) at batch 1 and 4, the
-    2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens, and
-    the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
+    tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
+    the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
+    the Q5_K prefill GEMM at 512 tokens, and the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
     import torch
     out = {}
@@ -263,6 +263,18 @@ def secondary(cq, gs, dev, stream):
                 "us": round(us, 2), "GB/s": round(gbs, 1),
                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
         del wl
+    # Q5_K FFN-up GEMV 14336 x 4096 (the FFN type of Q5_K_M models)
+    n, k = 14336, 4096
+    c5 = gs.CONFIGS["q5_k_gemv_ffn_up"]
+    w5 = copies(gs.weights(gs.Q5_K, n, k, cfg=c5["cfg"]))
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(5, k, cfg=c5["cfg"])).to(dev))
+    y = torch.empty((5, n), dtype=torch.float32, device=dev)
+    for b in (1, 5):
+        us = _burst_us(lambda i: cq.cq_gemv(gs.Q5_K, w5[i % len(w5)], n, k, xq, b, y=y), 100, stream)
+        gbs = w5[0].numel() / us / 1e3
+        out[f"q5_k_gemv_14336x4096_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    del w5
     # 2048 x 2048 Q4_0 GEMV (2.36 MB per call: launch-latency bound)
     n, k = 2048, 2048
     w0 = copies(gs.weights(gs.Q4_0, n, k, cfg=0))
@@ -283,6 +295,16 @@ def secondary(cq, gs, dev, stream):
         tops = 2 * m * n * k / us / 1e6
         out[f"q4_0_gemm_{m}x14336x4096"] = {"us": round(us, 2), "TOPS": round(tops, 1),
                                             "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
+    del wg
+    c5 = gs.CONFIGS["q5_k_gemm_prefill_512"]
+    wg = torch.from_numpy(gs.weights(gs.Q5_K, n, k, cfg=c5["cfg"])).to(dev)
+    m = c5["m"]
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c5["cfg"])).to(dev))
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    us = _burst_us(lambda i: cq.cq_gemm(gs.Q5_K, wg, n, k, xq, m, y=y), 20, stream)
+    tops = 2 * m * n * k / us / 1e6
+    out[f"q5_k_gemm_{m}x14336x4096"] = {"us": round(us, 2), "TOPS": round(tops, 1),
+                                        "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
     del wg
     # routed FFN
     c = gs.CONFIGS["q4_k_moe_ffn"]
