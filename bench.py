@@ -240,7 +240,7 @@ def secondary(cq, gs, dev, stream):
     Infinity Cache): the 128K-vocabulary LM head (Q4_K, and Q6_K as for a
     tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
     the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
-    the Q5_K prefill GEMM at 512 tokens, and the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
+    the Q5_K and Q6_K prefill GEMMs at 512 tokens, and the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
     import torch
     out = {}
@@ -296,16 +296,18 @@ def secondary(cq, gs, dev, stream):
         out[f"q4_0_gemm_{m}x14336x4096"] = {"us": round(us, 2), "TOPS": round(tops, 1),
                                             "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
     del wg
-    c5 = gs.CONFIGS["q5_k_gemm_prefill_512"]
-    wg = torch.from_numpy(gs.weights(gs.Q5_K, n, k, cfg=c5["cfg"])).to(dev)
-    m = c5["m"]
-    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c5["cfg"])).to(dev))
-    y = torch.empty((m, n), dtype=torch.float32, device=dev)
-    us = _burst_us(lambda i: cq.cq_gemm(gs.Q5_K, wg, n, k, xq, m, y=y), 20, stream)
-    tops = 2 * m * n * k / us / 1e6
-    out[f"q5_k_gemm_{m}x14336x4096"] = {"us": round(us, 2), "TOPS": round(tops, 1),
-                                        "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
-    del wg
+    for fmt, name in ((gs.Q5_K, "q5_k_gemm_prefill_512"), (gs.Q6_K, "q6_k_gemm_prefill_512")):
+        c5 = gs.CONFIGS[name]
+        wg = torch.from_numpy(gs.weights(fmt, n, k, cfg=c5["cfg"])).to(dev)
+        m = c5["m"]
+        xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c5["cfg"])).to(dev))
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        us = _burst_us(lambda i: cq.cq_gemm(fmt, wg, n, k, xq, m, y=y), 20, stream)
+        tops = 2 * m * n * k / us / 1e6
+        out[f"{gs.NAMES[fmt]}_gemm_{m}x14336x4096"] = {
+            "us": round(us, 2), "TOPS": round(tops, 1),
+            "pct_int8_mfma_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2)}
+        del wg
     # routed FFN
     c = gs.CONFIGS["q4_k_moe_ffn"]
     T, H, F, E, K = c["n_tokens"], c["hidden"], c["ffn"], c["n_experts"], c["top_k"]

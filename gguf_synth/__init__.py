@@ -111,11 +111,14 @@ CONFIGS = {
     "q8_0_gemv_ffn_up": dict(cfg=1, kind="gemv", fmt=Q8_0, n=14336, k=4096, batches=(1, 5)),
     "q4_1_gemv_ffn_up": dict(cfg=11, kind="gemv", fmt=Q4_1, n=14336, k=4096, batches=(1, 5)),
     "q4_k_gemv_lm_head": dict(cfg=2, kind="gemv", fmt=Q4_K, n=128256, k=4096, batches=(1, 4)),
-    # the tied-embedding LM head in Q6_K (a "next" type: GEMV only)
+    # the tied-embedding LM head in Q6_K
     "q6_k_gemv_lm_head": dict(cfg=22, kind="gemv", fmt=Q6_K, n=128256, k=4096, batches=(1, 4)),
     # Q5_K (the FFN type of Q5_K_M models): decode GEMV and prefill GEMM
     "q5_k_gemv_ffn_up": dict(cfg=15, kind="gemv", fmt=Q5_K, n=14336, k=4096, batches=(1, 5)),
     "q5_k_gemm_prefill_512": dict(cfg=25, kind="gemm", fmt=Q5_K, n=14336, k=4096, m=512),
+    # Q6_K prefill GEMM (Q6_K holds the FFN-down and embedding tensors of
+    # Q4_K_M models)
+    "q6_k_gemm_prefill_512": dict(cfg=26, kind="gemm", fmt=Q6_K, n=14336, k=4096, m=512),
     "q4_0_gemm_prefill_512": dict(cfg=3, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=512),
     "q4_0_gemm_prefill_2048": dict(cfg=13, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=2048),
     "q4_k_moe_ffn": dict(cfg=4, kind="moe", fmt=Q4_K, n_tokens=256, hidden=2048, ffn=1536,

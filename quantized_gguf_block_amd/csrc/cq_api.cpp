@@ -16,7 +16,7 @@
 namespace cq {
 
 int gemv_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
-int gemm_shape_ok(int wt, int64_t k);                  // gemm.hip
+int gemm_shape_ok(int wt, int64_t n, int64_t k);       // gemm.hip
 int moe_shape_ok(int wt, int64_t n, int64_t k);        // moe.hip
 
 namespace {
@@ -89,7 +89,7 @@ const char* cq_status_string(int status) {
     switch (status) {
         case CQ_OK: return "CQ_OK";
         case CQ_ERR_INVALID_ARG: return "CQ_ERR_INVALID_ARG: null pointer, negative size or bad flag";
-        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K everywhere; Q6_K in cq_gemv)";
+        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K)";
         case CQ_ERR_SHAPE: return "CQ_ERR_SHAPE: k is not a whole number of blocks or exceeds the kernel's limit";
         case CQ_ERR_ALIGNMENT: return "CQ_ERR_ALIGNMENT: pointer or leading dimension misaligned";
         case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE";
@@ -131,10 +131,9 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t
 
 int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,
             int64_t ldy, cq_stream_t stream) {
-    if (wt == CQ_Q6_K) return CQ_ERR_UNSUPPORTED_TYPE;
     if (int rc = check_weights(wt, w, n, k)) return rc;
     if (m < 0 || ldy < n) return CQ_ERR_INVALID_ARG;
-    if (k % 256 != 0 || gemm_shape_ok(wt, k) != 0) return CQ_ERR_SHAPE;
+    if (k % 256 != 0 || gemm_shape_ok(wt, n, k) != 0) return CQ_ERR_SHAPE;
     if (n == 0 || m == 0) return CQ_OK;
     if (!xq || !y) return CQ_ERR_INVALID_ARG;
     if (!aligned(xq, 4) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
@@ -158,7 +157,6 @@ int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, int
 int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                 const void* xq, int x_per_pair, const int32_t* offsets, const int32_t* pairs,
                 int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, cq_stream_t stream) {
-    if (wt == CQ_Q6_K) return CQ_ERR_UNSUPPORTED_TYPE;
     if (int rc = check_weights(wt, w_experts, n, k)) return rc;
     if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || ldy < n ||
         (x_per_pair != 0 && x_per_pair != 1))

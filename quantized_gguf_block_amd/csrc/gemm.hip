@@ -33,7 +33,7 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14 };
 
 // Q4_K and Q5_K share the super-block header and nibble chunks (Q5_K adds a
 // high bit per value from qh[32])
@@ -65,7 +65,8 @@ template <int BM, int BN>
 struct Smem {
     int8_t w[BN * ROW];       // decoded weight quants, row n, k within the step
     int8_t x[BM * ROW];       // activation quants
-    float dw[KB][BN];         // weight block scale (Q4_K: d*sc)
+    float dw[KB][BN];         // weight block scale (Q4_K: d*sc; Q6_K: d*sc of values 0..15)
+    float dw2[KB][BN];        // Q6_K: d*sc of values 16..31
     float dx[KB][BM];         // activation block scale
     float cw[KB][BN];         // Q4_1: m; Q4_K: -dmin*min  (additive weight term)
     float sx[KB][BM];         // dx * sum of the block's activation quants
@@ -119,6 +120,12 @@ template <> struct WRaw<T_Q4_K> {     // super-block header + one 32-byte chunk
 template <> struct WRaw<T_Q5_K> {     // header, the 32 qh bytes, one 32-byte chunk
     uint32_t hdr[4], qh[8], q[8];
 };
+template <> struct WRaw<T_Q6_K> {     // one 32-byte ql run and the qh bytes of a half
+    uint32_t ql[9], qh[9];            // dword-aligned covers (see load_weights)
+    uint32_t sc0, sc1;                // scale byte pairs of the two quadrants
+    uint32_t d;                       // fp16 d
+    uint32_t sh;                      // 16 when the runs start 2 bytes into a dword
+};
 struct XRaw {                         // two Q8_0 activation blocks
     uint32_t v[17];
 };
@@ -128,7 +135,32 @@ __device__ __forceinline__ void load_weights(WRaw<FMT>& r, const uint8_t* __rest
                                              int64_t rb, int64_t n0, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
     const int64_t gn = n0 + row < n ? n0 + row : n - 1;
-    if constexpr (kK45<FMT>) {
+    if constexpr (FMT == T_Q6_K) {
+        // A k step is one 128-value half h of super-block sb; this thread
+        // decodes quadrants g = half and half + 2 of it, which share the ql
+        // run [64h + 32*half, +32) (low and high nibbles).  Super-blocks are
+        // 210 bytes, so the runs may start 2 bytes into a dword: the dwords
+        // covering them are loaded through a buffer descriptor over the
+        // matrix (reads past it return zeros) and re-aligned when stored.
+        const int h = kstep & 1;
+        const uintptr_t wa = reinterpret_cast<uintptr_t>(w);
+        const uint8_t* wal = reinterpret_cast<const uint8_t*>(wa & ~static_cast<uintptr_t>(3));
+        const int delta = static_cast<int>(wa & 3);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(wal), 0, static_cast<int>(delta + n * rb), 0x00020000);
+        const int base = delta + static_cast<int>(gn * rb) + (kstep >> 1) * 210;
+        const int mis = base & 2;
+        r.sh = static_cast<uint32_t>(mis) * 8;
+        const int aql = base + 64 * h + 32 * half - mis, aqh = base + 128 + 32 * h - mis;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            r.ql[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, aql + 4 * i, 0, 0);
+            r.qh[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, aqh + 4 * i, 0, 0);
+        }
+        r.sc0 = __builtin_amdgcn_raw_buffer_load_b16(rs, base + 192 + 8 * h + 2 * half, 0, 0);
+        r.sc1 = __builtin_amdgcn_raw_buffer_load_b16(rs, base + 196 + 8 * h + 2 * half, 0, 0);
+        r.d = __builtin_amdgcn_raw_buffer_load_b16(rs, base + 208, 0, 0);
+    } else if constexpr (kK45<FMT>) {
         // a 256-value super-block spans two k steps; this step holds nibble
         // chunks 2*(kstep&1) and +1, this thread chunk c (sub-blocks 2c, 2c+1)
         constexpr int SB = FMT == T_Q4_K ? 144 : 176, QS = FMT == T_Q4_K ? 16 : 48;
@@ -158,7 +190,32 @@ __device__ __forceinline__ void load_weights(WRaw<FMT>& r, const uint8_t* __rest
 template <int FMT, class S>
 __device__ __forceinline__ void store_weights(S& s, const WRaw<FMT>& r, int kstep) {
     const int t = threadIdx.x, row = t >> 1, half = t & 1;
-    if constexpr (kK45<FMT>) {
+    if constexpr (FMT == T_Q6_K) {
+        const float d = h2f(r.d);
+        uint32_t ql[8], qh[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ql[i] = __builtin_amdgcn_alignbit(r.ql[i + 1], r.ql[i], r.sh);
+            qh[i] = __builtin_amdgcn_alignbit(r.qh[i + 1], r.qh[i], r.sh);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int g = half + 2 * e;       // quadrant = local block of the step
+            const uint32_t scp = e ? r.sc1 : r.sc0;  // signed scales of values 0..15, 16..31
+            s.dw[g][row] = d * static_cast<float>(static_cast<int8_t>(scp & 0xFFu));
+            s.dw2[g][row] = d * static_cast<float>(static_cast<int8_t>((scp >> 8) & 0xFFu));
+            uint32_t o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t nib = e ? (ql[i] >> 4) & 0x0F0F0F0Fu : ql[i] & 0x0F0F0F0Fu;
+                const uint32_t v = nib | (((qh[i] >> (2 * g)) & 0x03030303u) << 4);   // 0..63
+                o[i] = (v + 0x60606060u) ^ 0x80808080u;   // v - 32 per byte, no carries
+            }
+            uint4* d4 = reinterpret_cast<uint4*>(s.w + row * ROW + 32 * g);
+            d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    } else if constexpr (kK45<FMT>) {
         const int c = 2 * (kstep & 1) + half;
         const float d = h2f(r.hdr[0] & 0xFFFFu), dmin = h2f(r.hdr[0] >> 16);
         const uint32_t S0 = r.hdr[1], S1 = r.hdr[2], S2 = r.hdr[3];
@@ -310,7 +367,42 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
                 dx[mi] = s.dx[b][(wm * MI + mi) * 32 + l32];
                 ndx[mi] = -kBiasF * dx[mi];
             }
-            if constexpr (kAllLive) {
+            if constexpr (FMT == T_Q6_K) {
+                // 16-value scale groups: one v_mfma_i32_32x32x16_i8 per
+                // half block, each rescaled with its own d*sc
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    long A2[NI], B2[MI];
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni)
+                        A2[ni] = *reinterpret_cast<const long*>(
+                            s.w + ((wn * NI + ni) * 32 + l32) * ROW + 32 * b + 16 * hh + 8 * h);
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        B2[mi] = *reinterpret_cast<const long*>(
+                            s.x + ((wm * MI + mi) * 32 + l32) * ROW + 32 * b + 16 * hh + 8 * h);
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) {
+                        float dwv[16];
+                        const float* dsrc = hh ? &s.dw2[b][0] : &s.dw[b][0];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 d4 = *reinterpret_cast<const float4*>(dsrc + (wn * NI + ni) * 32 + 8 * q + 4 * h);
+                            dwv[4 * q] = d4.x; dwv[4 * q + 1] = d4.y; dwv[4 * q + 2] = d4.z; dwv[4 * q + 3] = d4.w;
+                        }
+#pragma unroll
+                        for (int mi = 0; mi < MI; ++mi) {
+                            if (!kAllLive && mi >= mi_live) break;
+                            const v16i D = __builtin_amdgcn_mfma_i32_32x32x16_i8(A2[ni], B2[mi], bias, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const float tq = fmaf(__int_as_float(D[r]), dx[mi], ndx[mi]);
+                                acc[mi][ni][r] = fmaf(tq, dwv[r], acc[mi][ni][r]);
+                            }
+                        }
+                    }
+                }
+            } else if constexpr (kAllLive) {
                 // every (ni, mi) tile is live: the MFMA of the next tile is
                 // issued before the rescale of the current one, so the
                 // rescale does not wait for the MFMA it follows
@@ -732,16 +824,23 @@ __global__ __launch_bounds__(kStreamThreads, 3) void moe_stream_q4k_kernel(
 
 }  // namespace
 
-int gemm_shape_ok(int wt, int64_t k) {
-    (void)wt;
-    return (k % 256 == 0) ? 0 : -3;
+// Q6_K weights are read through one buffer descriptor per matrix (expert),
+// with 31-bit byte offsets
+static bool q6k_range_ok(int wt, int64_t n, int64_t k) {
+    return wt != T_Q6_K || n * (k / 256) * 210 + 4 <= 0x7FFFFFFFll;
+}
+
+int gemm_shape_ok(int wt, int64_t n, int64_t k) {
+    return (k % 256 == 0 && q6k_range_ok(wt, n, k)) ? 0 : -3;
 }
 
 int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,
                 int64_t ldy, hipStream_t stream) {
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 176;
-    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K ? 256 : 32;
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144
+                       : wt == T_Q5_K ? 176 : 210;
+    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
+    if (!q6k_range_ok(wt, n, k)) return -3;
     const int64_t tiles_m = (m + 127) / 128, tiles_n = (n + 127) / 128;
     const int64_t tiles = tiles_m * tiles_n;
     if (tiles > 0x7FFFFFFF) return -3;
@@ -755,24 +854,25 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q8_0: hipLaunchKernelGGL(gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q4_K: hipLaunchKernelGGL(gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q5_K: hipLaunchKernelGGL(gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
+        case T_Q6_K: hipLaunchKernelGGL(gemm_kernel<T_Q6_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         default: return -2;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 int moe_shape_ok(int wt, int64_t n, int64_t k) {
-    (void)wt;
-    (void)n;
-    return (k % 256 == 0) ? 0 : -3;
+    return (k % 256 == 0 && q6k_range_ok(wt, n, k)) ? 0 : -3;
 }
 
 int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
                     const void* xq, int x_per_pair, const int32_t* offsets,
                     const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
                     int64_t ldy, hipStream_t stream) {
-    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144 : 176;
-    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K ? 256 : 32;
+    const int64_t bs = wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144
+                       : wt == T_Q5_K ? 176 : 210;
+    const int64_t qk = wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : 32;
     const int64_t rb = k / qk * bs;
+    if (!q6k_range_ok(wt, n, k)) return -3;
     const int64_t tiles_n = (n + 127) / 128;
     const int64_t np = n_tokens * top_k;
     if (tiles_n > 0x7FFFFFFF || np > 0x7FFFFFFF) return -3;
@@ -785,6 +885,7 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
         case T_Q4_1: hipLaunchKernelGGL(moe_gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q8_0: hipLaunchKernelGGL(moe_gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q5_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
+        case T_Q6_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q6_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q4_K: {
             const dim3 gs(static_cast<unsigned>((n + kSbRows - 1) / kSbRows), static_cast<unsigned>(n_experts));
             hipLaunchKernelGGL(moe_stream_q4k_kernel, gs, dim3(kStreamThreads), 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);

@@ -92,7 +92,9 @@ def test_gemm_validation(lib):
     assert f(2, P(FAKE), 8, 256, P(FAKE), -1, P(FAKE), 8, None) == INVALID
     assert f(2, P(FAKE), 8, 256, None, 0, None, 8, None) == OK             # m == 0
     assert f(5, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
-    assert f(14, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED  # Q6_K: GEMV only
+    assert f(7, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
+    # Q6_K rows are read with 31-bit offsets: a matrix of 2 GiB or more is refused
+    assert f(14, P(FAKE), 1 << 20, 2560, P(FAKE), 4, P(FAKE), 1 << 20, None) == SHAPE
 
 
 def test_moe_validation(lib):
@@ -108,8 +110,10 @@ def test_moe_validation(lib):
              None) == SHAPE
     assert m(12, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 0, 4, P(FAKE), 64,
              None) == OK                                                     # no tokens
-    assert m(14, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
-             None) == UNSUPPORTED                                            # Q6_K: GEMV only
+    assert m(7, P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
+             None) == UNSUPPORTED
+    assert m(14, P(FAKE), 2, 1 << 20, 2560, P(FAKE), 0, P(FAKE), P(FAKE), 4, 2, P(FAKE),
+             1 << 20, None) == SHAPE                                         # Q6_K expert >= 2 GiB
     s = lib.cq_swiglu_quantize_q8_0
     assert s(P(FAKE), P(FAKE), 64, 2, 48, None, P(FAKE), None) == SHAPE
     assert s(P(FAKE), P(FAKE + 4), 64, 2, 64, None, P(FAKE), None) == ALIGN

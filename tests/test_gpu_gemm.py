@@ -11,7 +11,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
@@ -42,7 +42,8 @@ def test_gemm_prefill_512_full(cq, orc):
     print(f"prefill 512: max |err|/S = {r:.3e}")
 
 
-@pytest.mark.parametrize("name", ["q4_0_gemm_prefill_2048", "q5_k_gemm_prefill_512"])
+@pytest.mark.parametrize("name", ["q4_0_gemm_prefill_2048", "q5_k_gemm_prefill_512",
+                                  "q6_k_gemm_prefill_512"])
 def test_gemm_prefill_sampled(cq, orc, name):
     c = gs.CONFIGS[name]
     n, k, m = c["n"], c["k"], c["m"]
@@ -73,10 +74,10 @@ def test_gemm_invariants(cq, orc, fmt):
     assert np.array_equal(y0, y1)
     # doubling every weight scale doubles y bitwise
     w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[fmt])
-    nf = 2 if fmt in (gs.Q4_1, gs.Q4_K, gs.Q5_K) else 1
-    for f in range(nf):
-        h = w2[:, 2 * f:2 * f + 2].copy().view(np.float16)
-        w2[:, 2 * f:2 * f + 2] = (h * np.float16(2)).view(np.uint8)
+    offs = [208] if fmt == gs.Q6_K else [0, 2] if fmt in (gs.Q4_1, gs.Q4_K, gs.Q5_K) else [0]
+    for o in offs:
+        h = w2[:, o:o + 2].copy().view(np.float16)
+        w2[:, o:o + 2] = (h * np.float16(2)).view(np.uint8)
     y2 = to_host(cq.cq_gemm(fmt, to_dev(w2.reshape(n, -1)), n, k, xd, m))
     assert np.array_equal(y2, 2 * y0)
     # a GEMM row agrees with the GEMV on that row (both within tolerance of

@@ -172,7 +172,7 @@ def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
         assert_close_to_oracle(y, y_ref, s_ref, what="moe shape")
 
 
-@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q5_K], ids=lambda f: gs.NAMES[f])
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q5_K, gs.Q6_K], ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(40, 6, 2, 200, 512), (130, 3, 3, 70, 256)])
 def test_moe_gemm_other_formats(cq, orc, fmt, n_tokens, n_experts, top_k, n, k):
     """Grouped GEMM over the 32-value formats (the dense tile engine over
