@@ -5,11 +5,10 @@
  * What is computed (pages cited by title and section):
  *   - Weights stay in GGUF block form as stored: Q4_0, Q4_1, Q8_0, Q4_K
  *     (Cera README, "Quantization"; alice-llm 2.0.0 README, "Quantization
- *     Block Specs"), Q5_K (same table; Cera README, "Quantization"), and
- *     for the decode GEMV also Q6_K, the type of the tied-embedding LM head
- *     (same table; Cera README, "Performance").  The LM head runs on the
- *     weight as stored, not on a dequantized copy (Cera README,
- *     "Performance").
+ *     Block Specs"), Q5_K and Q6_K (same table; Cera README, "Quantization";
+ *     Q6_K is the type of the tied-embedding LM head, Cera README,
+ *     "Performance").  The LM head runs on the weight as stored, not on a
+ *     dequantized copy (Cera README, "Performance").
  *   - Activations are quantized on the fly to Q8_0 blocks of 32 (Cera
  *     README, "Quantization"; alice-llm 2.0.0 README, "The CPU Optimization
  *     Journey", Phase 4).
@@ -145,9 +144,9 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  *     y[r*ldy + i] = sum_j w_hat[i][j] * x_hat[r][j]
  * computed as int8 MFMA products of each 32-value block with the two block
  * scales applied per block in fp32.
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K (CQ_Q6_K returns
- *          CQ_ERR_UNSUPPORTED_TYPE: its 16-value scale groups do not fit the
- *          32-value MFMA block step).
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K (Q6_K:
+ *          one K = 16 MFMA step per 16-value scale group; its weight matrix
+ *          must be under 2 GiB, else CQ_ERR_SHAPE).
  *   w      [n][k/qk] blocks, 16-byte aligned; xq [m][k/32] Q8_0 blocks,
  *          4-byte aligned; y fp32 [m][ldy], ldy >= n, 4-byte aligned.
  *   k      multiple of 256, k <= CQ_MAX_K.
@@ -182,8 +181,8 @@ int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
  * where row = p / top_k (x_per_pair = 0: gate/up read the token row) or
  * row = p (x_per_pair = 1: down reads the pair row).  Each expert's weight
  * matrix is streamed once for all of its pairs.
- *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K (CQ_Q6_K: as
- *              cq_gemm).
+ *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K (Q6_K:
+ *              each expert's matrix under 2 GiB, else CQ_ERR_SHAPE).
  *   w_experts  n_experts matrices [n][k/qk], back to back, 16-B aligned.
  *   xq         Q8_0 rows of k/32 blocks (n_tokens or n_tokens*top_k rows).
  *   offsets, pairs  as written by cq_moe_group.
