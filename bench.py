@@ -239,6 +239,7 @@ def secondary(cq, gs, dev, stream):
     (weights rotated through >= 512 MB of copies where they would fit the
     Infinity Cache): the 128K-vocabulary LM head (Q4_K, and Q6_K as for a
     tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
+    the fused Q4_K gate/up/SwiGLU GEMV against the separate kernels,
     the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
     the Q5_K and Q6_K prefill GEMMs at 512 tokens, and the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
@@ -275,6 +276,34 @@ def secondary(cq, gs, dev, stream):
         out[f"q5_k_gemv_14336x4096_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                                              "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
     del w5
+    # decode FFN front half, Q4_K gate/up 14336 x 4096: fused gate + up +
+    # SwiGLU GEMV then the Q8_0 of h, against two GEMVs and the SwiGLU +
+    # requantization kernel (both produce the down GEMV's input)
+    wgt = copies(gs.weights(gs.Q4_K, n, k, cfg=810, tensor=0), 256 * 2**20)
+    wup = copies(gs.weights(gs.Q4_K, n, k, cfg=810, tensor=1), 256 * 2**20)
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(5, k, cfg=810)).to(dev))
+    g = torch.empty((5, n), dtype=torch.float32, device=dev)
+    u = torch.empty_like(g)
+    h = torch.empty_like(g)
+    hq = torch.empty((5, n // 32 * 34), dtype=torch.uint8, device=dev)
+    for b in (1, 5):
+        def fused(i, b=b):
+            cq.cq_gemv_swiglu(gs.Q4_K, wgt[i % len(wgt)], wup[i % len(wup)], n, k, xq, b, h=h)
+            cq.cq_quantize_q8_0(h[:b], hq[:b])
+
+        def separate(i, b=b):
+            cq.cq_gemv(gs.Q4_K, wgt[i % len(wgt)], n, k, xq, b, y=g)
+            cq.cq_gemv(gs.Q4_K, wup[i % len(wup)], n, k, xq, b, y=u)
+            cq.cq_swiglu_quantize_q8_0(g[:b], u[:b], hq=hq[:b])
+
+        us_f = _burst_us(fused, 100, stream)
+        us_s = _burst_us(separate, 100, stream)
+        wb = 2 * wgt[0].numel()
+        out[f"q4_k_ffn_gate_up_swiglu_14336x4096_b{b}"] = {
+            "fused_us": round(us_f, 2), "separate_us": round(us_s, 2),
+            "fused_weight_GB/s": round(wb / us_f / 1e3, 1),
+            "fused_pct_hbm_peak": round(100 * wb / us_f / 1e3 / HBM_PEAK_GBS, 1)}
+    del wgt, wup
     # 2048 x 2048 Q4_0 GEMV (2.36 MB per call: launch-latency bound)
     n, k = 2048, 2048
     w0 = copies(gs.weights(gs.Q4_0, n, k, cfg=0))

@@ -140,6 +140,30 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
             cq_stream_t stream);
 
 /*
+ * cq_gemv_swiglu -- fused decode FFN front half for 1..8 activation rows:
+ *     h[b*ldh + i] = silu(g) * u,  g = sum_j Wg_hat[i][j] * x_hat[b][j],
+ *                                  u = sum_j Wu_hat[i][j] * x_hat[b][j],
+ * silu(z) = z / (1 + exp(-z)) evaluated in fp64 from the fp32 g and u and
+ * rounded once to fp32 (alice-llm 2.0.0 README, "The GPU Optimization
+ * Journey", phase 4: gate + up + silu x mul in one pass that shares the
+ * activation read).  One kernel streams the gate and up rows of each output
+ * in turn; g and u are bitwise the values cq_gemv returns for the two
+ * matrices, so h equals SwiGLU of those up to the fp64 exp's last bit.
+ *   wt          any cq_gemv type; w_gate, w_up [n][k/qk] blocks, 16-byte
+ *               aligned (both matrices of the same type and shape).
+ *   xq          [batch][k/32] Q8_0 blocks, 16-byte aligned.
+ *   h           fp32, row b at h + b*ldh, ldh >= n, 4-byte aligned.
+ *   Shapes: the single-pass kernel needs one wave per row: k <= 4096 and
+ *   k a multiple of 256 (whole 16-byte weight and activation rows; Q6_K:
+ *   k a multiple of 2048); other shapes return CQ_ERR_SHAPE (use cq_gemv
+ *   twice and cq_swiglu_quantize_q8_0).  An xq not 16-byte aligned returns
+ *   CQ_ERR_ALIGNMENT.
+ */
+int cq_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                   const void* xq, int64_t batch, float* h, int64_t ldh,
+                   cq_stream_t stream);
+
+/*
  * cq_gemm -- prefill GEMM over m activation rows:
  *     y[r*ldy + i] = sum_j w_hat[i][j] * x_hat[r][j]
  * computed as int8 MFMA products of each 32-value block with the two block

@@ -25,7 +25,7 @@ STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",
 
 EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
-    "cq_quantize_q8_0", "cq_gemv", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
+    "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
     "cq_swiglu_quantize_q8_0", "cq_moe_combine",
 ]
 
@@ -63,6 +63,7 @@ def load():
         "cq_row_bytes": (I64, [I, I64]),
         "cq_quantize_q8_0": (I, [P, I64, I64, I64, P, P]),
         "cq_gemv": (I, [I, P, I64, I64, P, I64, P, I64, P]),
+        "cq_gemv_swiglu": (I, [I, P, P, I64, I64, P, I64, P, I64, P]),
         "cq_gemm": (I, [I, P, I64, I64, P, I64, P, I64, P]),
         "cq_moe_group": (I, [P, I64, I64, I64, P, P, P]),
         "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
@@ -135,6 +136,21 @@ def cq_gemv(wt, w, n, k, xq, batch, y=None, ldy=None, stream=None):
     _check("cq_gemv", load().cq_gemv(wt, _ptr(w), n, k, _ptr(xq), batch, _ptr(y), ldy,
                                       _stream(stream)))
     return y
+
+
+def cq_gemv_swiglu(wt, w_gate, w_up, n, k, xq, batch, h=None, ldh=None, stream=None):
+    """h[b][i] = silu(g) * u with g, u the gate and up GEMVs of row b (fused)."""
+    import torch
+    _dev_tensor(w_gate, "w_gate", torch.uint8)
+    _dev_tensor(w_up, "w_up", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    if h is None:
+        h = torch.empty((batch, n), dtype=torch.float32, device=w_gate.device)
+    _dev_tensor(h, "h", torch.float32)
+    ldh = ldh if ldh is not None else (h.stride(0) if h.dim() == 2 else n)
+    _check("cq_gemv_swiglu", load().cq_gemv_swiglu(wt, _ptr(w_gate), _ptr(w_up), n, k, _ptr(xq),
+                                                    batch, _ptr(h), ldh, _stream(stream)))
+    return h
 
 
 def cq_gemm(wt, w, n, k, xq, m, y=None, ldy=None, stream=None):

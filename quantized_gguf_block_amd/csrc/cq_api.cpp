@@ -16,6 +16,7 @@
 namespace cq {
 
 int gemv_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
+int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
 int gemm_shape_ok(int wt, int64_t n, int64_t k);       // gemm.hip
 int moe_shape_ok(int wt, int64_t n, int64_t k);        // moe.hip
 
@@ -127,6 +128,20 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t
     if (!aligned(xq, 2) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
     return status_of(launch_gemv(wt, w, n, k, xq, batch, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                   const void* xq, int64_t batch, float* h, int64_t ldh, cq_stream_t stream) {
+    if (int rc = check_weights(wt, w_gate, n, k)) return rc;
+    if (int rc = check_weights(wt, w_up, n, k)) return rc;
+    if (batch < 1 || batch > CQ_GEMV_MAX_BATCH || ldh < n) return CQ_ERR_INVALID_ARG;
+    if (gemv_swiglu_shape_ok(wt, k, batch) != 0) return CQ_ERR_SHAPE;
+    if (n == 0) return CQ_OK;
+    if (!xq || !h) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(h, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_gemv_swiglu(wt, w_gate, w_up, n, k, xq, batch, h, ldh,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,

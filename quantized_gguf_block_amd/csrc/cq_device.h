@@ -10,6 +10,14 @@ namespace cq {
 
 constexpr int kWave = 64;
 
+// h = fp32( silu(g) * u ) with silu(z) = z / (1 + exp(-z)) evaluated in fp64
+// and rounded once.
+__device__ __forceinline__ float swiglu1(float g, float u) {
+    const double z = static_cast<double>(g);
+    const double s = z / (1.0 + exp(-z));
+    return static_cast<float>(s * static_cast<double>(u));
+}
+
 // ---- fp16 ---------------------------------------------------------------
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));

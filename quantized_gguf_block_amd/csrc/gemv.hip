@@ -580,6 +580,51 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_
     if (g < NG && idx < V && r < rt) y[j * ldy + r0 + r * rs] = out;
 }
 
+// As reduce_store, for rows that alternate gate, up, gate, up (r0 even):
+// after the reduction the lane holding gate row 2p, batch j fetches the up
+// row 2p+1 of the same batch row from the lane that holds it and stores
+// h[j*ldh + (r0 + 2p)/2] = silu(gate)*up.  The sums are those reduce_store
+// forms (the association order does not depend on the slot).
+template <int RT, int B>
+__device__ __forceinline__ void reduce_swiglu(float (&acc)[RT][B], int rt, int64_t r0,
+                                              float* __restrict__ h, int64_t ldh, int lane) {
+    static_assert(RT % 2 == 0, "gate/up pairs");
+    constexpr int V = RT * B;
+    constexpr int NG = (V + 3) / 4;
+    static_assert(NG <= 16, "at most 64 values");
+    float vals[4 * NG];
+#pragma unroll
+    for (int i = 0; i < 4 * NG; ++i) vals[i] = (i < V) ? acc[i / B][i % B] : 0.0f;
+    float out = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g]),
+                                                         __float_as_uint(vals[4 * g + 1]), false, false);
+        const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g + 2]),
+                                                         __float_as_uint(vals[4 * g + 3]), false, false);
+        const float sab = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
+        const float scd = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(sab), __float_as_uint(scd),
+                                                        false, false);
+        float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        v += dpp_f<0xB1>(v);
+        v += dpp_f<0x4E>(v);
+        v += dpp_f<0x141>(v);
+        v += dpp_f<0x140>(v);
+        if ((lane & 15) == g) out = v;
+    }
+    // value idx sits in lane 16*perm(idx % 4) + idx / 4, perm swapping 1 and 2
+    const int row = lane >> 4, g = lane & 15;
+    const int idx = 4 * g + (row == 1 ? 2 : (row == 2 ? 1 : row));
+    const int r = idx / B, j = idx - (idx / B) * B;
+    const int pidx = (idx + B < V) ? idx + B : idx;
+    const int pm = pidx & 3;
+    const int plane = 16 * (pm == 1 ? 2 : (pm == 2 ? 1 : pm)) + (pidx >> 2);
+    const float up = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * plane, __float_as_int(out)));
+    if (g < NG && idx < V && (r & 1) == 0 && r < rt)
+        h[j * ldh + (r0 + r) / 2] = swiglu1(out, up);
+}
+
 // ---- streaming kernel: one wave per workgroup, each wave owns a contiguous
 // range of rows; every lane loads its own blocks of each row straight from
 // HBM into registers (non-temporal 16-byte loads), through a ring of P row
@@ -712,11 +757,15 @@ constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per 
 template <int FMT, int B, int C>
 constexpr int kActMax = B * (kSuper<FMT> ? 128 : 64) * C * 34;
 
-template <int FMT, int B, int C, int P>
+// SW: fused gate/up + SwiGLU.  Then w is the gate matrix, w2 the up matrix,
+// the wave's rows are gate/up pairs (rows_q, rows_r count pairs), row 2i of
+// the wave's virtual range is gate row i and row 2i+1 up row i, and y
+// receives h = silu(gate)*up.
+template <int FMT, int B, int C, int P, bool SW = false>
 __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
-        int64_t ldy) {
+        int64_t ldy, const uint8_t* __restrict__ w2 = nullptr) {
     using W = Win<FMT, C>;
     // 16-byte pieces per lane and row: piece j of lane l is row bytes
     // [1024 j + 16 l, +16), so every load instruction reads one contiguous KiB
@@ -746,8 +795,9 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // global wave g owns rows [rbeg, rend): rows_q each, one more for the
     // first rows_r (possibly none)
     const int64_t g = static_cast<int64_t>(blockIdx.x) * kGW + wv;
-    const int64_t rbeg = g * rows_q + (g < rows_r ? g : rows_r);
-    const int64_t rend = rbeg + rows_q + (g < rows_r ? 1 : 0);
+    constexpr int U = SW ? 2 : 1;  // rows per unit (SW: a gate/up pair)
+    const int64_t rbeg = U * (g * rows_q + (g < rows_r ? g : rows_r));
+    const int64_t rend = rbeg + U * (rows_q + (g < rows_r ? 1 : 0));
     const bool valid = C * lane < ncols;
     // byte offsets of this lane's column data within a row
     int off, qoff = 0, c0 = 0;
@@ -769,7 +819,10 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // without memory traffic; they are staged or computed and never stored.
     auto load_row = [&](int64_t r, u32x4* d) {
         const bool in = r < rend;
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(w + (in ? r : 0) * rb, in ? static_cast<int>(rb) : 0);
+        const uint8_t* base;
+        if constexpr (SW) base = ((r & 1) ? w2 : w) + (in ? r >> 1 : 0) * rb;
+        else base = w + (in ? r : 0) * rb;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(base, in ? static_cast<int>(rb) : 0);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
             d[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 * j + 16 * lane, 0, kNonTemporal);
@@ -960,7 +1013,8 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const int rt = static_cast<int>(rend - r < P ? rend - r : P);
-        reduce_store<P, B>(acc, rt, r, y, ldy, lane);
+        if constexpr (SW) reduce_swiglu<P, B>(acc, rt, r, y, ldy, lane);
+        else reduce_store<P, B>(acc, rt, r, y, ldy, lane);
     };
     int64_t r = rbeg;
     for (; r + P < rend; r += P) group(r, Bool<true>{});
@@ -1011,22 +1065,25 @@ int resident_blocks_per_cu(K kernel, int threads) {
     return nb;
 }
 
-template <int FMT, int B, int SC>
+template <int FMT, int B, int SC, bool SW = false>
 int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint8_t* xq,
-                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
-    auto kern = gemv_stream_kernel<FMT, B, SC, kRing>;
+                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream,
+                  const uint8_t* w2 = nullptr) {
+    auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW>;
     static const int occ = kGW * resident_blocks_per_cu(kern, kWave * kGW);
     int per_cu = occ < 8 ? occ : 8;
     // as many waves as fit, each with a whole number of P-row groups where
     // possible: gpw groups per wave, then the fewest waves that cover n,
-    // rounded up to whole workgroups (spare waves get no rows)
+    // rounded up to whole workgroups (spare waves get no rows).  Units are
+    // rows, or gate/up row pairs (two per group) for SW.
+    constexpr int64_t upg = SW ? kRing / 2 : kRing;  // units per group
     const int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu;
-    const int64_t groups = (n + kRing - 1) / kRing;
+    const int64_t groups = (n + upg - 1) / upg;
     const int64_t gpw = (groups + gmax - 1) / gmax;
-    const int64_t waves = (n + gpw * kRing - 1) / (gpw * kRing);
+    const int64_t waves = (n + gpw * upg - 1) / (gpw * upg);
     const int64_t wgs = (waves + kGW - 1) / kGW, nw = wgs * kGW;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(kWave * kGW), 0, stream, w,
-                       n / nw, static_cast<int>(n % nw), rb, ncols, xq, xrb, y, ldy);
+                       n / nw, static_cast<int>(n % nw), rb, ncols, xq, xrb, y, ldy, w2);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -1112,6 +1169,62 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_K: return launch_fmt<T_Q4_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q5_K: return launch_fmt<T_Q5_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q6_K: return launch_fmt<T_Q6_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        default: return -2;
+    }
+}
+
+// ---- fused gate/up GEMV + SwiGLU (decode FFN) -------------------------------
+// Streaming kernel only: the shape must give one wave per row (k <= 4096 for
+// the 32-value formats, k <= 4096 for the super-block formats), whole 16-byte
+// weight and activation rows, and a 16-byte aligned xq.
+int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch) {
+    if (gemv_shape_ok(wt, k, batch) != 0) return -3;
+    const Plan p = make_plan(wt, k, k / block_elems_of(wt) * block_bytes_of(wt),
+                             static_cast<int>(batch), true);
+    return p.SC > 0 ? 0 : -3;
+}
+
+template <int FMT, int B>
+int launch_sw_b(int SC, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb, int ncols,
+                const uint8_t* xq, int64_t xrb, float* h, int64_t ldh, hipStream_t stream) {
+    if (SC == 1) return launch_stream<FMT, B, 1, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+    if constexpr (!kSuper<FMT>)
+        if (SC == 2) return launch_stream<FMT, B, 2, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+    return -3;
+}
+
+template <int FMT>
+int launch_sw(int SC, int b, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb,
+              int ncols, const uint8_t* xq, int64_t xrb, float* h, int64_t ldh, hipStream_t s) {
+    switch (b) {
+        case 1: return launch_sw_b<FMT, 1>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 2: return launch_sw_b<FMT, 2>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 3: return launch_sw_b<FMT, 3>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 4: return launch_sw_b<FMT, 4>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 5: return launch_sw_b<FMT, 5>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 6: return launch_sw_b<FMT, 6>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 7: return launch_sw_b<FMT, 7>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        default: return launch_sw_b<FMT, 8>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+    }
+}
+
+int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
+                       const void* xq, int64_t batch, float* h, int64_t ldh, hipStream_t stream) {
+    if (gemv_swiglu_shape_ok(wt, k, batch) != 0) return -3;
+    const int64_t rb = k / block_elems_of(wt) * block_bytes_of(wt);
+    const Plan p = make_plan(wt, k, rb, static_cast<int>(batch), true);
+    const uint8_t* wg = static_cast<const uint8_t*>(w_gate);
+    const uint8_t* wu = static_cast<const uint8_t*>(w_up);
+    const uint8_t* xp = static_cast<const uint8_t*>(xq);
+    const int64_t xrb = k / 32 * 34;
+    const int b = static_cast<int>(batch);
+    switch (wt) {
+        case T_Q4_0: return launch_sw<T_Q4_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q4_1: return launch_sw<T_Q4_1>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q8_0: return launch_sw<T_Q8_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q4_K: return launch_sw<T_Q4_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q5_K: return launch_sw<T_Q5_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         default: return -2;
     }
 }

@@ -34,13 +34,6 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(
     }
 }
 
-// h = fp32( silu(g) * u ) with silu(z) = z / (1 + exp(-z)) in fp64.
-__device__ __forceinline__ float swiglu1(float g, float u) {
-    const double z = static_cast<double>(g);
-    const double s = z / (1.0 + exp(-z));
-    return static_cast<float>(s * static_cast<double>(u));
-}
-
 __global__ __launch_bounds__(256) void swiglu_quantize_q8_0_kernel(
         const float* __restrict__ g, const float* __restrict__ u, int64_t ld, int64_t rows,
         int64_t nb, float* __restrict__ h, uint8_t* __restrict__ hq) {

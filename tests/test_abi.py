@@ -86,6 +86,20 @@ def test_gemv_validation(lib):
     assert f(8, P(FAKE), -1, 256, P(FAKE), 1, P(FAKE), 8, None) == INVALID
 
 
+def test_gemv_swiglu_validation(lib):
+    f = lib.cq_gemv_swiglu
+    A = (P(FAKE), P(FAKE))
+    assert f(7, *A, 8, 256, P(FAKE), 1, P(FAKE), 8, None) == UNSUPPORTED
+    assert f(2, *A, 8, 8192, P(FAKE), 1, P(FAKE), 8, None) == SHAPE     # two waves per row
+    assert f(2, *A, 8, 352, P(FAKE), 1, P(FAKE), 8, None) == SHAPE      # not 16-byte rows
+    assert f(14, *A, 8, 1024, P(FAKE), 1, P(FAKE), 8, None) == SHAPE    # Q6_K needs k % 2048
+    assert f(2, *A, 8, 256, P(FAKE), 0, P(FAKE), 8, None) == INVALID    # batch 0
+    assert f(2, *A, 8, 256, P(FAKE), 1, P(FAKE), 7, None) == INVALID    # ldh < n
+    assert f(2, P(FAKE), P(FAKE + 8), 8, 256, P(FAKE), 1, P(FAKE), 8, None) == ALIGN
+    assert f(2, *A, 8, 256, P(FAKE + 2), 1, P(FAKE), 8, None) == ALIGN  # xq 16-aligned
+    assert f(2, *A, 0, 256, None, 1, None, 0, None) == OK               # n == 0
+
+
 def test_gemm_validation(lib):
     f = lib.cq_gemm
     assert f(2, P(FAKE), 8, 32, P(FAKE), 4, P(FAKE), 8, None) == SHAPE     # k % 256
