@@ -241,7 +241,8 @@ def secondary(cq, gs, dev, stream):
     tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
     the fused Q4_K gate/up/SwiGLU GEMV against the separate kernels,
     the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
-    the Q5_K and Q6_K prefill GEMMs at 512 tokens, and the whole routed FFN (quantize, group, gate, up, SwiGLU + requantize,
+    the Q5_K and Q6_K prefill GEMMs at 512 tokens, the whole routed FFN, and
+    one decode token through the routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
     import torch
     out = {}
@@ -369,6 +370,41 @@ def secondary(cq, gs, dev, stream):
         cq.cq_moe_combine(d, rw, y=yt)
 
     us = _burst_us(ffn, 50, stream)
+
+    # decode: one token, top 4, the whole FFN through the per-pair GEMV path
+    # (no grouping call) against the grouped path on the same token
+    ids1, rw1 = gs.routing(1, E, K, 850)
+    ids1, rw1 = torch.from_numpy(ids1).to(dev), torch.from_numpy(rw1).to(dev)
+    x1 = torch.from_numpy(gs.activations(1, H, 850)).to(dev)
+    h1 = torch.empty((K, F), dtype=torch.float32, device=dev)
+    hq1 = torch.empty((K, F // 32 * 34), dtype=torch.uint8, device=dev)
+    d1 = torch.empty((K, H), dtype=torch.float32, device=dev)
+    y1 = torch.empty((1, H), dtype=torch.float32, device=dev)
+
+    def ffn_decode(i):
+        wg_, wu_, wd_ = sets[i % len(sets)]
+        cq.cq_quantize_q8_0(x1, xq[:1])
+        cq.cq_moe_gemv_swiglu(gs.Q4_K, wg_, wu_, E, F, H, xq[:1], ids1, h=h1)
+        cq.cq_quantize_q8_0(h1, hq1)
+        cq.cq_moe_gemv(gs.Q4_K, wd_, E, H, F, hq1, True, ids1, y=d1)
+        cq.cq_moe_combine(d1, rw1, y=y1)
+
+    def ffn_decode_grouped(i):
+        wg_, wu_, wd_ = sets[i % len(sets)]
+        cq.cq_quantize_q8_0(x1, xq[:1])
+        cq.cq_moe_group(ids1, E, offs, pairs[:K])
+        cq.cq_moe_gemm(gs.Q4_K, wg_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=g[:K])
+        cq.cq_moe_gemm(gs.Q4_K, wu_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=u[:K])
+        cq.cq_swiglu_quantize_q8_0(g[:K], u[:K], hq=hq1)
+        cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq1, True, offs, pairs[:K], 1, K, y=d1)
+        cq.cq_moe_combine(d1, rw1, y=y1)
+
+    us_dec = _burst_us(ffn_decode, 100, stream)
+    us_dec_g = _burst_us(ffn_decode_grouped, 100, stream)
+    wdec = K * sum(m_.nbytes for m_ in mats) // E
+    out["q4_k_moe_ffn_decode_1tok_top4"] = {
+        "us": round(us_dec, 2), "grouped_path_us": round(us_dec_g, 2),
+        "expert_weight_GB/s": round(wdec / us_dec / 1e3, 1)}
     ops = 2 * T * K * (2 * F * H + H * F)
     out["q4_k_moe_ffn_256tok_32x_top4"] = {
         "us": round(us, 2), "expert_weight_GB/s": round(wbytes / us / 1e3, 1),

@@ -219,6 +219,37 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
                 float* y, int64_t ldy, cq_stream_t stream);
 
 /*
+ * cq_moe_gemv -- routed experts at decode: the same product as cq_moe_gemm
+ * for a few tokens, taken straight from the routing table, one GEMV per
+ * token-expert pair p = t*top_k + s (no grouping call):
+ *     y[p*ldy + i] = sum_j W_e_hat[i][j] * x_hat[row][j],  e = expert_ids[p],
+ * row = p / top_k (x_per_pair = 0) or p (x_per_pair = 1).  Each pair
+ * streams its expert's matrix once, so an expert chosen by two pairs is read
+ * twice: meant for decode and verify batches (Cera README, "Supported
+ * models": lfm2moe's routed FFN; 1 token x top-4), where the grouped MFMA
+ * path would run 16-token tiles with one live row.
+ *   expert_ids  device int32 [n_tokens][top_k]; ids outside [0, n_experts)
+ *               are clamped into range (they cannot be checked on the host).
+ *   xq          Q8_0 rows, 16-byte aligned; y fp32 [n_tokens*top_k][ldy].
+ *   Shapes: as cq_gemv_swiglu (one wave per row), n_tokens*top_k <= 65535;
+ *   else CQ_ERR_SHAPE.
+ */
+int cq_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int x_per_pair, const int32_t* expert_ids,
+                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy,
+                cq_stream_t stream);
+
+/*
+ * cq_moe_gemv_swiglu -- cq_moe_gemv over the gate and up expert matrices
+ * fused with SwiGLU, as cq_gemv_swiglu per pair (x row = the pair's token):
+ *     h[p*ldh + i] = silu(g) * u for the pair's expert.
+ */
+int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_experts,
+                       int64_t n_experts, int64_t n, int64_t k, const void* xq,
+                       const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
+                       float* h, int64_t ldh, cq_stream_t stream);
+
+/*
  * cq_swiglu_quantize_q8_0 -- h = silu(g) * u with silu(z) = z/(1+exp(-z))
  * (alice-llm 2.0.0 README, "The GPU Optimization Journey", phase 4: fused
  * gate/up SwiGLU), evaluated in fp64 from the fp32 inputs and rounded once

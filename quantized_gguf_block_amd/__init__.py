@@ -26,7 +26,7 @@ STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",
 EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
     "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
-    "cq_swiglu_quantize_q8_0", "cq_moe_combine",
+    "cq_swiglu_quantize_q8_0", "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu",
 ]
 
 
@@ -69,6 +69,8 @@ def load():
         "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
         "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, I64, P, P, P]),
         "cq_moe_combine": (I, [P, P, I64, I64, I64, P, I64, P]),
+        "cq_moe_gemv": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, I64, P]),
+        "cq_moe_gemv_swiglu": (I, [I, P, P, I64, I64, I64, P, P, I64, I64, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -213,6 +215,43 @@ def cq_swiglu_quantize_q8_0(g, u, h=None, want_h=False, hq=None, stream=None):
         _ptr(g), _ptr(u), g.stride(0) if rows > 1 else k, rows, k, _ptr(h), _ptr(hq),
         _stream(stream)))
     return h, hq
+
+
+def cq_moe_gemv(wt, w_experts, n_experts, n, k, xq, x_per_pair, expert_ids, y=None, ldy=None,
+                stream=None):
+    """Decode routed experts: y[t*top_k+s] = W[ids[t][s]] x_hat[t or t*top_k+s] (one GEMV per pair)."""
+    import torch
+    _dev_tensor(w_experts, "w_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(expert_ids, "expert_ids", torch.int32)
+    n_tokens, top_k = expert_ids.shape
+    if y is None:
+        y = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_experts.device)
+    _dev_tensor(y, "y", torch.float32)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    _check("cq_moe_gemv", load().cq_moe_gemv(wt, _ptr(w_experts), n_experts, n, k, _ptr(xq),
+                                              int(bool(x_per_pair)), _ptr(expert_ids), n_tokens,
+                                              top_k, _ptr(y), ldy, _stream(stream)))
+    return y
+
+
+def cq_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq, expert_ids,
+                       h=None, ldh=None, stream=None):
+    """Decode routed gate/up + SwiGLU: h[t*top_k+s] = silu(Wg_e x_t) * (Wu_e x_t), e = ids[t][s]."""
+    import torch
+    _dev_tensor(w_gate_experts, "w_gate_experts", torch.uint8)
+    _dev_tensor(w_up_experts, "w_up_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(expert_ids, "expert_ids", torch.int32)
+    n_tokens, top_k = expert_ids.shape
+    if h is None:
+        h = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_gate_experts.device)
+    _dev_tensor(h, "h", torch.float32)
+    ldh = ldh if ldh is not None else (h.stride(0) if h.dim() == 2 else n)
+    _check("cq_moe_gemv_swiglu", load().cq_moe_gemv_swiglu(
+        wt, _ptr(w_gate_experts), _ptr(w_up_experts), n_experts, n, k, _ptr(xq), _ptr(expert_ids),
+        n_tokens, top_k, _ptr(h), ldh, _stream(stream)))
+    return h
 
 
 def cq_moe_combine(d, route_w, y=None, stream=None):

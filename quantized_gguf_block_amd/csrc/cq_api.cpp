@@ -17,6 +17,7 @@ namespace cq {
 
 int gemv_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
 int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch);  // gemv.hip
+int moe_gemv_shape_ok(int wt, int64_t k, int64_t npairs);     // gemv.hip
 int gemm_shape_ok(int wt, int64_t n, int64_t k);       // gemm.hip
 int moe_shape_ok(int wt, int64_t n, int64_t k);        // moe.hip
 
@@ -142,6 +143,49 @@ int cq_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int6
     if (int rc = check_device()) return rc;
     return status_of(launch_gemv_swiglu(wt, w_gate, w_up, n, k, xq, batch, h, ldh,
                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+// shared argument checks of the two decode-MoE GEMV entry points
+static int check_moe_gemv(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                          const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t ldy) {
+    if (int rc = check_weights(wt, w, n, k)) return rc;
+    if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || top_k > n_experts ||
+        ldy < n)
+        return CQ_ERR_INVALID_ARG;
+    if (moe_gemv_shape_ok(wt, k, n_tokens * top_k) != 0) return CQ_ERR_SHAPE;
+    if (!aligned(ids, 4)) return CQ_ERR_ALIGNMENT;
+    return CQ_OK;
+}
+
+int cq_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int x_per_pair, const int32_t* expert_ids, int64_t n_tokens,
+                int64_t top_k, float* y, int64_t ldy, cq_stream_t stream) {
+    if (x_per_pair != 0 && x_per_pair != 1) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_moe_gemv(wt, w_experts, n_experts, n, k, expert_ids, n_tokens, top_k, ldy))
+        return rc;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    if (!xq || !expert_ids || !y) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_gemv(wt, w_experts, n_experts, n, k, xq, x_per_pair, expert_ids,
+                                     n_tokens, top_k, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_experts,
+                       int64_t n_experts, int64_t n, int64_t k, const void* xq,
+                       const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, float* h,
+                       int64_t ldh, cq_stream_t stream) {
+    if (int rc = check_moe_gemv(wt, w_gate_experts, n_experts, n, k, expert_ids, n_tokens, top_k,
+                                ldh))
+        return rc;
+    if (int rc = check_weights(wt, w_up_experts, n, k)) return rc;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    if (!xq || !expert_ids || !h) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(h, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq,
+                                            expert_ids, n_tokens, top_k, h, ldh,
+                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,

@@ -18,6 +18,13 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
                 float* y, int64_t ldy, hipStream_t stream);
 int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
                        const void* xq, int64_t batch, float* h, int64_t ldh, hipStream_t stream);
+int launch_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                    const void* xq, int x_per_pair, const int32_t* ids, int64_t n_tokens,
+                    int64_t top_k, float* y, int64_t ldy, hipStream_t stream);
+int launch_moe_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n_experts,
+                           int64_t n, int64_t k, const void* xq, const int32_t* ids,
+                           int64_t n_tokens, int64_t top_k, float* h, int64_t ldh,
+                           hipStream_t stream);
 int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m,
                 float* y, int64_t ldy, hipStream_t stream);
 int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,

@@ -757,15 +757,36 @@ constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per 
 template <int FMT, int B, int C>
 constexpr int kActMax = B * (kSuper<FMT> ? 128 : 64) * C * 34;
 
+// Routed-expert addressing for decode (MOE): blockIdx.y is the
+// token-expert pair p = t*top_k + s; its matrix is expert ids[p] (clamped
+// to the expert count) of the n_experts back-to-back matrices of mat_bytes
+// each, its activation row is xq row p (x_per_pair) or t, and its output
+// row is y + p*ldy.
+struct MoeMap {
+    const int32_t* ids;
+    int64_t mat_bytes;
+    int n_experts, top_k, x_per_pair;
+};
+
 // SW: fused gate/up + SwiGLU.  Then w is the gate matrix, w2 the up matrix,
 // the wave's rows are gate/up pairs (rows_q, rows_r count pairs), row 2i of
 // the wave's virtual range is gate row i and row 2i+1 up row i, and y
 // receives h = silu(gate)*up.
-template <int FMT, int B, int C, int P, bool SW = false>
+template <int FMT, int B, int C, int P, bool SW = false, bool MOE = false>
 __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
-        int64_t ldy, const uint8_t* __restrict__ w2 = nullptr) {
+        int64_t ldy, const uint8_t* __restrict__ w2 = nullptr, MoeMap mm = {}) {
+    if constexpr (MOE) {
+        static_assert(B == 1, "one activation row per token-expert pair");
+        const int pr = static_cast<int>(blockIdx.y);
+        int e = mm.ids[pr];
+        e = e < 0 ? 0 : (e >= mm.n_experts ? mm.n_experts - 1 : e);
+        w += static_cast<int64_t>(e) * mm.mat_bytes;
+        if constexpr (SW) w2 += static_cast<int64_t>(e) * mm.mat_bytes;
+        xq += static_cast<int64_t>(mm.x_per_pair ? pr : pr / mm.top_k) * xq_row_bytes;
+        y += static_cast<int64_t>(pr) * ldy;
+    }
     using W = Win<FMT, C>;
     // 16-byte pieces per lane and row: piece j of lane l is row bytes
     // [1024 j + 16 l, +16), so every load instruction reads one contiguous KiB
@@ -1065,11 +1086,11 @@ int resident_blocks_per_cu(K kernel, int threads) {
     return nb;
 }
 
-template <int FMT, int B, int SC, bool SW = false>
+template <int FMT, int B, int SC, bool SW = false, bool MOE = false>
 int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint8_t* xq,
                   int64_t xrb, float* y, int64_t ldy, hipStream_t stream,
-                  const uint8_t* w2 = nullptr) {
-    auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW>;
+                  const uint8_t* w2 = nullptr, MoeMap mm = {}, int npairs = 1) {
+    auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW, MOE>;
     static const int occ = kGW * resident_blocks_per_cu(kern, kWave * kGW);
     int per_cu = occ < 8 ? occ : 8;
     // as many waves as fit, each with a whole number of P-row groups where
@@ -1077,13 +1098,16 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
     // rounded up to whole workgroups (spare waves get no rows).  Units are
     // rows, or gate/up row pairs (two per group) for SW.
     constexpr int64_t upg = SW ? kRing / 2 : kRing;  // units per group
-    const int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu;
+    // (MOE: the wave slots are shared by the npairs matrices of the launch)
+    int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu / npairs;
+    if (gmax < kGW) gmax = kGW;
     const int64_t groups = (n + upg - 1) / upg;
     const int64_t gpw = (groups + gmax - 1) / gmax;
     const int64_t waves = (n + gpw * upg - 1) / (gpw * upg);
     const int64_t wgs = (waves + kGW - 1) / kGW, nw = wgs * kGW;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(kWave * kGW), 0, stream, w,
-                       n / nw, static_cast<int>(n % nw), rb, ncols, xq, xrb, y, ldy, w2);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs), static_cast<unsigned>(npairs)),
+                       dim3(kWave * kGW), 0, stream, w, n / nw, static_cast<int>(n % nw), rb, ncols,
+                       xq, xrb, y, ldy, w2, mm);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -1227,6 +1251,64 @@ int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, 
         case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         default: return -2;
     }
+}
+
+// ---- routed experts at decode: one GEMV per token-expert pair ---------------
+// Same single-pass shapes as the fused FFN (one wave per row); pairs beyond
+// grid.y's range are refused.
+int moe_gemv_shape_ok(int wt, int64_t k, int64_t npairs) {
+    if (npairs > 65535) return -3;
+    return gemv_swiglu_shape_ok(wt, k, 1);
+}
+
+template <int FMT, bool SW>
+int launch_moe_gemv_fmt(int SC, const uint8_t* w, const uint8_t* w2, int64_t n, int64_t rb,
+                        int ncols, const uint8_t* xq, int64_t xrb, float* y, int64_t ldy,
+                        const MoeMap& mm, int npairs, hipStream_t s) {
+    if (SC == 1) return launch_stream<FMT, 1, 1, SW, true>(w, n, rb, ncols, xq, xrb, y, ldy, s, w2, mm, npairs);
+    if constexpr (!kSuper<FMT>)
+        if (SC == 2) return launch_stream<FMT, 1, 2, SW, true>(w, n, rb, ncols, xq, xrb, y, ldy, s, w2, mm, npairs);
+    return -3;
+}
+
+template <bool SW>
+int launch_moe_gemv_any(int wt, const void* w, const void* w2, int64_t n_experts, int64_t n,
+                        int64_t k, const void* xq, int x_per_pair, const int32_t* ids,
+                        int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, hipStream_t s) {
+    const int64_t npairs = n_tokens * top_k;
+    if (moe_gemv_shape_ok(wt, k, npairs) != 0) return -3;
+    const int64_t rb = k / block_elems_of(wt) * block_bytes_of(wt);
+    const Plan p = make_plan(wt, k, rb, 1, true);
+    const MoeMap mm{ids, n * rb, static_cast<int>(n_experts), static_cast<int>(top_k), x_per_pair};
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    const uint8_t* wp2 = static_cast<const uint8_t*>(w2);
+    const uint8_t* xp = static_cast<const uint8_t*>(xq);
+    const int64_t xrb = k / 32 * 34;
+    const int np = static_cast<int>(npairs);
+    switch (wt) {
+        case T_Q4_0: return launch_moe_gemv_fmt<T_Q4_0, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q4_1: return launch_moe_gemv_fmt<T_Q4_1, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q8_0: return launch_moe_gemv_fmt<T_Q8_0, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q4_K: return launch_moe_gemv_fmt<T_Q4_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q5_K: return launch_moe_gemv_fmt<T_Q5_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q6_K: return launch_moe_gemv_fmt<T_Q6_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        default: return -2;
+    }
+}
+
+int launch_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                    const void* xq, int x_per_pair, const int32_t* ids, int64_t n_tokens,
+                    int64_t top_k, float* y, int64_t ldy, hipStream_t stream) {
+    return launch_moe_gemv_any<false>(wt, w_experts, nullptr, n_experts, n, k, xq, x_per_pair, ids,
+                                      n_tokens, top_k, y, ldy, stream);
+}
+
+int launch_moe_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n_experts,
+                           int64_t n, int64_t k, const void* xq, const int32_t* ids,
+                           int64_t n_tokens, int64_t top_k, float* h, int64_t ldh,
+                           hipStream_t stream) {
+    return launch_moe_gemv_any<true>(wt, w_gate, w_up, n_experts, n, k, xq, 0, ids, n_tokens,
+                                     top_k, h, ldh, stream);
 }
 
 }  // namespace cq

@@ -100,6 +100,24 @@ def test_gemv_swiglu_validation(lib):
     assert f(2, *A, 0, 256, None, 1, None, 0, None) == OK               # n == 0
 
 
+def test_moe_gemv_validation(lib):
+    f = lib.cq_moe_gemv
+    A = (P(FAKE), 32, 64, 2048)
+    assert f(7, *A, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == UNSUPPORTED
+    assert f(12, *A, P(FAKE), 2, P(FAKE), 1, 4, P(FAKE), 64, None) == INVALID   # x_per_pair
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 1, 40, P(FAKE), 64, None) == INVALID  # top_k > E
+    assert f(12, P(FAKE), 32, 64, 8192, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == SHAPE
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 20000, 4, P(FAKE), 64, None) == SHAPE  # > 65535 pairs
+    assert f(12, *A, P(FAKE + 2), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == ALIGN  # xq
+    assert f(12, *A, P(FAKE), 0, P(FAKE + 2), 1, 4, P(FAKE), 64, None) == ALIGN  # ids
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 0, 4, P(FAKE), 64, None) == OK         # no tokens
+    g = lib.cq_moe_gemv_swiglu
+    assert g(12, P(FAKE), P(FAKE + 8), 32, 64, 2048, P(FAKE), P(FAKE), 1, 4, P(FAKE), 64,
+             None) == ALIGN                                                      # w_up
+    assert g(12, P(FAKE), P(FAKE), 32, 64, 2048, P(FAKE), P(FAKE), 1, 4, P(FAKE), 63,
+             None) == INVALID                                                    # ldh < n
+
+
 def test_gemm_validation(lib):
     f = lib.cq_gemm
     assert f(2, P(FAKE), 8, 32, P(FAKE), 4, P(FAKE), 8, None) == SHAPE     # k % 256
