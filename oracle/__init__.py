@@ -43,6 +43,8 @@ def lib():
             "oracle_moe_group": (I, [P, I64, I64, I64, P, P]),
             "oracle_moe_matmul": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, P, I]),
             "oracle_moe_combine": (I, [P, P, P, I64, I64, I64, P, P]),
+            "oracle_argmax_rows": (None, [P, I64, I64, I64, P]),
+            "oracle_topk_softmax": (I, [P, I64, I64, I64, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -191,3 +193,24 @@ def moe_combine(d, s_in, route_w):
     _check(lib().oracle_moe_combine(_p(d), _p(s_in), _p(route_w), n_tokens, top_k, n,
                                     _p(y), _p(s)), "moe_combine")
     return y, (s if s_in is not None else None)
+
+
+def argmax_rows(y):
+    """First index of the largest value of each row of fp32 y [rows][n]."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    rows, n = y.shape
+    idx = np.empty(rows, np.int32)
+    lib().oracle_argmax_rows(_p(y), rows, n, n, _p(idx))
+    return idx
+
+
+def topk_softmax(logits, top_k):
+    """Router: (ids int32 [rows][top_k], w fp32 [rows][top_k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    rows, n_experts = logits.shape
+    ids = np.empty((rows, top_k), np.int32)
+    w = np.empty((rows, top_k), np.float32)
+    _check(lib().oracle_topk_softmax(_p(logits), rows, n_experts, n_experts, top_k, _p(ids), _p(w)),
+           "topk_softmax")
+    return ids, w
+

@@ -569,3 +569,36 @@ int oracle_moe_combine(const double* d, const double* s_in, const float* route_w
 }
 
 }  // extern "C"
+
+/* ---- greedy arg-max and router ------------------------------------------ */
+
+void oracle_argmax_rows(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* row = y + r * ldy;
+        int64_t best = 0;
+        for (int64_t i = 1; i < n; ++i)
+            if (row[i] > row[best]) best = i;   /* strict: the first maximum wins */
+        idx[r] = static_cast<int32_t>(best);
+    }
+}
+
+int oracle_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_t ld,
+                        int64_t top_k, int32_t* ids, float* w) {
+    if (rows < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts || ld < n_experts) return -1;
+    std::vector<int64_t> order(static_cast<size_t>(n_experts));
+    for (int64_t t = 0; t < rows; ++t) {
+        const float* l = logits + t * ld;
+        for (int64_t e = 0; e < n_experts; ++e) order[static_cast<size_t>(e)] = e;
+        /* descending logit, then ascending id */
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int64_t a, int64_t b) { return l[a] > l[b]; });
+        const double l0 = static_cast<double>(l[order[0]]);
+        double sum = 0.0;
+        for (int64_t s = 0; s < top_k; ++s) sum += std::exp(static_cast<double>(l[order[s]]) - l0);
+        for (int64_t s = 0; s < top_k; ++s) {
+            ids[t * top_k + s] = static_cast<int32_t>(order[static_cast<size_t>(s)]);
+            w[t * top_k + s] = static_cast<float>(std::exp(static_cast<double>(l[order[s]]) - l0) / sum);
+        }
+    }
+    return 0;
+}

@@ -30,6 +30,12 @@
  *                 by expert is the stated follow-up.
  *   [alice-GPU]   alice-llm 2.0.0 README, "The GPU Optimization Journey",
  *                 phase 4: fused SwiGLU (gate + up + silu x mul).
+ *   [cera-V]      cera 0.5.3 README, "Speculative decoding", and Cera README,
+ *                 "Performance": greedy verification compares the target's
+ *                 arg-max token with the draft, and keeping the arg-max on
+ *                 the device reads a few bytes instead of the full logits.
+ *   [cera-R]      Cera README, "Supported models": lfm2moe routes each token
+ *                 to its own 4 of 32 experts.
  *   [alice-Q5K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
  *                 a Q5_K super-block is 176 bytes for 256 values (5.5 bpw),
  *                 fields d (fp16), dmin (fp16), scales[12], qh[32], qs[128].
@@ -63,6 +69,11 @@
  *     4-5 (the four shift-masks above); element l + 32*g takes the signed
  *     scale byte scales[8h + 2g + l/16]; value d*scale*(q-32).  This is the
  *     GGUF layout, so real GGUF tensors decode as stored.
+ *   - Greedy arg-max: the first index of the largest value (NaN-free rows;
+ *     -0 and +0 compare equal).
+ *   - Router: the top_k largest logits in descending order (equal logits:
+ *     smaller expert id first) and their softmax over those top_k only,
+ *     evaluated in fp64 and rounded once to fp32.
  *   - fp16 is IEEE-754 binary16, little-endian, subnormals honoured.
  *   - Q8_0 quantization: see oracle_quantize_q8_0.
  *   - SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z)), evaluated
@@ -156,6 +167,16 @@ int oracle_moe_matmul(int type, const uint8_t* w, int64_t n_experts, int64_t n, 
 int oracle_moe_combine(const double* d, const double* s_in, const float* route_w,
                        int64_t n_tokens, int64_t top_k, int64_t n,
                        double* y, double* s_out);
+
+/* idx[r] = first index of the largest of y[r*ldy + 0 .. n-1] [cera-V]. */
+void oracle_argmax_rows(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx);
+
+/* Router [cera-R]: for each row of logits (n_experts values, row stride ld),
+ * ids[t][0..top_k) = the top_k largest in descending order (ties: smaller
+ * id first) and w[t][s] = exp(l_s - l_0) / sum over the top_k of
+ * exp(l_j - l_0) in fp64, rounded to fp32.  Returns -1 on bad sizes. */
+int oracle_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_t ld,
+                        int64_t top_k, int32_t* ids, float* w);
 
 #ifdef __cplusplus
 }

@@ -622,3 +622,54 @@ def test_q5k_matmul_equals_q4k_plus_high_part(orc):
     y4, _ = orc.matmul(gs.Q4_K, wk.reshape(n, -1), n, k, xq, 2)
     y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
     assert np.allclose(y5, y4 + y8, rtol=0, atol=1e-12 * np.abs(y5).max())
+
+
+# --------------------------------------------------------- greedy arg-max
+# cera 0.5.3 README, "Speculative decoding": greedy verification compares
+# arg-max tokens.  Reading: the first index of the largest value.
+
+def test_argmax_rows_matches_numpy(orc):
+    rng = np.random.default_rng(60)
+    y = rng.standard_normal((7, 1000)).astype(np.float32)
+    y[1, 10] = y[1, 900] = 9.0          # a tie: the first index wins
+    y[2, :] = 0.0
+    y[2, 5] = np.float32(-0.0)          # -0 and +0 compare equal
+    y[3, :] = -np.inf
+    y[3, 17] = -1e30
+    assert np.array_equal(orc.argmax_rows(y), np.argmax(y, axis=1))
+    assert orc.argmax_rows(y)[1] == 10 and orc.argmax_rows(y)[2] == 0
+
+
+# ------------------------------------------------------------------ router
+# Cera README, "Supported models": each token picks its own 4 of 32 experts.
+# Reading: the top_k largest logits, descending (equal logits: smaller id
+# first), softmax over those top_k in fp64, rounded to fp32.
+
+def test_router_topk_matches_stable_argsort(orc):
+    rng = np.random.default_rng(61)
+    logits = rng.standard_normal((50, 32)).astype(np.float32)
+    ids, w = orc.topk_softmax(logits, 4)
+    assert np.array_equal(ids, np.argsort(-logits, axis=1, kind="stable")[:, :4])
+    sel = np.take_along_axis(logits, ids, axis=1).astype(np.float64)
+    e = np.exp(sel - sel.max(axis=1, keepdims=True))
+    ref = e / e.sum(axis=1, keepdims=True)
+    assert np.allclose(w, ref, rtol=1e-6, atol=0)
+    assert np.all(np.diff(w, axis=1) <= 0)                     # descending logits -> weights
+    assert np.allclose(w.sum(axis=1), 1.0, atol=4 * 2.0 ** -24)
+
+
+def test_router_closed_forms(orc):
+    logits = np.zeros((3, 8), np.float32)
+    logits[1, [2, 5, 6]] = 3.0                                 # three-way tie at the top
+    logits[2] = np.arange(8, dtype=np.float32)
+    ids, w = orc.topk_softmax(logits, 4)
+    assert ids[0].tolist() == [0, 1, 2, 3] and np.all(w[0] == np.float32(0.25))
+    assert ids[1].tolist() == [2, 5, 6, 0]
+    assert ids[2].tolist() == [7, 6, 5, 4]
+    # exact shift invariance (integer logits, shift by 16)
+    ids2, w2 = orc.topk_softmax(logits + np.float32(16), 4)
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
+    # top_k = n_experts: the full softmax
+    idsf, wf = orc.topk_softmax(logits[2:3], 8)
+    e = np.exp(np.arange(8)[::-1] - 7.0)
+    assert np.allclose(wf[0], e / e.sum(), rtol=1e-7)
