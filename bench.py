@@ -241,9 +241,11 @@ def secondary(cq, gs, dev, stream):
     tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
     the fused Q4_K gate/up/SwiGLU GEMV against the separate kernels,
     the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
-    the Q5_K and Q6_K prefill GEMMs at 512 tokens, the whole routed FFN, and
-    one decode token through the routed FFN (quantize, group, gate, up, SwiGLU + requantize,
+    the Q5_K and Q6_K prefill GEMMs at 512 tokens, the greedy arg-max over
+    the LM-head logits, the router, the whole routed FFN, and one decode
+    token through the routed FFN (quantize, group, gate, up, SwiGLU + requantize,
     down, combine)."""
+    import numpy as np
     import torch
     out = {}
 
@@ -265,6 +267,13 @@ def secondary(cq, gs, dev, stream):
                 "us": round(us, 2), "GB/s": round(gbs, 1),
                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
         del wl
+    # greedy verify on the device: arg-max over the 128256 logits per row
+    for b in (1, 4):
+        ws = torch.empty(cq.load().cq_argmax_workspace_bytes(b, n), dtype=torch.uint8, device=dev)
+        idx = torch.empty(b, dtype=torch.int32, device=dev)
+        us = _burst_us(lambda i: cq.cq_argmax(y[:b], idx=idx, workspace=ws), 200, stream)
+        out[f"argmax_128256_logits_b{b}"] = {"us": round(us, 2),
+                                             "GB/s": round(b * n * 4 / us / 1e3, 1)}
     # Q5_K FFN-up GEMV 14336 x 4096 (the FFN type of Q5_K_M models)
     n, k = 14336, 4096
     c5 = gs.CONFIGS["q5_k_gemv_ffn_up"]
@@ -371,6 +380,12 @@ def secondary(cq, gs, dev, stream):
 
     us = _burst_us(ffn, 50, stream)
 
+    # router: top 4 of 32 with softmax, 256 tokens
+    lg = torch.from_numpy(np.random.default_rng(5).standard_normal((T, E)).astype(np.float32)).to(dev)
+    rid = torch.empty((T, K), dtype=torch.int32, device=dev)
+    rwt = torch.empty((T, K), dtype=torch.float32, device=dev)
+    out["router_top4_of_32_256tok"] = {
+        "us": round(_burst_us(lambda i: cq.cq_topk_softmax(lg, K, ids=rid, w=rwt), 200, stream), 2)}
     # decode: one token, top 4, the whole FFN through the per-pair GEMV path
     # (no grouping call) against the grouped path on the same token
     ids1, rw1 = gs.routing(1, E, K, 850)

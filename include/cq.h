@@ -80,7 +80,7 @@ typedef enum {
     CQ_ERR_UNSUPPORTED_TYPE = -2, /* weight type not supported by the call   */
     CQ_ERR_SHAPE = -3,            /* k not a multiple of the block, too big  */
     CQ_ERR_ALIGNMENT = -4,        /* pointer or leading dim misaligned       */
-    CQ_ERR_WORKSPACE = -5,        /* reserved                                */
+    CQ_ERR_WORKSPACE = -5,        /* caller workspace too small or misaligned */
     CQ_ERR_HIP = -6,              /* a HIP runtime call failed               */
     CQ_ERR_NO_DEVICE = -7         /* no gfx950 device current                */
 } cq_status;
@@ -248,6 +248,45 @@ int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_expe
                        int64_t n_experts, int64_t n, int64_t k, const void* xq,
                        const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
                        float* h, int64_t ldh, cq_stream_t stream);
+
+/*
+ * cq_argmax_workspace_bytes -- bytes of device workspace cq_argmax needs for
+ * rows x n logits (8 bytes per 4096-value chunk of each row); 0 on bad
+ * sizes.
+ */
+size_t cq_argmax_workspace_bytes(int64_t rows, int64_t n);
+
+/*
+ * cq_argmax -- greedy token choice on the device: idx[r] = the first index of
+ * the largest of y[r*ldy + 0 .. n-1] (cera 0.5.3 README, "Speculative
+ * decoding": the greedy verify compares arg-max tokens; Cera README,
+ * "Performance": the verify then reads 4 bytes per row instead of the
+ * logits).  -0 and +0 compare equal; rows must hold no NaN.  Deterministic
+ * (a maximum of (value, first index) keys).
+ *   y          fp32, 4-byte aligned (16-byte aligned rows read faster).
+ *   rows       0..65535; n 1..2^31-1; ldy >= n.
+ *   idx        int32 [rows].
+ *   workspace  caller device memory, 8-byte aligned, ws_bytes >=
+ *              cq_argmax_workspace_bytes(rows, n) (else CQ_ERR_WORKSPACE);
+ *              its contents are scratch, overwritten by each call.
+ */
+int cq_argmax(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx,
+              void* workspace, size_t ws_bytes, cq_stream_t stream);
+
+/*
+ * cq_topk_softmax -- the expert router (Cera README, "Supported models":
+ * each token picks its own top_k of n_experts): ids[t][0..top_k) = the
+ * top_k largest logits of row t in descending order (equal logits: smaller
+ * expert id first) and w[t][s] = their softmax over the chosen top_k only,
+ * exp(l_s - l_0) / sum_j exp(l_j - l_0) in fp64 summed in slot order,
+ * rounded once to fp32.  The output feeds cq_moe_group / cq_moe_gemv
+ * (ids) and cq_moe_combine (w).
+ *   logits     fp32 [rows][ld], ld >= n_experts, 4-byte aligned, no NaN.
+ *   n_experts  1..1024; top_k 1..min(16, n_experts).
+ *   ids        int32 [rows][top_k]; w fp32 [rows][top_k].
+ */
+int cq_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_t ld,
+                    int64_t top_k, int32_t* ids, float* w, cq_stream_t stream);
 
 /*
  * cq_swiglu_quantize_q8_0 -- h = silu(g) * u with silu(z) = z/(1+exp(-z))

@@ -27,6 +27,7 @@ EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
     "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
     "cq_swiglu_quantize_q8_0", "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu",
+    "cq_argmax_workspace_bytes", "cq_argmax", "cq_topk_softmax",
 ]
 
 
@@ -70,6 +71,9 @@ def load():
         "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, I64, P, P, P]),
         "cq_moe_combine": (I, [P, P, I64, I64, I64, P, I64, P]),
         "cq_moe_gemv": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, I64, P]),
+        "cq_argmax_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
+        "cq_argmax": (I, [P, I64, I64, I64, P, P, ctypes.c_size_t, P]),
+        "cq_topk_softmax": (I, [P, I64, I64, I64, I64, P, P, P]),
         "cq_moe_gemv_swiglu": (I, [I, P, P, I64, I64, I64, P, P, I64, I64, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
@@ -252,6 +256,41 @@ def cq_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq, ex
         wt, _ptr(w_gate_experts), _ptr(w_up_experts), n_experts, n, k, _ptr(xq), _ptr(expert_ids),
         n_tokens, top_k, _ptr(h), ldh, _stream(stream)))
     return h
+
+
+def cq_argmax(y, idx=None, workspace=None, stream=None):
+    """idx[r] = first index of the largest value of row r of fp32 y [rows][n]."""
+    import torch
+    _dev_tensor(y, "y", torch.float32)
+    rows, n = y.shape
+    if idx is None:
+        idx = torch.empty(rows, dtype=torch.int32, device=y.device)
+    _dev_tensor(idx, "idx", torch.int32)
+    need = load().cq_argmax_workspace_bytes(rows, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=y.device)
+    _dev_tensor(workspace, "workspace", torch.uint8)
+    ldy = y.stride(0) if rows > 1 else n
+    _check("cq_argmax", load().cq_argmax(_ptr(y), rows, n, ldy, _ptr(idx), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
+    return idx
+
+
+def cq_topk_softmax(logits, top_k, ids=None, w=None, stream=None):
+    """Router: (ids int32 [rows][top_k], w fp32 [rows][top_k]) from fp32 logits [rows][E]."""
+    import torch
+    _dev_tensor(logits, "logits", torch.float32)
+    rows, n_experts = logits.shape
+    if ids is None:
+        ids = torch.empty((rows, top_k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((rows, top_k), dtype=torch.float32, device=logits.device)
+    _dev_tensor(ids, "ids", torch.int32)
+    _dev_tensor(w, "w", torch.float32)
+    ld = logits.stride(0) if rows > 1 else n_experts
+    _check("cq_topk_softmax", load().cq_topk_softmax(_ptr(logits), rows, n_experts, ld, top_k,
+                                                      _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
 
 
 def cq_moe_combine(d, route_w, y=None, stream=None):

@@ -94,7 +94,7 @@ const char* cq_status_string(int status) {
         case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K)";
         case CQ_ERR_SHAPE: return "CQ_ERR_SHAPE: k is not a whole number of blocks or exceeds the kernel's limit";
         case CQ_ERR_ALIGNMENT: return "CQ_ERR_ALIGNMENT: pointer or leading dimension misaligned";
-        case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE";
+        case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE: workspace smaller than required or misaligned";
         case CQ_ERR_HIP: return "CQ_ERR_HIP: a HIP runtime call failed";
         case CQ_ERR_NO_DEVICE: return "CQ_ERR_NO_DEVICE: no HIP device is current";
         default: return "unknown cq status";
@@ -186,6 +186,39 @@ int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_expe
     return status_of(launch_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq,
                                             expert_ids, n_tokens, top_k, h, ldh,
                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t cq_argmax_workspace_bytes(int64_t rows, int64_t n) {
+    if (rows < 0 || n < 1 || n > 0x7FFFFFFF) return 0;
+    return static_cast<size_t>(rows) * static_cast<size_t>(argmax_chunks(n)) * 8u;
+}
+
+int cq_argmax(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx, void* workspace,
+              size_t ws_bytes, cq_stream_t stream) {
+    if (rows < 0 || n < 1 || ldy < n) return CQ_ERR_INVALID_ARG;
+    if (rows > 65535 || n > 0x7FFFFFFF) return CQ_ERR_SHAPE;
+    if (rows == 0) return CQ_OK;
+    if (!y || !idx || !workspace) return CQ_ERR_INVALID_ARG;
+    if (!aligned(y, 4) || !aligned(idx, 4)) return CQ_ERR_ALIGNMENT;
+    if (!aligned(workspace, 8) || ws_bytes < cq_argmax_workspace_bytes(rows, n))
+        return CQ_ERR_WORKSPACE;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_argmax(y, rows, n, ldy, idx, workspace,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_t ld,
+                    int64_t top_k, int32_t* ids, float* w, cq_stream_t stream) {
+    if (rows < 0 || n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > 16 ||
+        top_k > n_experts || ld < n_experts)
+        return CQ_ERR_INVALID_ARG;
+    if (rows > (int64_t(1) << 31)) return CQ_ERR_SHAPE;
+    if (rows == 0) return CQ_OK;
+    if (!logits || !ids || !w) return CQ_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4)) return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_topk_softmax(logits, rows, n_experts, ld, top_k, ids, w,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,

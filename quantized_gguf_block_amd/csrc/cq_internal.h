@@ -25,6 +25,11 @@ int launch_moe_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t
                            int64_t n, int64_t k, const void* xq, const int32_t* ids,
                            int64_t n_tokens, int64_t top_k, float* h, int64_t ldh,
                            hipStream_t stream);
+int64_t argmax_chunks(int64_t n);
+int launch_argmax(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx, void* ws,
+                  hipStream_t stream);
+int launch_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_t ld,
+                        int64_t top_k, int32_t* ids, float* w, hipStream_t stream);
 int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m,
                 float* y, int64_t ldy, hipStream_t stream);
 int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,

@@ -118,6 +118,27 @@ def test_moe_gemv_validation(lib):
              None) == INVALID                                                    # ldh < n
 
 
+def test_argmax_and_router_validation(lib):
+    assert lib.cq_argmax_workspace_bytes(4, 128256) == 4 * 32 * 8
+    assert lib.cq_argmax_workspace_bytes(1, 4096) == 8
+    assert lib.cq_argmax_workspace_bytes(1, 0) == 0
+    f = lib.cq_argmax
+    assert f(P(FAKE), 2, 0, 8, P(FAKE), P(FAKE), 64, None) == INVALID       # n == 0
+    assert f(P(FAKE), 2, 8, 7, P(FAKE), P(FAKE), 64, None) == INVALID       # ldy < n
+    assert f(P(FAKE), 70000, 8, 8, P(FAKE), P(FAKE), 1 << 20, None) == SHAPE
+    assert f(P(FAKE + 2), 2, 8, 8, P(FAKE), P(FAKE), 64, None) == ALIGN
+    assert f(P(FAKE), 2, 8, 8, P(FAKE), P(FAKE), 15, None) == -5            # workspace too small
+    assert f(P(FAKE), 2, 8, 8, P(FAKE), P(FAKE + 4), 64, None) == -5        # workspace alignment
+    assert f(None, 0, 8, 8, None, None, 0, None) == OK                      # no rows
+    g = lib.cq_topk_softmax
+    assert g(P(FAKE), 4, 32, 32, 0, P(FAKE), P(FAKE), None) == INVALID      # top_k 0
+    assert g(P(FAKE), 4, 32, 32, 17, P(FAKE), P(FAKE), None) == INVALID     # top_k > 16
+    assert g(P(FAKE), 4, 2000, 2000, 4, P(FAKE), P(FAKE), None) == INVALID  # > 1024 experts
+    assert g(P(FAKE), 4, 32, 31, 4, P(FAKE), P(FAKE), None) == INVALID      # ld < E
+    assert g(P(FAKE), 4, 32, 32, 4, P(FAKE + 1), P(FAKE), None) == ALIGN
+    assert g(None, 0, 32, 32, 4, None, None, None) == OK
+
+
 def test_gemm_validation(lib):
     f = lib.cq_gemm
     assert f(2, P(FAKE), 8, 32, P(FAKE), 4, P(FAKE), 8, None) == SHAPE     # k % 256
