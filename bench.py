@@ -173,7 +173,7 @@ def main():
     alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
     achieved = alg / (burst_ms * 1e-3) / 1e9
 
-    traffic, prof_us = profiled("gemv_stream_kernel<8, 5, 2, 4>")
+    traffic, prof_us = profiled("gemv_stream_kernel<8, 5, 2, 4, false, false>")
 
     extra = None if args.no_extra else secondary(cq, gs, dev, stream)
 
@@ -199,7 +199,7 @@ def main():
                    "n": n, "k": k, "batches": [1, B], "formats": ["q8_0", "q4_1"],
                    "weight_copies": {gs.NAMES[f]: len(copies[f]) for f in fmts}},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel<8, 5, 2, 4> (Q8_0, batch 5)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel<8, 5, 2, 4, false, false> (Q8_0, batch 5)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(burst_ms * 1e3, 3),
