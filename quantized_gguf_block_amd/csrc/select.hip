@@ -104,11 +104,12 @@ __global__ __launch_bounds__(kWave) void argmax_final_kernel(const uint64_t* __r
 }
 
 constexpr int kMaxExperts = 1024;
-constexpr int kPerLane = kMaxExperts / kWave;   // logits held per lane
 constexpr int kRouterWaves = 4;
 constexpr int kMaxTopK = 16;                   // largest top_k the router takes
 
-// One wave per token row (4 per workgroup).
+// One wave per token row (4 per workgroup); PL logits per lane (n_experts
+// <= 64 * PL).
+template <int PL>
 __global__ __launch_bounds__(kWave * kRouterWaves) void topk_softmax_kernel(
         const float* __restrict__ logits, int64_t rows, int n_experts, int64_t ld, int top_k,
         int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -116,47 +117,48 @@ __global__ __launch_bounds__(kWave * kRouterWaves) void topk_softmax_kernel(
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouterWaves + threadIdx.x / kWave;
     if (t >= rows) return;            // the whole wave leaves together
     const float* l = logits + t * ld;
-    uint64_t key[kPerLane];
+    uint64_t key[PL];
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
+    for (int j = 0; j < PL; ++j) {
         const int e = lane + kWave * j;
         key[j] = e < n_experts ? make_key(l[e], static_cast<uint32_t>(e)) : 0;
     }
-    // (rounds unrolled to the largest top_k so the chosen ids and logits
-    // stay in registers)
-    float val[kMaxTopK];
-    int sel[kMaxTopK];
+    // Each round every lane learns the chosen expert; lane s keeps the
+    // choice of round s (rounds unrolled, so no register array is indexed
+    // at run time).
+    int my_sel = 0;
+    float my_val = 0.0f, l0f = 0.0f;
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) {
-        sel[s] = 0;
-        val[s] = 0.0f;
         if (s < top_k) {              // (top_k is uniform: no divergence)
             uint64_t best = 0;
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j) best = umax64(best, key[j]);
+            for (int j = 0; j < PL; ++j) best = umax64(best, key[j]);
             best = wave_max64(best);
             const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFu));
-            sel[s] = e;
-            val[s] = l[e];
+            const float v = l[e];
+            if (s == 0) l0f = v;
+            if (lane == s) {
+                my_sel = e;
+                my_val = v;
+            }
             // the owner drops the chosen logit from later rounds
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j)
+            for (int j = 0; j < PL; ++j)
                 if (lane + kWave * j == e) key[j] = 0;
         }
     }
-    if (lane == 0) {
-        const double l0 = static_cast<double>(val[0]);
-        double sum = 0.0;
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-            if (s < top_k) sum += exp(static_cast<double>(val[s]) - l0);
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (s < top_k) {
-                ids[t * top_k + s] = sel[s];
-                w[t * top_k + s] = static_cast<float>(exp(static_cast<double>(val[s]) - l0) / sum);
-            }
-        }
+    // softmax over the chosen logits: one fp64 exp per lane, the sum taken
+    // in slot order
+    const double l0 = static_cast<double>(l0f);
+    const double ex = lane < top_k ? exp(static_cast<double>(my_val) - l0) : 0.0;
+    const int lo = __double2loint(ex), hi = __double2hiint(ex);
+    double sum = 0.0;
+    for (int s = 0; s < top_k; ++s)
+        sum += __hiloint2double(__shfl(hi, s), __shfl(lo, s));
+    if (lane < top_k) {
+        ids[t * top_k + lane] = my_sel;
+        w[t * top_k + lane] = static_cast<float>(ex / sum);
     }
 }
 
@@ -186,9 +188,18 @@ int launch_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, in
                         int64_t top_k, int32_t* ids, float* w, hipStream_t stream) {
     const int64_t wgs = (rows + kRouterWaves - 1) / kRouterWaves;
     if (wgs > 0x7FFFFFFF || n_experts > kMaxExperts || top_k > kMaxTopK) return -3;
-    hipLaunchKernelGGL(topk_softmax_kernel, dim3(static_cast<unsigned>(wgs)),
-                       dim3(kWave * kRouterWaves), 0, stream, logits, rows,
-                       static_cast<int>(n_experts), ld, static_cast<int>(top_k), ids, w);
+    const dim3 g(static_cast<unsigned>(wgs)), b(kWave * kRouterWaves);
+    const int ne = static_cast<int>(n_experts), tk = static_cast<int>(top_k);
+    if (n_experts <= 64)
+        hipLaunchKernelGGL(topk_softmax_kernel<1>, g, b, 0, stream, logits, rows, ne, ld, tk, ids, w);
+    else if (n_experts <= 128)
+        hipLaunchKernelGGL(topk_softmax_kernel<2>, g, b, 0, stream, logits, rows, ne, ld, tk, ids, w);
+    else if (n_experts <= 256)
+        hipLaunchKernelGGL(topk_softmax_kernel<4>, g, b, 0, stream, logits, rows, ne, ld, tk, ids, w);
+    else if (n_experts <= 512)
+        hipLaunchKernelGGL(topk_softmax_kernel<8>, g, b, 0, stream, logits, rows, ne, ld, tk, ids, w);
+    else
+        hipLaunchKernelGGL(topk_softmax_kernel<16>, g, b, 0, stream, logits, rows, ne, ld, tk, ids, w);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
