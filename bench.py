@@ -234,6 +234,37 @@ def _burst_us(fn, reps, stream):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def _graph_us(fn, nsteps, reps, stream):
+    """Average duration of one call of fn(i) with the launches captured in a
+    HIP graph (fn(0) .. fn(nsteps-1) in one graph, replayed `reps` times
+    between HIP events): the GPU time of launch-bound sequences without the
+    Python call overhead."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nsteps):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nsteps):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * nsteps) * 1e3
+
+
 def secondary(cq, gs, dev, stream):
     """The other workloads, each timed as a burst of back-to-back launches
     (weights rotated through >= 512 MB of copies where they would fit the
@@ -271,8 +302,10 @@ def secondary(cq, gs, dev, stream):
     for b in (1, 4):
         ws = torch.empty(cq.load().cq_argmax_workspace_bytes(b, n), dtype=torch.uint8, device=dev)
         idx = torch.empty(b, dtype=torch.int32, device=dev)
-        us = _burst_us(lambda i: cq.cq_argmax(y[:b], idx=idx, workspace=ws), 200, stream)
-        out[f"argmax_128256_logits_b{b}"] = {"us": round(us, 2),
+        fn = (lambda i, b=b, idx=idx, ws=ws: cq.cq_argmax(y[:b], idx=idx, workspace=ws))
+        us = _graph_us(fn, 8, 50, stream)
+        out[f"argmax_128256_logits_b{b}"] = {"graph_us": round(us, 2),
+                                             "python_burst_us": round(_burst_us(fn, 200, stream), 2),
                                              "GB/s": round(b * n * 4 / us / 1e3, 1)}
     # Q5_K FFN-up GEMV 14336 x 4096 (the FFN type of Q5_K_M models)
     n, k = 14336, 4096
@@ -306,11 +339,13 @@ def secondary(cq, gs, dev, stream):
             cq.cq_gemv(gs.Q4_K, wup[i % len(wup)], n, k, xq, b, y=u)
             cq.cq_swiglu_quantize_q8_0(g[:b], u[:b], hq=hq[:b])
 
-        us_f = _burst_us(fused, 100, stream)
-        us_s = _burst_us(separate, 100, stream)
+        ns = min(len(wgt), len(wup))
+        us_f = _graph_us(fused, ns, 20, stream)
+        us_s = _graph_us(separate, ns, 20, stream)
         wb = 2 * wgt[0].numel()
         out[f"q4_k_ffn_gate_up_swiglu_14336x4096_b{b}"] = {
-            "fused_us": round(us_f, 2), "separate_us": round(us_s, 2),
+            "fused_graph_us": round(us_f, 2), "separate_graph_us": round(us_s, 2),
+            "fused_python_burst_us": round(_burst_us(fused, 100, stream), 2),
             "fused_weight_GB/s": round(wb / us_f / 1e3, 1),
             "fused_pct_hbm_peak": round(100 * wb / us_f / 1e3 / HBM_PEAK_GBS, 1)}
     del wgt, wup
@@ -384,8 +419,9 @@ def secondary(cq, gs, dev, stream):
     lg = torch.from_numpy(np.random.default_rng(5).standard_normal((T, E)).astype(np.float32)).to(dev)
     rid = torch.empty((T, K), dtype=torch.int32, device=dev)
     rwt = torch.empty((T, K), dtype=torch.float32, device=dev)
-    out["router_top4_of_32_256tok"] = {
-        "us": round(_burst_us(lambda i: cq.cq_topk_softmax(lg, K, ids=rid, w=rwt), 200, stream), 2)}
+    rfn = (lambda i: cq.cq_topk_softmax(lg, K, ids=rid, w=rwt))
+    out["router_top4_of_32_256tok"] = {"graph_us": round(_graph_us(rfn, 8, 50, stream), 2),
+                                       "python_burst_us": round(_burst_us(rfn, 200, stream), 2)}
     # decode: one token, top 4, the whole FFN through the per-pair GEMV path
     # (no grouping call) against the grouped path on the same token
     ids1, rw1 = gs.routing(1, E, K, 850)
@@ -414,11 +450,12 @@ def secondary(cq, gs, dev, stream):
         cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq1, True, offs, pairs[:K], 1, K, y=d1)
         cq.cq_moe_combine(d1, rw1, y=y1)
 
-    us_dec = _burst_us(ffn_decode, 100, stream)
-    us_dec_g = _burst_us(ffn_decode_grouped, 100, stream)
+    us_dec = _graph_us(ffn_decode, len(sets), 20, stream)
+    us_dec_g = _graph_us(ffn_decode_grouped, len(sets), 20, stream)
     wdec = K * sum(m_.nbytes for m_ in mats) // E
     out["q4_k_moe_ffn_decode_1tok_top4"] = {
-        "us": round(us_dec, 2), "grouped_path_us": round(us_dec_g, 2),
+        "graph_us": round(us_dec, 2), "grouped_path_graph_us": round(us_dec_g, 2),
+        "python_burst_us": round(_burst_us(ffn_decode, 100, stream), 2),
         "expert_weight_GB/s": round(wdec / us_dec / 1e3, 1)}
     ops = 2 * T * K * (2 * F * H + H * F)
     out["q4_k_moe_ffn_256tok_32x_top4"] = {
