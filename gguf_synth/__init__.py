@@ -19,11 +19,12 @@ import numpy as np
 
 SEED = 20261202
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K = 2, 3, 8, 12, 13, 14
-FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0 = 2, 3, 8, 12, 13, 14, 41
+FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K,
+           "q1_0": Q1_0}
 NAMES = {v: k for k, v in FORMATS.items()}
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q1_0: 128}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q1_0: 18}
 
 # scale distributions (fp64 uniform draws, rounded to fp16 by numpy)
 D_RANGE = (1e-3, 2e-2)
@@ -70,6 +71,9 @@ def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
         out[:, 0:2] = _f16_field(gs, nblk, *d_range)   # d
         out[:, 2:4] = _f16_field(gs, nblk, *d_range)   # dmin
         out[:, 4:176] = gq.integers(0, 256, size=(nblk, 172), dtype=np.uint8)  # scales, qh, qs
+    elif fmt == Q1_0:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)
+        out[:, 2:18] = gq.integers(0, 256, size=(nblk, 16), dtype=np.uint8)   # sign bits
     elif fmt == Q6_K:
         # ql[128], qh[64], 16 signed scale bytes: uniform random bytes;
         # d (fp16) last
@@ -111,6 +115,9 @@ CONFIGS = {
     "q8_0_gemv_ffn_up": dict(cfg=1, kind="gemv", fmt=Q8_0, n=14336, k=4096, batches=(1, 5)),
     "q4_1_gemv_ffn_up": dict(cfg=11, kind="gemv", fmt=Q4_1, n=14336, k=4096, batches=(1, 5)),
     "q4_k_gemv_lm_head": dict(cfg=2, kind="gemv", fmt=Q4_K, n=128256, k=4096, batches=(1, 4)),
+    # Q1_0 binary weights: the largest matvec of a 27B Q1_0 model
+    # (attention QKV 10240 x 5120) at batch 1 and 4
+    "q1_0_gemv_qkv": dict(cfg=41, kind="gemv", fmt=Q1_0, n=10240, k=5120, batches=(1, 4)),
     # the tied-embedding LM head in Q6_K
     "q6_k_gemv_lm_head": dict(cfg=22, kind="gemv", fmt=Q6_K, n=128256, k=4096, batches=(1, 4)),
     # Q5_K (the FFN type of Q5_K_M models): decode GEMV and prefill GEMM

@@ -82,6 +82,7 @@ int64_t elems_of(int type) {
     switch (type) {
         case ORACLE_Q4_0: case ORACLE_Q4_1: case ORACLE_Q8_0: return 32;
         case ORACLE_Q4_K: case ORACLE_Q5_K: case ORACLE_Q6_K: return 256;
+        case ORACLE_Q1_0: return 128;
         default: return -1;
     }
 }
@@ -93,6 +94,7 @@ int64_t bytes_of(int type) {
         case ORACLE_Q8_0: return 34;   /* fp16 d + 32 int8 [alice-QBS]    */
         case ORACLE_Q4_K: return 144;  /* 2 + 2 + 12 + 128 [alice-QBS]    */
         case ORACLE_Q5_K: return 176;  /* 2 + 2 + 12 + 32 + 128 [alice-Q5K] */
+        case ORACLE_Q1_0: return 18;   /* 2 + 16 [alice-Q10]              */
         case ORACLE_Q6_K: return 210;  /* 128 + 64 + 16 + 2 [alice-Q6K]   */
         default: return -1;
     }
@@ -156,6 +158,11 @@ void decode_block(int type, const uint8_t* b, double* out) {
                 out[i]      = d * (b[4 + i] & 0x0F) + m;
                 out[i + 16] = d * (b[4 + i] >> 4) + m;
             }
+            break;
+        }
+        case ORACLE_Q1_0: {
+            const double d = half_value(rd16(b));
+            for (int i = 0; i < 128; ++i) out[i] = ((b[2 + i / 8] >> (i % 8)) & 1) ? d : -d;
             break;
         }
         case ORACLE_Q8_0: {
@@ -305,6 +312,24 @@ double factored_dot(int type, const uint8_t* wrow, const uint8_t* xrow, int64_t 
                 /* d*dx*sc*sum(q*qx) - dmin*dx*m*sum(qx) [alice-Q4K] */
                 acc += d * dx * sc * static_cast<double>(idot32(q, xq)) -
                        dmin * dx * mn * static_cast<double>(isum32(xq));
+            }
+        }
+        return acc;
+    }
+    if (type == ORACLE_Q1_0) {
+        /* per 32-value activation block: d*dx*sum(s*qx), s = +-1 [alice-Q10] */
+        for (int64_t blk = 0; blk < k / 128; ++blk) {
+            const uint8_t* b = wrow + blk * 18;
+            const double d = half_value(rd16(b));
+            for (int j = 0; j < 4; ++j) {
+                int s[32];
+                for (int i = 0; i < 32; ++i) {
+                    const int e = 32 * j + i;
+                    s[i] = ((b[2 + e / 8] >> (e % 8)) & 1) ? 1 : -1;
+                }
+                const uint8_t* xb = xrow + (blk * 4 + j) * 34;
+                const double dx = half_value(rd16(xb));
+                acc += d * dx * static_cast<double>(idot32(s, reinterpret_cast<const int8_t*>(xb + 2)));
             }
         }
         return acc;

@@ -36,6 +36,9 @@
  *                 the device reads a few bytes instead of the full logits.
  *   [cera-R]      Cera README, "Supported models": lfm2moe routes each token
  *                 to its own 4 of 32 experts.
+ *   [alice-Q10]   alice-llm 2.0.0 README, "Bonsai 27B" notes: Q1_0 packs 128
+ *                 values in 18 bytes, an fp16 scale d then 16 bytes of 1-bit
+ *                 weights, each value +d or -d (1.125 bits per weight).
  *   [alice-Q5K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
  *                 a Q5_K super-block is 176 bytes for 256 values (5.5 bpw),
  *                 fields d (fp16), dmin (fp16), scales[12], qh[32], qs[128].
@@ -55,6 +58,8 @@
  *     (see oracle_q4k_scale_min); qs chunk c (32 bytes) holds sub-block 2c
  *     in low nibbles and sub-block 2c+1 in high nibbles.  Value
  *     d*sc*q - dmin*m.
+ *   - Q1_0: value i of the block is bit (i % 8) of byte 2 + i/8 (least
+ *     significant bit first); a set bit is +d, a clear bit -d.
  *   - Q5_K: d, dmin and the 12 scale bytes as in Q4_K (same six-bit
  *     scale/min packing); qs chunk c (32 bytes) holds the low four bits of
  *     sub-block 2c in low nibbles and of sub-block 2c+1 in high nibbles, as
@@ -96,6 +101,7 @@ enum {
     ORACLE_Q8_0 = 8,
     ORACLE_Q4_K = 12,
     ORACLE_Q5_K = 13,
+    ORACLE_Q1_0 = 41,   /* library-assigned id (the pages give no GGUF type id) */
     ORACLE_Q6_K = 14
 };
 

@@ -47,6 +47,9 @@ def test_block_sizes_match_pages(orc):
     # 5.5 bits per weight, same table
     assert (orc.block_elems(orc.Q5_K), orc.block_bytes(orc.Q5_K)) == (256, 176)
     assert 2 + 2 + 12 + 32 + 128 == 176 and 176 * 8 / 256 == 5.5
+    # Q1_0 (Bonsai notes): 128 values in 18 bytes, 1.125 bits per weight
+    assert (orc.block_elems(orc.Q1_0), orc.block_bytes(orc.Q1_0)) == (128, 18)
+    assert 18 * 8 / 128 == 1.125
     assert orc.block_bytes(99) == -1
 
 
@@ -316,7 +319,7 @@ def test_q4k_subblock_equals_q4_1(orc):
     assert np.array_equal(yk, y1)
 
 
-@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K])
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0])
 def test_two_formulations_agree(orc, fmt):
     n, m, k = 33, 5, 1024
     w = gs.weights(fmt, n, k, cfg=914)
@@ -331,7 +334,8 @@ def test_two_formulations_agree(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt,k", [(gs.Q4_0, 32), (gs.Q4_1, 64), (gs.Q8_0, 96), (gs.Q4_K, 256),
-                                   (gs.Q4_K, 512), (gs.Q5_K, 256), (gs.Q6_K, 256)])
+                                   (gs.Q4_K, 512), (gs.Q5_K, 256), (gs.Q6_K, 256),
+                                   (gs.Q1_0, 128), (gs.Q1_0, 384)])
 def test_exact_rational_brute_force(orc, fmt, k):
     """Tiny shapes in exact rational arithmetic: the fp64 sums must agree
     with the exact value to within the fp64 summation bound."""
@@ -673,3 +677,48 @@ def test_router_closed_forms(orc):
     idsf, wf = orc.topk_softmax(logits[2:3], 8)
     e = np.exp(np.arange(8)[::-1] - 7.0)
     assert np.allclose(wf[0], e / e.sum(), rtol=1e-7)
+
+
+# ------------------------------------------------------------------- Q1_0
+# alice-llm 2.0.0 README, Bonsai notes: 128-value blocks of 18 bytes, fp16 d
+# then 16 bytes of 1-bit weights, value +d or -d.  Reading: value i is bit
+# i % 8 of byte 2 + i/8 (LSB first), set = +d.
+
+def _q10_block(d, bits):
+    b = np.zeros(18, np.uint8)
+    b[0:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+    b[2:18] = bits
+    return b
+
+
+def test_q1_0_all_set_and_clear(orc):
+    assert np.all(orc.dequantize(gs.Q1_0, _q10_block(0.5, np.full(16, 255, np.uint8)), 128) == 0.5)
+    assert np.all(orc.dequantize(gs.Q1_0, _q10_block(0.5, np.zeros(16, np.uint8)), 128) == -0.5)
+
+
+def test_q1_0_one_hot_bits(orc):
+    """Setting bit b of sign byte m turns exactly value 8m + b from -d to +d."""
+    base = orc.dequantize(gs.Q1_0, _q10_block(2.0, np.zeros(16, np.uint8)), 128)
+    for m, b in [(0, 0), (0, 7), (3, 1), (8, 4), (15, 7)]:
+        bits = np.zeros(16, np.uint8)
+        bits[m] = 1 << b
+        v = orc.dequantize(gs.Q1_0, _q10_block(2.0, bits), 128)
+        diff = np.flatnonzero(v != base)
+        assert diff.tolist() == [8 * m + b] and v[8 * m + b] == 2.0
+
+
+def test_q1_0_equals_q8_0_of_signs(orc):
+    """A Q1_0 row equals the Q8_0 row with the same d and quants +-1, built
+    in the test from the sign bits (exact in fp64)."""
+    n, k = 3, 512
+    w1 = gs.weights(gs.Q1_0, n, k, cfg=940).reshape(-1, 18)
+    w8 = np.zeros((w1.shape[0] * 4, 34), np.uint8)
+    for b in range(w1.shape[0]):
+        signs = np.unpackbits(w1[b, 2:18], bitorder="little").astype(np.int8) * 2 - 1
+        for j in range(4):
+            w8[4 * b + j, 0:2] = w1[b, 0:2]
+            w8[4 * b + j, 2:34] = signs[32 * j: 32 * j + 32].view(np.uint8)
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=940))
+    y1, _ = orc.matmul(gs.Q1_0, w1.reshape(n, -1), n, k, xq, 2)
+    y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
+    assert np.array_equal(y1, y8)
