@@ -270,7 +270,8 @@ def secondary(cq, gs, dev, stream):
     (weights rotated through >= 512 MB of copies where they would fit the
     Infinity Cache): the 128K-vocabulary LM head (Q4_K, and Q6_K as for a
     tied embedding) at batch 1 and 4, the Q5_K FFN-up GEMV at batch 1 and 5,
-    the fused Q4_K gate/up/SwiGLU GEMV against the separate kernels,
+    the fused Q4_K gate/up/SwiGLU GEMV against the separate kernels, the Q1_0
+    10240 x 5120 matvec at batch 1 and 4,
     the 2048 x 2048 Q4_0 GEMV, the Q4_0 prefill GEMM at 512 and 2048 tokens,
     the Q5_K and Q6_K prefill GEMMs at 512 tokens, the greedy arg-max over
     the LM-head logits, the router, the whole routed FFN, and one decode
@@ -349,6 +350,20 @@ def secondary(cq, gs, dev, stream):
             "fused_weight_GB/s": round(wb / us_f / 1e3, 1),
             "fused_pct_hbm_peak": round(100 * wb / us_f / 1e3 / HBM_PEAK_GBS, 1)}
     del wgt, wup
+    # Q1_0 attention QKV matvec 10240 x 5120 (the pages' Q1_0 micro-benchmark
+    # shape, 5.9 MB of weights), batch 1 and 4, weights rotated through copies
+    c1 = gs.CONFIGS["q1_0_gemv_qkv"]
+    n1, k1 = c1["n"], c1["k"]
+    w1 = copies(gs.weights(gs.Q1_0, n1, k1, cfg=c1["cfg"]), 256 * 2**20)
+    xq1 = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(4, k1, cfg=c1["cfg"])).to(dev))
+    y1q = torch.empty((4, n1), dtype=torch.float32, device=dev)
+    for b in (1, 4):
+        fn = (lambda i, b=b: cq.cq_gemv(gs.Q1_0, w1[i % len(w1)], n1, k1, xq1, b, y=y1q))
+        us = _graph_us(fn, len(w1), 5, stream)
+        gbs = w1[0].numel() / us / 1e3
+        out[f"q1_0_gemv_10240x5120_b{b}"] = {"graph_us": round(us, 2), "GB/s": round(gbs, 1),
+                                             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    del w1
     # 2048 x 2048 Q4_0 GEMV (2.36 MB per call: launch-latency bound)
     n, k = 2048, 2048
     w0 = copies(gs.weights(gs.Q4_0, n, k, cfg=0))

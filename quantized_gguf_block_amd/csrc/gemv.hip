@@ -35,16 +35,19 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_Q1_0 = 41 };
 
 // Q4_K and Q5_K share the super-block header (d, dmin, 6-bit scales and
 // mins) and the nibble chunks; Q5_K adds one high bit per value from qh.
 template <int FMT> constexpr bool kK45 = (FMT == T_Q4_K || FMT == T_Q5_K);
 // super-block formats: a lane column spans 64 values
 template <int FMT> constexpr bool kSuper = kK45<FMT> || FMT == T_Q6_K;
+// one column per lane (no two-column streaming instantiation)
+template <int FMT> constexpr bool kOneCol = kSuper<FMT> || FMT == T_Q1_0;
 
-// columns per lane: a super-block column already spans 64 values
-template <int FMT> constexpr int kCMax = kSuper<FMT> ? 1 : 2;
+// columns per lane: a super-block column already spans 64 values, and a
+// Q1_0 column (64 values, 9 bytes) carries two activation blocks, so one
+template <int FMT> constexpr int kCMax = kOneCol<FMT> ? 1 : 2;
 constexpr int kMaxThreads = 512;    // 8 waves
 
 // bytes per block of the 32-value formats
@@ -82,6 +85,15 @@ template <> struct Act<T_Q4_K> {
     float sa, sb;           // dx * sum(q) of each block
 };
 template <> struct Act<T_Q5_K> : Act<T_Q4_K> {};
+
+// Q1_0 column (64 values): half col & 1 of block col >> 1, i.e. Q8_0
+// activation blocks 2 col and 2 col + 1.
+template <> struct Act<T_Q1_0> {
+    uint32_t q[2][8];
+    float dx[2];
+    float ndx[2];      // -12582912 * dx
+    int start[2];      // kBias - sum(q): start of the dot with the 0/2 sign bytes
+};
 
 // Q6_K column (64 values): half h of super-block sb, l in [16 i, 16 i + 16)
 // of each of the four 32-value quadrants g; quadrant g of the half is Q8_0
@@ -175,6 +187,17 @@ __device__ __forceinline__ void load_act<T_Q5_K>(const uint8_t* xq_row, int col,
 }
 
 template <>
+__device__ __forceinline__ void load_act<T_Q1_0>(const uint8_t* xq_row, int col, Act<T_Q1_0>& a) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int sum;
+        load_q8(xq_row + static_cast<int64_t>(2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
+        a.start[j] = kBias - sum;
+        a.ndx[j] = -kBiasF * a.dx[j];
+    }
+}
+
+template <>
 __device__ __forceinline__ void load_act<T_Q6_K>(const uint8_t* xq_row, int col, Act<T_Q6_K>& a) {
     const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
 #pragma unroll
@@ -201,6 +224,7 @@ __device__ __forceinline__ int col_offset(int row_base, int col) {
     if constexpr (FMT == T_Q4_K) return row_base + (col >> 2) * 144;
     else if constexpr (FMT == T_Q5_K) return row_base + (col >> 2) * 176;
     else if constexpr (FMT == T_Q6_K) return row_base + (col >> 2) * 210;
+    else if constexpr (FMT == T_Q1_0) return row_base + (col >> 1) * 18;
     else return row_base + col * Fmt<FMT>::BS;
 }
 
@@ -292,6 +316,33 @@ __device__ __forceinline__ void chunk_dot_k45(const uint32_t* hdr, const uint32_
     }
 }
 
+// acc[j] += one Q1_0 column (see Act<T_Q1_0>) of the block at LDS byte
+// offset off (2-byte aligned): the 32 sign bits of each activation block
+// become bytes 0 or 2 (4 bits per multiply), so the dot chain from
+// kBias - sum(qx) ends at kBias + sum(+-qx); then dx, then d.
+template <int B>
+__device__ __forceinline__ void q10_column_dot(const uint8_t* lds, int off, int col,
+                                               const Act<T_Q1_0>* a, float* acc) {
+    const float d = h2f(lds_u16(lds, off));
+    uint32_t bits[2];
+    lds_dwords_a2<2>(lds, off + 2 + 8 * (col & 1), bits);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint32_t e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            e[t] = (__builtin_amdgcn_ubfe(bits[j], 4 * t, 4) * 0x00408102u) & 0x02020202u;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            int s = a[b].start[j];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) s = sdot4(e[t], a[b].q[j][t], s);
+            const float sx = fmaf(__int_as_float(s), a[b].dx[j], a[b].ndx[j]);
+            acc[b] = fmaf(sx, d, acc[b]);
+        }
+    }
+}
+
 // acc[j] += dot of one column of one weight row with activation row j.
 template <int FMT, int B>
 __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Act<FMT>* a,
@@ -365,6 +416,8 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         }
     } else if constexpr (FMT == T_Q6_K) {
         q6k_column_dot<B>(lds, off, col, a, acc);
+    } else if constexpr (FMT == T_Q1_0) {
+        q10_column_dot<B>(lds, off, col, a, acc);
     } else if constexpr (FMT == T_Q5_K) {  // chunk c, its 32 qh bytes at off + 16
         const int c = col & 3;
         const uint4 h4 = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
@@ -670,6 +723,10 @@ template <int C> struct Win<T_Q5_K, C> {
     static constexpr bool kMis = false;
     static constexpr int NDW = 12 + 8 * C;                 // header + qh + C nibble chunks
 };
+template <int C> struct Win<T_Q1_0, C> {                 // (reads LDS directly)
+    static constexpr bool kMis = false;
+    static constexpr int NDW = 1;
+};
 template <int C> struct Win<T_Q6_K, C> {                 // (reads LDS directly)
     static constexpr bool kMis = false;
     static constexpr int NDW = 1;
@@ -748,6 +805,7 @@ template <int FMT> constexpr int col_bytes() {
     if constexpr (FMT == T_Q4_K) return 36;
     else if constexpr (FMT == T_Q5_K) return 44;
     else if constexpr (FMT == T_Q6_K) return 53;
+    else if constexpr (FMT == T_Q1_0) return 9;
     else return Fmt<FMT>::BS;
 }
 
@@ -755,7 +813,7 @@ constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per 
 
 // Largest activation bytes (all batch rows) one streaming workgroup stages.
 template <int FMT, int B, int C>
-constexpr int kActMax = B * (kSuper<FMT> ? 128 : 64) * C * 34;
+constexpr int kActMax = B * (kSuper<FMT> || FMT == T_Q1_0 ? 128 : 64) * C * 34;
 
 // Routed-expert addressing for decode (MOE): blockIdx.y is the
 // token-expert pair p = t*top_k + s; its matrix is expert ids[p] (clamped
@@ -796,7 +854,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
     // read consecutive words (no bank conflicts).  A slot is one Q8_0 block
     // (Q6_K: the 16 values of one quadrant that the column covers).
-    constexpr int NS = kK45<FMT> ? 2 : FMT == T_Q6_K ? 4 : 1;      // slots per column
+    constexpr int NS = (kK45<FMT> || FMT == T_Q1_0) ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
     constexpr int NP = kWave * C;                                  // column positions per row
     constexpr int NBMAX = B * NS * NP;                             // slots, all rows
     constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
@@ -830,6 +888,9 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     } else if constexpr (FMT == T_Q6_K) {
         c0 = valid ? C * lane : 0;               // the column
         off = (c0 >> 2) * 210;
+    } else if constexpr (FMT == T_Q1_0) {
+        c0 = valid ? C * lane : 0;               // first column; block c0 / 2
+        off = (c0 >> 1) * 18;
     } else {
         off = valid ? C * lane * Fmt<FMT>::BS : 0;
     }
@@ -917,7 +978,8 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     int sum = 0;
 #pragma unroll
                     for (int u = 0; u < 8; ++u) sum = sdot4(q[u], 0x01010101u, sum);
-                    xau[gi] = FMT == T_Q4_0 ? __int_as_float(sum) : dx * static_cast<float>(sum);
+                    xau[gi] = (FMT == T_Q4_0 || FMT == T_Q1_0) ? __int_as_float(sum)
+                                                               : dx * static_cast<float>(sum);
                 }
             }
         }
@@ -929,7 +991,19 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     for (int i = 0; i < C; ++i)
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            if constexpr (FMT == T_Q6_K) {
+            if constexpr (FMT == T_Q1_0) {
+                Act<T_Q1_0>& a = act[i][j];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int gi = (j * NS + h) * NP + kWave * i + lane;
+                    const u32x4 q0 = xq0[gi], q1 = xq1[gi];
+                    a.q[h][0] = q0.x; a.q[h][1] = q0.y; a.q[h][2] = q0.z; a.q[h][3] = q0.w;
+                    a.q[h][4] = q1.x; a.q[h][5] = q1.y; a.q[h][6] = q1.z; a.q[h][7] = q1.w;
+                    a.dx[h] = xda[gi];
+                    a.ndx[h] = -kBiasF * a.dx[h];
+                    a.start[h] = kBias - __float_as_int(xau[gi]);
+                }
+            } else if constexpr (FMT == T_Q6_K) {
                 Act<T_Q6_K>& a = act[i][j];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -1004,6 +1078,10 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             if constexpr (FMT == T_Q6_K) {
                 static_assert(C == 1, "one Q6_K column per lane");
                 q6k_column_dot<B>(stage, off, c0, act[0], acc[i]);
+            } else if constexpr (FMT == T_Q1_0) {
+#pragma unroll
+                for (int cc = 0; cc < C; ++cc)
+                    q10_column_dot<B>(stage, ((c0 + cc) >> 1) * 18, c0 + cc, act[cc], acc[i]);
             } else if constexpr (kK45<FMT>) {
                 // header (and Q5_K's 32 qh bytes), then the C nibble chunks
                 constexpr int NH = FMT == T_Q4_K ? 1 : 3;
@@ -1028,7 +1106,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     v[W::NDW - 1] >>= mis;
                 }
             }
-            if constexpr (FMT != T_Q6_K) row_dot<FMT, B, C>(v, act, c0, acc[i]);
+            if constexpr (FMT != T_Q6_K && FMT != T_Q1_0) row_dot<FMT, B, C>(v, act, c0, acc[i]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1056,8 +1134,8 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     const int64_t xrb = k / 32 * 34;
     Plan p{};
     const bool super = wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K;
-    p.ncols = static_cast<int>(super ? k / 64 : k / 32);
-    p.C = (super || p.ncols <= kWave) ? 1 : 2;
+    p.ncols = static_cast<int>(super || wt == T_Q1_0 ? k / 64 : k / 32);   // Q1_0: half blocks
+    p.C = (super || wt == T_Q1_0 || p.ncols <= kWave) ? 1 : 2;
     p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
     // general kernel: about 16 KiB of weights per tile, at most 32 live
     // accumulators per lane
@@ -1073,7 +1151,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     // one (type, k) must take the same kernel)
     const int sc = (p.ncols + kWave - 1) / kWave;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !(super && sc == 2))
+        !((super || wt == T_Q1_0) && sc == 2))
         p.SC = sc;
     return p;
 }
@@ -1115,7 +1193,7 @@ template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
     if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
-    if constexpr (!kSuper<FMT>)  // (one column per lane for the super-block formats)
+    if constexpr (!kOneCol<FMT>)  // (one column per lane for the super-block formats, Q1_0)
         if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
@@ -1157,10 +1235,12 @@ int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb
 }
 
 int64_t block_bytes_of(int wt) {
-    return wt == T_Q4_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34 : wt == T_Q4_K ? 144
-           : wt == T_Q5_K ? 176 : 210;
+    return wt == T_Q4_0 || wt == T_Q1_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34
+           : wt == T_Q4_K ? 144 : wt == T_Q5_K ? 176 : 210;
 }
-int64_t block_elems_of(int wt) { return wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : 32; }
+int64_t block_elems_of(int wt) {
+    return wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : wt == T_Q1_0 ? 128 : 32;
+}
 
 }  // namespace
 
@@ -1193,6 +1273,7 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q4_K: return launch_fmt<T_Q4_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q5_K: return launch_fmt<T_Q5_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q6_K: return launch_fmt<T_Q6_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_Q1_0: return launch_fmt<T_Q1_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         default: return -2;
     }
 }
@@ -1212,7 +1293,7 @@ template <int FMT, int B>
 int launch_sw_b(int SC, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb, int ncols,
                 const uint8_t* xq, int64_t xrb, float* h, int64_t ldh, hipStream_t stream) {
     if (SC == 1) return launch_stream<FMT, B, 1, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
-    if constexpr (!kSuper<FMT>)
+    if constexpr (!kOneCol<FMT>)
         if (SC == 2) return launch_stream<FMT, B, 2, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
     return -3;
 }
@@ -1249,6 +1330,7 @@ int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, 
         case T_Q4_K: return launch_sw<T_Q4_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         case T_Q5_K: return launch_sw<T_Q5_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q1_0: return launch_sw<T_Q1_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         default: return -2;
     }
 }
@@ -1266,7 +1348,7 @@ int launch_moe_gemv_fmt(int SC, const uint8_t* w, const uint8_t* w2, int64_t n, 
                         int ncols, const uint8_t* xq, int64_t xrb, float* y, int64_t ldy,
                         const MoeMap& mm, int npairs, hipStream_t s) {
     if (SC == 1) return launch_stream<FMT, 1, 1, SW, true>(w, n, rb, ncols, xq, xrb, y, ldy, s, w2, mm, npairs);
-    if constexpr (!kSuper<FMT>)
+    if constexpr (!kOneCol<FMT>)
         if (SC == 2) return launch_stream<FMT, 1, 2, SW, true>(w, n, rb, ncols, xq, xrb, y, ldy, s, w2, mm, npairs);
     return -3;
 }
@@ -1292,6 +1374,7 @@ int launch_moe_gemv_any(int wt, const void* w, const void* w2, int64_t n_experts
         case T_Q4_K: return launch_moe_gemv_fmt<T_Q4_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         case T_Q5_K: return launch_moe_gemv_fmt<T_Q5_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         case T_Q6_K: return launch_moe_gemv_fmt<T_Q6_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_Q1_0: return launch_moe_gemv_fmt<T_Q1_0, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         default: return -2;
     }
 }

@@ -46,6 +46,7 @@ def test_block_geometry(lib):
     assert [lib.cq_block_elems(t) for t in (2, 3, 8, 12, 13, 14)] == [32, 32, 32, 256, 256, 256]
     assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12, 13, 14)] == [18, 20, 34, 144, 176, 210]
     assert lib.cq_row_bytes(13, 4096) == 2816
+    assert (lib.cq_block_elems(41), lib.cq_block_bytes(41), lib.cq_row_bytes(41, 5120)) == (128, 18, 720)
     assert lib.cq_row_bytes(14, 4096) == 3360
     assert lib.cq_row_bytes(12, 4096) == 2304
     assert lib.cq_row_bytes(8, 4096) == 4352
@@ -146,6 +147,7 @@ def test_gemm_validation(lib):
     assert f(2, P(FAKE), 8, 256, None, 0, None, 8, None) == OK             # m == 0
     assert f(5, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
     assert f(7, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
+    assert f(41, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED  # Q1_0: GEMV only
     # Q6_K rows are read with 31-bit offsets: a matrix of 2 GiB or more is refused
     assert f(14, P(FAKE), 1 << 20, 2560, P(FAKE), 4, P(FAKE), 1 << 20, None) == SHAPE
 

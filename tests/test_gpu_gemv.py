@@ -13,7 +13,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0]
 
 
 def run_gemv(cq, fmt, w, n, k, xq, batch):
@@ -45,7 +45,7 @@ def config_inputs(name):
 
 
 @pytest.mark.parametrize("name", ["q4_0_gemv_2048", "q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up",
-                                  "q5_k_gemv_ffn_up"])
+                                  "q5_k_gemv_ffn_up", "q1_0_gemv_qkv"])
 def test_gemv_config_full(cq, orc, name):
     c, w, x = config_inputs(name)
     xq = orc.quantize_q8_0(x)
