@@ -96,6 +96,7 @@ typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q5_K = 13
 #define CQ_ABI_VERSION 1
 #define CQ_GEMV_MAX_BATCH 8
 #define CQ_MAX_K 65536
+#define CQ_GEMV_MAX_K 32768   /* cq_gemv: up to 8 waves of 64 lanes per row */
 
 int cq_abi_version(void);
 /* Static, never-null string naming a status code. */
@@ -136,7 +137,7 @@ int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k,
  *   batch  1..CQ_GEMV_MAX_BATCH.
  *   y      fp32, row b at y + b*ldy, ldy >= n, 4-byte aligned.
  *   k      multiple of 32 (of 256 for Q4_K, Q5_K and Q6_K; of 128 for Q1_0),
- *          k <= CQ_MAX_K.
+ *          k <= CQ_GEMV_MAX_K (a longer row returns CQ_ERR_SHAPE).
  * Each row b of a batched call is bitwise equal to the batch-1 call on that
  * row alone.  Accuracy: |y - y_exact| <= 2e-5 * sum_j |w_hat*x_hat|.
  */

@@ -125,7 +125,7 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t
             float* y, int64_t ldy, cq_stream_t stream) {
     if (int rc = check_weights(wt, w, n, k)) return rc;
     if (batch < 1 || batch > CQ_GEMV_MAX_BATCH || ldy < n) return CQ_ERR_INVALID_ARG;
-    if (gemv_shape_ok(wt, k, batch) != 0) return CQ_ERR_SHAPE;
+    if (k > CQ_GEMV_MAX_K || gemv_shape_ok(wt, k, batch) != 0) return CQ_ERR_SHAPE;
     if (n == 0) return CQ_OK;
     if (!xq || !y) return CQ_ERR_INVALID_ARG;
     if (!aligned(xq, 2) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;

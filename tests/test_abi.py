@@ -85,6 +85,7 @@ def test_gemv_validation(lib):
     assert f(2, None, 8, 256, P(FAKE), 1, P(FAKE), 8, None) == INVALID
     assert f(2, None, 0, 256, None, 1, None, 0, None) == OK              # n == 0
     assert f(8, P(FAKE), -1, 256, P(FAKE), 1, P(FAKE), 8, None) == INVALID
+    assert f(8, P(FAKE), 8, 32768 + 256, P(FAKE), 1, P(FAKE), 8, None) == SHAPE  # > CQ_GEMV_MAX_K
 
 
 def test_gemv_swiglu_validation(lib):

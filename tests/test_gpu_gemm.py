@@ -100,3 +100,15 @@ def test_gemm_strided_output(cq, orc):
     y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, m)
     assert_close_to_oracle(yh[:, :n], y_ref, s_ref, what="strided")
     assert np.all(yh[:, n:] == -3.0)
+
+
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q6_K], ids=lambda f: gs.NAMES[f])
+def test_gemm_max_k(cq, orc, fmt):
+    """k = CQ_MAX_K (65536) with ragged m and n."""
+    m, n, k = 19, 130, 65536
+    w = gs.weights(fmt, n, k, cfg=620)
+    xq = orc.quantize_q8_0(gs.activations(m, k, cfg=620))
+    note("gemm max k", gs.NAMES[fmt])
+    y = to_host(cq.cq_gemm(fmt, to_dev(w), n, k, to_dev(xq), m))
+    y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, m)
+    assert_close_to_oracle(y, y_ref, s_ref, what="gemm max k")

@@ -151,3 +151,24 @@ def test_gemv_zero_weights_exact(cq, orc):
     note("gemv zero weights")
     y = run_gemv(cq, gs.Q4_0, w, 64, k, xq, 2)
     assert not y.any()
+
+
+@pytest.mark.parametrize("fmt", [gs.Q8_0, gs.Q4_K, gs.Q6_K, gs.Q1_0], ids=lambda f: gs.NAMES[f])
+def test_gemv_max_k(cq, orc, fmt):
+    """k = CQ_GEMV_MAX_K (32768): the multi-wave kernel at its largest row
+    (8 waves), with a ragged row count, at batch 1 and 8; one block more per
+    row is refused."""
+    n, k = 33, 32768
+    w = gs.weights(fmt, n, k, cfg=310)
+    xq = orc.quantize_q8_0(gs.activations(8, k, cfg=310))
+    y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, 8)
+    wd, xd = to_dev(w), to_dev(xq)
+    for batch in (1, 8):
+        note("gemv max k", gs.NAMES[fmt], batch)
+        y = to_host(cq.cq_gemv(fmt, wd, n, k, xd[:batch], batch))
+        assert_close_to_oracle(y, y_ref[:batch], s_ref[:batch], what=f"max k b{batch}")
+    k2 = k + gs.BLOCK_ELEMS[fmt] * (256 // gs.BLOCK_ELEMS[fmt] if gs.BLOCK_ELEMS[fmt] < 256 else 1)
+    w2 = to_dev(gs.weights(fmt, 2, k2, cfg=311))
+    x2 = to_dev(orc.quantize_q8_0(gs.activations(1, k2, cfg=311)))
+    with pytest.raises(RuntimeError, match="SHAPE"):
+        cq.cq_gemv(fmt, w2, 2, k2, x2, 1)
