@@ -189,3 +189,21 @@ def test_moe_gemm_other_formats(cq, orc, fmt, n_tokens, n_experts, top_k, n, k):
                                    to_dev(offs), to_dev(pairs), n_tokens, top_k))
         y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
         assert_close_to_oracle(y, y_ref, s_ref, what=f"moe {gs.NAMES[fmt]}")
+
+
+@pytest.mark.parametrize("fmt", [gs.Q4_K, gs.Q8_0], ids=lambda f: gs.NAMES[f])
+def test_moe_gemm_max_k(cq, orc, fmt):
+    """k = CQ_MAX_K (65536): the streaming Q4_K kernel and the tile engine at
+    their longest rows, per-token and per-pair activation rows."""
+    n_tokens, n_experts, top_k, n, k = 9, 4, 2, 70, 65536
+    w = gs.expert_weights(fmt, n_experts, n, k, cfg=730, which=0)
+    ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=730)
+    offs, pairs = orc.moe_group(ids, n_experts)
+    for x_per_pair in (False, True):
+        rows = n_tokens * top_k if x_per_pair else n_tokens
+        xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=731))
+        note("moe gemm max k", gs.NAMES[fmt], x_per_pair)
+        y = to_host(cq.cq_moe_gemm(fmt, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
+                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
+        assert_close_to_oracle(y, y_ref, s_ref, what=f"moe max k {gs.NAMES[fmt]}")

@@ -14,7 +14,7 @@ def q8(cq, x):
 
 
 @pytest.mark.parametrize("rows,k", [(1, 2048), (5, 4096), (4, 4096), (3, 32), (7, 96),
-                                    (512, 4096), (2048, 4096), (256, 2048)])
+                                    (512, 4096), (2048, 4096), (256, 2048), (2, 65536)])
 def test_quantize_bit_exact(cq, orc, rows, k):
     note("quantize", rows, k)
     x = gs.activations(rows, k, cfg=100 + rows)
