@@ -8,8 +8,10 @@
 //
 // Tiling: a 256-thread workgroup owns 128 tokens x 128 weight rows and walks
 // k in steps of 4 blocks (128 values).  Per step the weight blocks are
-// decoded once into signed int8 rows in LDS (Q4_0: q-8, Q4_1 / Q4_K: q) and
-// the Q8_0 activation blocks are split into int8 rows plus fp32 scales.
+// decoded once into signed int8 rows in LDS (Q4_0: q-8, Q4_1 / Q4_K: q,
+// Q5_K: q with its qh bit, Q6_K: q-32) and the Q8_0 activation blocks are
+// split into int8 rows plus fp32 scales.  Q6_K's 16-value scale groups take
+// one v_mfma_i32_32x32x16_i8 each (two rescales per 32 values).
 // Each wave computes 64 x 64 outputs as 2 x 2 tiles of
 // v_mfma_i32_32x32x32_i8: one MFMA is exactly one 32-value block.
 //

@@ -1,5 +1,7 @@
-// gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K, Q6_K)
-// for 1..8 Q8_0 activation rows.
+// gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K,
+// Q6_K, Q1_0) for 1..8 Q8_0 activation rows; the same streaming kernel also
+// runs the fused gate/up + SwiGLU GEMV and the per-pair routed-expert GEMVs
+// of decode.
 //
 // Streaming kernel (HBM-bound; the weights are read exactly once):
 //  * A wave owns a contiguous range of rows.  Every row is loaded with
@@ -9,8 +11,9 @@
 //    back, a row is one contiguous byte range whatever the 18/20/34/144-byte
 //    block size; it is staged in a wave-private LDS buffer and each lane
 //    re-slices its own blocks out of it.
-//  * Each lane owns fixed "columns" of K (one or two 32-value blocks, or for
-//    Q4_K one 32-byte nibble chunk = two 32-value sub-blocks) and keeps the
+//  * Each lane owns fixed "columns" of K (one or two 32-value blocks; for
+//    Q4_K / Q5_K one 32-byte nibble chunk = two 32-value sub-blocks; for
+//    Q6_K a 64-value quarter super-block; for Q1_0 half a block) and keeps the
 //    Q8_0 activation of its columns, for all batch rows, in registers.  The
 //    activations are copied once per workgroup into LDS with coalesced
 //    loads and unpacked from there.
@@ -25,6 +28,10 @@
 //    shared-memory tree), then stored with one instruction.
 //  * The column split depends only on (type, k), never on the batch size, so
 //    batch row b gives bitwise the batch-1 result.
+//  * Fused modes (template flags): SW walks the gate and up rows of each
+//    output in turn and stores silu(gate)*up after the reduction; MOE makes
+//    grid.y a token-expert pair whose expert id, activation row and output
+//    row offset the pointers at kernel start.
 // Shapes the streaming kernel does not cover (more than two columns per
 // lane, rows that are not whole 16-byte pieces, unaligned activations) use
 // the general kernel: several waves per row, cooperative staging of row
