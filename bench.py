@@ -173,7 +173,7 @@ def main():
     alg = wbytes[gs.Q8_0] + B * (k // 32 * 34) + B * n * 4
     achieved = alg / (burst_ms * 1e-3) / 1e9
 
-    traffic, prof_us = profiled("gemv_stream_kernel<8, 5, 2, 4, false, false>")
+    traffic, prof_us = profiled("gemv_stream_kernel<8, 5, 2, 4, false, false, 1>")
 
     extra = None if args.no_extra else secondary(cq, gs, dev, stream)
 
@@ -199,7 +199,7 @@ def main():
                    "n": n, "k": k, "batches": [1, B], "formats": ["q8_0", "q4_1"],
                    "weight_copies": {gs.NAMES[f]: len(copies[f]) for f in fmts}},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel<8, 5, 2, 4, false, false> (Q8_0, batch 5)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel<8, 5, 2, 4, false, false, 1> (Q8_0, batch 5)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(burst_ms * 1e3, 3),
@@ -320,6 +320,23 @@ def secondary(cq, gs, dev, stream):
         out[f"q5_k_gemv_14336x4096_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                                              "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
     del w5
+    # FFN-down GEMV 4096 x 14336 (rows of 3.5 wave widths: the four waves of a
+    # workgroup split k), Q8_0 and Q4_K, synthetic weights of those types
+    n, k = 4096, 14336
+    xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(5, k, cfg=16)).to(dev))
+    y = torch.empty((5, n), dtype=torch.float32, device=dev)
+    for fmt in (gs.Q8_0, gs.Q4_K):
+        wd = copies(gs.weights(fmt, n, k, cfg=16))
+        for b in (1, 5):
+            # (in a graph: a Q4_K launch is shorter than a Python call)
+            us = _graph_us(lambda i: cq.cq_gemv(fmt, wd[i % len(wd)], n, k, xq, b, y=y), 8, 50,
+                           stream)
+            gbs = wd[0].numel() / us / 1e3
+            out[f"{gs.NAMES[fmt]}_gemv_4096x14336_b{b}"] = {
+                "graph_us": round(us, 2), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+        del wd
+    n, k = 14336, 4096
     # decode FFN front half, Q4_K gate/up 14336 x 4096: fused gate + up +
     # SwiGLU GEMV then the Q8_0 of h, against two GEMVs and the SwiGLU +
     # requantization kernel (both produce the down GEMV's input)

@@ -32,10 +32,15 @@
 //    output in turn and stores silu(gate)*up after the reduction; MOE makes
 //    grid.y a token-expert pair whose expert id, activation row and output
 //    row offset the pointers at kernel start.
-// Shapes the streaming kernel does not cover (more than two columns per
-// lane, rows that are not whole 16-byte pieces, unaligned activations) use
-// the general kernel: several waves per row, cooperative staging of row
-// tiles in LDS, per-wave sums added in wave order.
+//  * k-split form (KS = 4, rows of two to four wave widths): the four waves
+//    of a workgroup stream the same rows, each over its own k-slice, load
+//    their slice's activations per lane from global memory, and add their
+//    per-row sums in slice order through LDS after each group of P rows.
+// Shapes the streaming kernel does not cover (longer rows, rows that are not
+// whole 16-byte pieces, unaligned activations at one wave per row, rows
+// just over one wave width) use the general kernel: several waves per row,
+// cooperative staging of row tiles in LDS, per-wave sums added in wave
+// order.
 #include "cq_device.h"
 #include "cq_internal.h"
 
@@ -600,16 +605,15 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
     }
 }
 
-// Sum each of the V = RT*B accumulators over the 64 lanes and store row r,
-// batch j to y[j*ldy + r0 + r] (r < rt) with one store instruction.
-// Groups of four values are transposed across the wave with
-// permlane32_swap / permlane16_swap so that each 16-lane row holds one
-// value, then each row is summed with four DPP steps.  The association
-// order is the same for every value slot.
+// Sum each of the V = RT*B accumulators over the 64 lanes.  Groups of four
+// values are transposed across the wave with permlane32_swap /
+// permlane16_swap so that each 16-lane row holds one value, then each row is
+// summed with four DPP steps.  The association order is the same for every
+// value slot.  Returns the sum this lane holds: value slot
+// idx = 4*(lane & 15) + perm(lane >> 4) (perm swapping 1 and 2; slot r*B + j
+// is row r, batch row j), nothing for lanes with lane & 15 >= ceil(V/4).
 template <int RT, int B>
-__device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_t r0,
-                                             float* __restrict__ y, int64_t ldy, int lane,
-                                             int64_t rs = 1) {
+__device__ __forceinline__ float reduce_lanes(float (&acc)[RT][B], int lane) {
     constexpr int V = RT * B;
     constexpr int NG = (V + 3) / 4;
     static_assert(NG <= 16, "at most 64 values");
@@ -634,10 +638,26 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_
         v += dpp_f<0x140>(v);                                                // row sums
         if ((lane & 15) == g) out = v;
     }
-    const int row = lane >> 4, g = lane & 15;
-    const int idx = 4 * g + (row == 1 ? 2 : (row == 2 ? 1 : row));
+    return out;
+}
+
+// value slot held by a lane after reduce_lanes (meaningful while it is < V)
+__device__ __forceinline__ int reduced_slot(int lane) {
+    const int row = lane >> 4;
+    return 4 * (lane & 15) + (row == 1 ? 2 : (row == 2 ? 1 : row));
+}
+
+// Reduce (reduce_lanes) and store row r, batch j to y[j*ldy + r0 + r*rs]
+// (r < rt) with one store instruction.
+template <int RT, int B>
+__device__ __forceinline__ void reduce_store(float (&acc)[RT][B], int rt, int64_t r0,
+                                             float* __restrict__ y, int64_t ldy, int lane,
+                                             int64_t rs = 1) {
+    constexpr int V = RT * B;
+    const float out = reduce_lanes<RT, B>(acc, lane);
+    const int idx = reduced_slot(lane);
     const int r = idx / B, j = idx - (idx / B) * B;
-    if (g < NG && idx < V && r < rt) y[j * ldy + r0 + r * rs] = out;
+    if (idx < V && r < rt) y[j * ldy + r0 + r * rs] = out;
 }
 
 // As reduce_store, for rows that alternate gate, up, gate, up (r0 even):
@@ -650,38 +670,15 @@ __device__ __forceinline__ void reduce_swiglu(float (&acc)[RT][B], int rt, int64
                                               float* __restrict__ h, int64_t ldh, int lane) {
     static_assert(RT % 2 == 0, "gate/up pairs");
     constexpr int V = RT * B;
-    constexpr int NG = (V + 3) / 4;
-    static_assert(NG <= 16, "at most 64 values");
-    float vals[4 * NG];
-#pragma unroll
-    for (int i = 0; i < 4 * NG; ++i) vals[i] = (i < V) ? acc[i / B][i % B] : 0.0f;
-    float out = 0.0f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g]),
-                                                         __float_as_uint(vals[4 * g + 1]), false, false);
-        const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[4 * g + 2]),
-                                                         __float_as_uint(vals[4 * g + 3]), false, false);
-        const float sab = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
-        const float scd = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
-        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(sab), __float_as_uint(scd),
-                                                        false, false);
-        float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-        v += dpp_f<0xB1>(v);
-        v += dpp_f<0x4E>(v);
-        v += dpp_f<0x141>(v);
-        v += dpp_f<0x140>(v);
-        if ((lane & 15) == g) out = v;
-    }
+    const float out = reduce_lanes<RT, B>(acc, lane);
     // value idx sits in lane 16*perm(idx % 4) + idx / 4, perm swapping 1 and 2
-    const int row = lane >> 4, g = lane & 15;
-    const int idx = 4 * g + (row == 1 ? 2 : (row == 2 ? 1 : row));
+    const int idx = reduced_slot(lane);
     const int r = idx / B, j = idx - (idx / B) * B;
     const int pidx = (idx + B < V) ? idx + B : idx;
     const int pm = pidx & 3;
     const int plane = 16 * (pm == 1 ? 2 : (pm == 2 ? 1 : pm)) + (pidx >> 2);
     const float up = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * plane, __float_as_int(out)));
-    if (g < NG && idx < V && (r & 1) == 0 && r < rt)
+    if (idx < V && (r & 1) == 0 && r < rt)
         h[j * ldh + (r0 + r) / 2] = swiglu1(out, up);
 }
 
@@ -703,6 +700,82 @@ constexpr int kBufWord3 = 0x00020000;  // raw 32-bit dwords
 constexpr int kNonTemporal = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufWord3);
+}
+
+// Activation blocks through a buffer resource over the xq rows whose base is
+// xq rounded down to 4 bytes and whose range is rounded up to 4 bytes (every
+// dword that holds an activation byte lies in the range and in a page the
+// buffer touches; nothing outside the range is read).  bo is a block's byte
+// offset from that base (even).  Nine dwords from bo rounded down to 4
+// cover the 34-byte block: three loads instead of seventeen 16-bit ones.
+__device__ __forceinline__ void load_q8_rs(__amdgpu_buffer_rsrc_t rs, int bo, uint32_t* q,
+                                           float* dx, int* sum) {
+    const int b4 = bo & ~3;
+    const bool odd = (bo & 2) != 0;   // d in the high half of the first dword
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, b4, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, b4 + 16, 0, 0);
+    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rs, b4 + 32, 0, 0);
+    const uint32_t wd[9] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c};
+    *dx = h2f(static_cast<uint16_t>(odd ? wd[0] >> 16 : wd[0]));
+    int acc = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        q[t] = odd ? wd[t + 1] : __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16);
+        acc = sdot4(q[t], 0x01010101u, acc);
+    }
+    *sum = acc;
+}
+
+// As load_act, from the buffer: xo is the batch row's byte offset from the
+// resource base.
+template <int FMT>
+__device__ __forceinline__ void load_act_rs(__amdgpu_buffer_rsrc_t rs, int xo, int col, Act<FMT>& a) {
+    if constexpr (kK45<FMT>) {
+        int sa, sb;
+        load_q8_rs(rs, xo + 2 * col * 34, a.qa, &a.dxa, &sa);
+        load_q8_rs(rs, xo + (2 * col + 1) * 34, a.qb, &a.dxb, &sb);
+        a.sa = a.dxa * static_cast<float>(sa);
+        a.sb = a.dxb * static_cast<float>(sb);
+        a.ndxa = -kBiasF * a.dxa;
+        a.ndxb = -kBiasF * a.dxb;
+    } else if constexpr (FMT == T_Q1_0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int sum;
+            load_q8_rs(rs, xo + (2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
+            a.start[j] = kBias - sum;
+            a.ndx[j] = -kBiasF * a.dx[j];
+        }
+    } else if constexpr (FMT == T_Q6_K) {
+        // quadrant g: d and the 16 quants [16 i, 16 i + 16) of block
+        // 8 sb + 4 h + g; five dwords from the quants' start rounded down
+        const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int bo = xo + (8 * sb + 4 * h + g) * 34;
+            const uint32_t dw = __builtin_amdgcn_raw_buffer_load_b32(rs, bo & ~3, 0, 0);
+            a.dx[g] = h2f(static_cast<uint16_t>((bo & 2) ? dw >> 16 : dw));
+            const int qs = bo + 2 + 16 * i, q4 = qs & ~3;
+            const bool odd = (qs & 2) != 0;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, q4, 0, 0);
+            const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, q4 + 16, 0, 0);
+            const uint32_t wd[5] = {v.x, v.y, v.z, v.w, e};
+            int sum = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                a.q[g][t] = odd ? __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16) : wd[t];
+                sum = sdot4(a.q[g][t], 0x01010101u, sum);
+            }
+            a.start[g] = kBias - 32 * sum;
+            a.ndx[g] = -kBiasF * a.dx[g];
+        }
+    } else {
+        int s;
+        load_q8_rs(rs, xo + col * 34, a.q, &a.dx, &s);
+        a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
+        a.ndx = -kBiasF * a.dx;
+        a.sdx = a.dx * static_cast<float>(s);
+    }
 }
 
 // the dword at (even) byte offset O of a dword window
@@ -816,6 +889,15 @@ template <int FMT> constexpr int col_bytes() {
     else return Fmt<FMT>::BS;
 }
 
+// bytes of the 64*C columns of one k-slice (a whole number of blocks)
+template <int FMT, int C> constexpr int slice_bytes() {
+    if constexpr (FMT == T_Q4_K) return kWave * C / 4 * 144;
+    else if constexpr (FMT == T_Q5_K) return kWave * C / 4 * 176;
+    else if constexpr (FMT == T_Q6_K) return kWave * C / 4 * 210;
+    else if constexpr (FMT == T_Q1_0) return kWave * C / 2 * 18;
+    else return kWave * C * Fmt<FMT>::BS;
+}
+
 constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per SIMD)
 
 // Largest activation bytes (all batch rows) one streaming workgroup stages.
@@ -837,11 +919,16 @@ struct MoeMap {
 // the wave's rows are gate/up pairs (rows_q, rows_r count pairs), row 2i of
 // the wave's virtual range is gate row i and row 2i+1 up row i, and y
 // receives h = silu(gate)*up.
-template <int FMT, int B, int C, int P, bool SW = false, bool MOE = false>
+// KS > 1 (rows longer than one wave covers): the KS waves of a row stream
+// take consecutive k-slices of 64*C columns of the same rows, load their
+// slice's activations per lane from global memory (no shared table), and
+// add their per-row sums in wave order through LDS after each group.
+template <int FMT, int B, int C, int P, bool SW = false, bool MOE = false, int KS = 1>
 __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy, const uint8_t* __restrict__ w2 = nullptr, MoeMap mm = {}) {
+    static_assert(KS == 1 || (!SW && !MOE && KS == kGW), "k-split: plain GEMV, one stream per workgroup");
     if constexpr (MOE) {
         static_assert(B == 1, "one activation row per token-expert pair");
         const int pr = static_cast<int>(blockIdx.y);
@@ -863,9 +950,9 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // (Q6_K: the 16 values of one quadrant that the column covers).
     constexpr int NS = (kK45<FMT> || FMT == T_Q1_0) ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
     constexpr int NP = kWave * C;                                  // column positions per row
-    constexpr int NBMAX = B * NS * NP;                             // slots, all rows
+    constexpr int NBMAX = KS == 1 ? B * NS * NP : 1;              // slots, all rows
     constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
-    constexpr int RAW = (XMAX + 16 > kGW * STG) ? XMAX + 16 : kGW * STG;
+    constexpr int RAW = (KS == 1 && XMAX + 16 > kGW * STG) ? XMAX + 16 : kGW * STG;
     // raw activation copy first, the waves' row staging buffers afterwards
     __shared__ __align__(16) uint8_t raw[RAW];
     __shared__ __align__(16) u32x4 xq0[NBMAX];  // quants 0..15 (Q6_K: the slot's 16)
@@ -878,13 +965,18 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     uint8_t* xs = raw;
     uint8_t* stage = raw + wv * STG;
-    // global wave g owns rows [rbeg, rend): rows_q each, one more for the
-    // first rows_r (possibly none)
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * kGW + wv;
+    // global row stream g owns rows [rbeg, rend): rows_q each, one more for
+    // the first rows_r (possibly none); a stream is one wave (KS = 1) or the
+    // KS waves of a workgroup
+    constexpr int NSTREAM = kGW / KS;
+    const int slice = KS > 1 ? wv % KS : 0;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * NSTREAM + wv / KS;
     constexpr int U = SW ? 2 : 1;  // rows per unit (SW: a gate/up pair)
     const int64_t rbeg = U * (g * rows_q + (g < rows_r ? g : rows_r));
     const int64_t rend = rbeg + U * (rows_q + (g < rows_r ? 1 : 0));
-    const bool valid = C * lane < ncols;
+    const int cbase = slice * kWave * C;   // first column of this wave's slice
+    const bool valid = cbase + C * lane < ncols;
+    const int slice_off = slice * slice_bytes<FMT, C>();   // its first byte in a row
     // byte offsets of this lane's column data within a row
     int off, qoff = 0, c0 = 0;
     if constexpr (kK45<FMT>) {
@@ -911,7 +1003,13 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* base;
         if constexpr (SW) base = ((r & 1) ? w2 : w) + (in ? r >> 1 : 0) * rb;
         else base = w + (in ? r : 0) * rb;
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(base, in ? static_cast<int>(rb) : 0);
+        int bytes = in ? static_cast<int>(rb) : 0;
+        if constexpr (KS > 1) {
+            const int left = bytes - slice_off;
+            bytes = left < 0 ? 0 : (left > slice_bytes<FMT, C>() ? slice_bytes<FMT, C>() : left);
+            base += slice_off;
+        }
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(base, bytes);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
             d[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 * j + 16 * lane, 0, kNonTemporal);
@@ -922,12 +1020,14 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // coalesced loads, issued before the first P rows of each wave; the
     // copy only waits for its own loads (they are the oldest).
     const int xact = static_cast<int>(B * xq_row_bytes);
-    constexpr int XPT = (XMAX / 16 + kWave * kGW - 1) / (kWave * kGW);  // pieces per thread
+    constexpr int XPT = KS > 1 ? 1 : (XMAX / 16 + kWave * kGW - 1) / (kWave * kGW);  // pieces per thread
     u32x4 xv[XPT];
+    if constexpr (KS == 1) {
 #pragma unroll
-    for (int t = 0; t < XPT; ++t) {
-        const int pc = threadIdx.x + t * kWave * kGW;
-        xv[t] = *reinterpret_cast<const u32x4*>(xq + (16 * pc < xact ? 16 * pc : 0));
+        for (int t = 0; t < XPT; ++t) {
+            const int pc = threadIdx.x + t * kWave * kGW;
+            xv[t] = *reinterpret_cast<const u32x4*>(xq + (16 * pc < xact ? 16 * pc : 0));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     // (no branch around these loads, even for a spare wave without rows,
@@ -938,6 +1038,24 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
 #pragma unroll
     for (int j = 0; j < P; ++j) load_row(rbeg + j, buf[j]);
     __builtin_amdgcn_sched_barrier(0);
+    Act<FMT> act[C][B];
+    if constexpr (KS > 1) {
+        // each lane loads its own columns' activations (its slice of k);
+        // lanes past the columns keep zeros and add exact zeros
+        (void)xs;
+        if (!has_rows) return;
+        const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(xq) & 3);
+        const __amdgpu_buffer_rsrc_t xr = row_rsrc(xq - mis, (mis + xact + 3) & ~3);
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                act[i][j] = Act<FMT>{};
+                if (valid)
+                    load_act_rs<FMT>(xr, mis + j * static_cast<int>(xq_row_bytes), cbase + C * lane + i,
+                                     act[i][j]);
+            }
+    } else {
 #pragma unroll
     for (int t = 0; t < XPT; ++t) {
         const int pc = threadIdx.x + t * kWave * kGW;
@@ -993,7 +1111,6 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     }
     __syncthreads();  // converted; the raw copy's space now serves as row staging
     if (!has_rows) return;
-    Act<FMT> act[C][B];
 #pragma unroll
     for (int i = 0; i < C; ++i)
 #pragma unroll
@@ -1051,6 +1168,11 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                 }
             }
         }
+    }
+
+    // per-row sums of the KS slices, by group parity (KS > 1)
+    __shared__ float part[KS > 1 ? 2 * KS * P * B : 1];
+    int gpar = 0;
 
     // One group of P rows: stage each row in LDS, refill its registers with
     // the row P further on (REFILL), compute, then reduce and store.  The
@@ -1119,8 +1241,30 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const int rt = static_cast<int>(rend - r < P ? rend - r : P);
-        if constexpr (SW) reduce_swiglu<P, B>(acc, rt, r, y, ldy, lane);
-        else reduce_store<P, B>(acc, rt, r, y, ldy, lane);
+        if constexpr (SW) {
+            reduce_swiglu<P, B>(acc, rt, r, y, ldy, lane);
+        } else if constexpr (KS > 1) {
+            // slice sums -> LDS; after one barrier the first wave adds them in
+            // slice order and stores (double-buffered by group parity, so a
+            // buffer is rewritten only after every wave passed the barrier
+            // that follows its reads)
+            constexpr int V = P * B;
+            const float out = reduce_lanes<P, B>(acc, lane);
+            const int idx = reduced_slot(lane);
+            float* pb = part + gpar * KS * V;
+            if (idx < V) pb[slice * V + idx] = out;
+            __syncthreads();
+            if (slice == 0 && idx < V) {
+                float sum = pb[idx];
+#pragma unroll
+                for (int q = 1; q < KS; ++q) sum += pb[q * V + idx];
+                const int rr = idx / B, jj = idx - (idx / B) * B;
+                if (rr < rt) y[jj * ldy + r + rr] = sum;
+            }
+            gpar ^= 1;
+        } else {
+            reduce_store<P, B>(acc, rt, r, y, ldy, lane);
+        }
     };
     int64_t r = rbeg;
     for (; r + P < rend; r += P) group(r, Bool<true>{});
@@ -1130,6 +1274,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
 struct Plan {
     int ncols, C, nw, RT, tile_lds, red_bytes;
     int SC;  // > 0: streaming kernel with SC columns per lane
+    int KS;  // streaming kernel: waves per row (k-slices), 1 or kGW
 };
 
 constexpr int kRing = 4;  // rows in flight per wave in the streaming kernel
@@ -1157,9 +1302,21 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     // more than the register file at the larger batches, and every batch of
     // one (type, k) must take the same kernel)
     const int sc = (p.ncols + kWave - 1) / kWave;
+    p.KS = 1;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !((super || wt == T_Q1_0) && sc == 2))
+        !((super || wt == T_Q1_0) && sc == 2)) {
         p.SC = sc;
+    } else if (rb % 16 == 0 && p.ncols >= 2 * kWave * p.C &&
+               p.ncols <= kGW * kWave * p.C && p.ncols % p.C == 0) {
+        // rows of two to four wave widths: the four waves of a workgroup
+        // split k (activations loaded per lane, so xq's alignment does not
+        // matter).  Below two widths (e.g. Q1_0 at k = 5120) the multi-wave
+        // tile kernel is faster: most of a k-split workgroup would idle.
+        // k-split vs tile kernel, 4096 rows x 14336: Q8_0 b1 12.5 vs 17.1 us,
+        // Q4_K b1 9.0 vs 15.1 us, Q4_K b8 18.2 vs 31.2 us.
+        p.SC = p.C;
+        p.KS = kGW;
+    }
     return p;
 }
 
@@ -1171,11 +1328,11 @@ int resident_blocks_per_cu(K kernel, int threads) {
     return nb;
 }
 
-template <int FMT, int B, int SC, bool SW = false, bool MOE = false>
+template <int FMT, int B, int SC, bool SW = false, bool MOE = false, int KS = 1>
 int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint8_t* xq,
                   int64_t xrb, float* y, int64_t ldy, hipStream_t stream,
                   const uint8_t* w2 = nullptr, MoeMap mm = {}, int npairs = 1) {
-    auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW, MOE>;
+    auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW, MOE, KS>;
     static const int occ = kGW * resident_blocks_per_cu(kern, kWave * kGW);
     int per_cu = occ < 8 ? occ : 8;
     // as many waves as fit, each with a whole number of P-row groups where
@@ -1183,13 +1340,15 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
     // rounded up to whole workgroups (spare waves get no rows).  Units are
     // rows, or gate/up row pairs (two per group) for SW.
     constexpr int64_t upg = SW ? kRing / 2 : kRing;  // units per group
-    // (MOE: the wave slots are shared by the npairs matrices of the launch)
-    int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu / npairs;
-    if (gmax < kGW) gmax = kGW;
+    // (MOE: the wave slots are shared by the npairs matrices of the launch;
+    // KS > 1: a row stream is KS waves)
+    constexpr int NSTREAM = kGW / KS;
+    int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu / npairs / KS;
+    if (gmax < NSTREAM) gmax = NSTREAM;
     const int64_t groups = (n + upg - 1) / upg;
     const int64_t gpw = (groups + gmax - 1) / gmax;
-    const int64_t waves = (n + gpw * upg - 1) / (gpw * upg);
-    const int64_t wgs = (waves + kGW - 1) / kGW, nw = wgs * kGW;
+    const int64_t waves = (n + gpw * upg - 1) / (gpw * upg);   // row streams
+    const int64_t wgs = (waves + NSTREAM - 1) / NSTREAM, nw = wgs * NSTREAM;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs), static_cast<unsigned>(npairs)),
                        dim3(kWave * kGW), 0, stream, w, n / nw, static_cast<int>(n % nw), rb, ncols,
                        xq, xrb, y, ldy, w2, mm);
@@ -1199,6 +1358,14 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
 template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
+    if (p.KS == kGW) {
+        if (p.SC == 1)
+            return launch_stream<FMT, B, 1, false, false, kGW>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+        if constexpr (!kOneCol<FMT>)
+            if (p.SC == 2)
+                return launch_stream<FMT, B, 2, false, false, kGW>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+        return -3;
+    }
     if (p.SC == 1) return launch_stream<FMT, B, 1>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
     if constexpr (!kOneCol<FMT>)  // (one column per lane for the super-block formats, Q1_0)
         if (p.SC == 2) return launch_stream<FMT, B, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
@@ -1293,7 +1460,7 @@ int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch) {
     if (gemv_shape_ok(wt, k, batch) != 0) return -3;
     const Plan p = make_plan(wt, k, k / block_elems_of(wt) * block_bytes_of(wt),
                              static_cast<int>(batch), true);
-    return p.SC > 0 ? 0 : -3;
+    return p.SC > 0 && p.KS == 1 ? 0 : -3;
 }
 
 template <int FMT, int B>

@@ -22,7 +22,8 @@ def run_gemv(cq, fmt, w, n, k, xq, batch):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n,k", [(1, 256), (37, 256), (130, 2048), (67, 4096), (9, 8192),
-                                 (21, 352), (45, 1056)])
+                                 (21, 352), (45, 1056), (11, 4160), (13, 5120), (70, 14336),
+                                 (5, 16384), (3, 16416)])
 def test_gemv_small_shapes(cq, orc, fmt, n, k):
     if k % gs.BLOCK_ELEMS[fmt]:
         pytest.skip("k not a whole number of blocks for this type")
@@ -87,7 +88,7 @@ def test_gemv_lm_head_sampled(cq, orc, name):
         assert np.array_equal(yb[0], y4[b])
 
 
-@pytest.mark.parametrize("k", [1024, 2048, 4096])
+@pytest.mark.parametrize("k", [1024, 2048, 4096, 8192, 14336])
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 def test_gemv_batch_rows_equal_single_rows(cq, orc, fmt, k):
     """Row b of a verify batch is bitwise the batch-1 result on that row, for
@@ -140,6 +141,32 @@ def test_gemv_strided_output(cq, orc):
     yh = to_host(y)
     y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, 3)
     assert_close_to_oracle(yh[:, :n], y_ref, s_ref, what="strided")
+    assert np.all(yh[:, n:] == -7.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
+def test_gemv_long_rows_unaligned_and_strided(cq, orc, fmt):
+    """Rows longer than one wave covers (k = 14336: the k-split streaming
+    path) with the activations 2 bytes past a 16-byte boundary and a strided
+    output: same values as the aligned call, bitwise, and within the oracle's
+    bound; the columns past n keep their contents."""
+    import torch
+    n, k, B = 77, 14336, 3
+    w = gs.weights(fmt, n, k, cfg=304)
+    xq = orc.quantize_q8_0(gs.activations(B, k, cfg=304))
+    y_ref, s_ref = orc.matmul(fmt, w, n, k, xq, B)
+    wd = to_dev(w)
+    note("gemv long rows aligned", gs.NAMES[fmt])
+    y0 = to_host(cq.cq_gemv(fmt, wd, n, k, to_dev(xq), B))
+    assert_close_to_oracle(y0, y_ref, s_ref, what="long rows")
+    buf = torch.zeros(xq.size + 16, dtype=torch.uint8, device="cuda")
+    buf[2:2 + xq.size] = to_dev(xq.reshape(-1))
+    xu = buf[2:2 + xq.size].view(B, -1)
+    y = torch.full((B, 100), -7.0, device="cuda")
+    note("gemv long rows unaligned strided", gs.NAMES[fmt])
+    cq.cq_gemv(fmt, wd, n, k, xu, B, y=y, ldy=100)
+    yh = to_host(y)
+    assert np.array_equal(yh[:, :n], y0)
     assert np.all(yh[:, n:] == -7.0)
 
 
