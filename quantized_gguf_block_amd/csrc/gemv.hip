@@ -162,70 +162,93 @@ __device__ __forceinline__ int dot8(const uint32_t* w, const uint32_t* x, int st
     }
 }
 
-// Load one 34-byte Q8_0 activation block (2-byte aligned) from global memory.
-__device__ __forceinline__ void load_q8(const uint8_t* p, uint32_t* q, float* dx, int* sum) {
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
-    *dx = h2f(s[0]);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Weight rows are read through buffer descriptors: the row base and its
+// length live in scalar registers, each lane adds a 32-bit offset, and the
+// hardware returns zeros for bytes at or past the length without touching
+// memory.  The loads carry the non-temporal hint (every weight byte is read
+// once).
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit dwords
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufWord3);
+}
+
+// Activation blocks through a buffer resource over the xq rows whose base is
+// xq rounded down to 4 bytes and whose range is rounded up to 4 bytes (every
+// dword that holds an activation byte lies in the range and in a page the
+// buffer touches; nothing outside the range is read).  bo is a block's byte
+// offset from that base (even).  Nine dwords from bo rounded down to 4
+// cover the 34-byte block: three loads instead of seventeen 16-bit ones.
+__device__ __forceinline__ void load_q8_rs(__amdgpu_buffer_rsrc_t rs, int bo, uint32_t* q,
+                                           float* dx, int* sum) {
+    const int b4 = bo & ~3;
+    const bool odd = (bo & 2) != 0;   // d in the high half of the first dword
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, b4, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, b4 + 16, 0, 0);
+    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rs, b4 + 32, 0, 0);
+    const uint32_t wd[9] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c};
+    *dx = h2f(static_cast<uint16_t>(odd ? wd[0] >> 16 : wd[0]));
     int acc = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        q[t] = static_cast<uint32_t>(s[1 + 2 * t]) | (static_cast<uint32_t>(s[2 + 2 * t]) << 16);
+        q[t] = odd ? wd[t + 1] : __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16);
         acc = sdot4(q[t], 0x01010101u, acc);
     }
     *sum = acc;
 }
 
+// The Q8_0 activation of lane column col (its blocks and the per-block
+// terms the dot chains start from) for one batch row, whose first byte is
+// at offset xo from the resource base.
 template <int FMT>
-__device__ __forceinline__ void load_act(const uint8_t* xq_row, int col, Act<FMT>& a) {
-    int s;
-    load_q8(xq_row + static_cast<int64_t>(col) * 34, a.q, &a.dx, &s);
-    a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
-    a.ndx = -kBiasF * a.dx;
-    a.sdx = a.dx * static_cast<float>(s);
-}
-template <>
-__device__ __forceinline__ void load_act<T_Q4_K>(const uint8_t* xq_row, int col, Act<T_Q4_K>& a) {
-    int sa, sb;
-    load_q8(xq_row + static_cast<int64_t>(2 * col) * 34, a.qa, &a.dxa, &sa);
-    load_q8(xq_row + static_cast<int64_t>(2 * col + 1) * 34, a.qb, &a.dxb, &sb);
-    a.sa = a.dxa * static_cast<float>(sa);
-    a.sb = a.dxb * static_cast<float>(sb);
-    a.ndxa = -kBiasF * a.dxa;
-    a.ndxb = -kBiasF * a.dxb;
-}
-template <>
-__device__ __forceinline__ void load_act<T_Q5_K>(const uint8_t* xq_row, int col, Act<T_Q5_K>& a) {
-    load_act<T_Q4_K>(xq_row, col, a);
-}
-
-template <>
-__device__ __forceinline__ void load_act<T_Q1_0>(const uint8_t* xq_row, int col, Act<T_Q1_0>& a) {
+__device__ __forceinline__ void load_act_rs(__amdgpu_buffer_rsrc_t rs, int xo, int col, Act<FMT>& a) {
+    if constexpr (kK45<FMT>) {
+        int sa, sb;
+        load_q8_rs(rs, xo + 2 * col * 34, a.qa, &a.dxa, &sa);
+        load_q8_rs(rs, xo + (2 * col + 1) * 34, a.qb, &a.dxb, &sb);
+        a.sa = a.dxa * static_cast<float>(sa);
+        a.sb = a.dxb * static_cast<float>(sb);
+        a.ndxa = -kBiasF * a.dxa;
+        a.ndxb = -kBiasF * a.dxb;
+    } else if constexpr (FMT == T_Q1_0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        int sum;
-        load_q8(xq_row + static_cast<int64_t>(2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
-        a.start[j] = kBias - sum;
-        a.ndx[j] = -kBiasF * a.dx[j];
-    }
-}
-
-template <>
-__device__ __forceinline__ void load_act<T_Q6_K>(const uint8_t* xq_row, int col, Act<T_Q6_K>& a) {
-    const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(
-            xq_row + static_cast<int64_t>(8 * sb + 4 * h + g) * 34);
-        a.dx[g] = h2f(p[0]);
-        int sum = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int o = 1 + 8 * i + 2 * t;  // 16-bit word of byte 2 + 16 i + 4 t
-            a.q[g][t] = static_cast<uint32_t>(p[o]) | (static_cast<uint32_t>(p[o + 1]) << 16);
-            sum = sdot4(a.q[g][t], 0x01010101u, sum);
+        for (int j = 0; j < 2; ++j) {
+            int sum;
+            load_q8_rs(rs, xo + (2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
+            a.start[j] = kBias - sum;
+            a.ndx[j] = -kBiasF * a.dx[j];
         }
-        a.start[g] = kBias - 32 * sum;
-        a.ndx[g] = -kBiasF * a.dx[g];
+    } else if constexpr (FMT == T_Q6_K) {
+        // quadrant g: d and the 16 quants [16 i, 16 i + 16) of block
+        // 8 sb + 4 h + g; five dwords from the quants' start rounded down
+        const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int bo = xo + (8 * sb + 4 * h + g) * 34;
+            const uint32_t dw = __builtin_amdgcn_raw_buffer_load_b32(rs, bo & ~3, 0, 0);
+            a.dx[g] = h2f(static_cast<uint16_t>((bo & 2) ? dw >> 16 : dw));
+            const int qs = bo + 2 + 16 * i, q4 = qs & ~3;
+            const bool odd = (qs & 2) != 0;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, q4, 0, 0);
+            const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, q4 + 16, 0, 0);
+            const uint32_t wd[5] = {v.x, v.y, v.z, v.w, e};
+            int sum = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                a.q[g][t] = odd ? __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16) : wd[t];
+                sum = sdot4(a.q[g][t], 0x01010101u, sum);
+            }
+            a.start[g] = kBias - 32 * sum;
+            a.ndx[g] = -kBiasF * a.dx[g];
+        }
+    } else {
+        int s;
+        load_q8_rs(rs, xo + col * 34, a.q, &a.dx, &s);
+        a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
+        a.ndx = -kBiasF * a.dx;
+        a.sdx = a.dx * static_cast<float>(s);
     }
 }
 
@@ -509,7 +532,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
     float* red = reinterpret_cast<float*>(smem + tile_lds_bytes);
     const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-    // columns of this lane and their activations, resident for the whole kernel
+    // columns of this lane and their activations, resident for the whole
+    // kernel (read through a descriptor over the activation rows, base
+    // rounded down and length rounded up to 4 bytes)
+    const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(xq) & 3);
+    const __amdgpu_buffer_rsrc_t xr =
+        row_rsrc(xq - mis, (mis + B * static_cast<int>(xq_row_bytes) + 3) & ~3);
     constexpr int CM = kCMax<FMT>;
     Act<FMT> act[CM][B];
     int col[CM];
@@ -520,7 +548,8 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(
         valid[i] = (i < C) && (col[i] < ncols);
 #pragma unroll
         for (int j = 0; j < B; ++j)
-            if (valid[i]) load_act<FMT>(xq + j * xq_row_bytes, col[i], act[i][j]);
+            if (valid[i])
+                load_act_rs<FMT>(xr, mis + j * static_cast<int>(xq_row_bytes), col[i], act[i][j]);
     }
 
     const int64_t total = n * rb;
@@ -682,102 +711,7 @@ __device__ __forceinline__ void reduce_swiglu(float (&acc)[RT][B], int rt, int64
         h[j * ldh + (r0 + r) / 2] = swiglu1(out, up);
 }
 
-// ---- streaming kernel: one wave per workgroup, each wave owns a contiguous
-// range of rows; every lane loads its own blocks of each row straight from
-// HBM into registers (non-temporal 16-byte loads), through a ring of P row
-// buffers, so P rows are in flight while one is computed.  Each lane owns C
-// consecutive columns (32-value blocks; Q4_K: 32-byte nibble chunks) and
-// keeps their activations for all batch rows in registers.  Every P rows the
-// P*B sums are reduced across the wave together and stored.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Weight rows are read through buffer descriptors: the row base and its
-// length live in scalar registers, each lane adds a 32-bit offset, and the
-// hardware returns zeros for bytes at or past the length without touching
-// memory.  The loads carry the non-temporal hint (every weight byte is read
-// once).
-constexpr int kBufWord3 = 0x00020000;  // raw 32-bit dwords
-constexpr int kNonTemporal = 2;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufWord3);
-}
-
-// Activation blocks through a buffer resource over the xq rows whose base is
-// xq rounded down to 4 bytes and whose range is rounded up to 4 bytes (every
-// dword that holds an activation byte lies in the range and in a page the
-// buffer touches; nothing outside the range is read).  bo is a block's byte
-// offset from that base (even).  Nine dwords from bo rounded down to 4
-// cover the 34-byte block: three loads instead of seventeen 16-bit ones.
-__device__ __forceinline__ void load_q8_rs(__amdgpu_buffer_rsrc_t rs, int bo, uint32_t* q,
-                                           float* dx, int* sum) {
-    const int b4 = bo & ~3;
-    const bool odd = (bo & 2) != 0;   // d in the high half of the first dword
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, b4, 0, 0);
-    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, b4 + 16, 0, 0);
-    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rs, b4 + 32, 0, 0);
-    const uint32_t wd[9] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c};
-    *dx = h2f(static_cast<uint16_t>(odd ? wd[0] >> 16 : wd[0]));
-    int acc = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        q[t] = odd ? wd[t + 1] : __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16);
-        acc = sdot4(q[t], 0x01010101u, acc);
-    }
-    *sum = acc;
-}
-
-// As load_act, from the buffer: xo is the batch row's byte offset from the
-// resource base.
-template <int FMT>
-__device__ __forceinline__ void load_act_rs(__amdgpu_buffer_rsrc_t rs, int xo, int col, Act<FMT>& a) {
-    if constexpr (kK45<FMT>) {
-        int sa, sb;
-        load_q8_rs(rs, xo + 2 * col * 34, a.qa, &a.dxa, &sa);
-        load_q8_rs(rs, xo + (2 * col + 1) * 34, a.qb, &a.dxb, &sb);
-        a.sa = a.dxa * static_cast<float>(sa);
-        a.sb = a.dxb * static_cast<float>(sb);
-        a.ndxa = -kBiasF * a.dxa;
-        a.ndxb = -kBiasF * a.dxb;
-    } else if constexpr (FMT == T_Q1_0) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            int sum;
-            load_q8_rs(rs, xo + (2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
-            a.start[j] = kBias - sum;
-            a.ndx[j] = -kBiasF * a.dx[j];
-        }
-    } else if constexpr (FMT == T_Q6_K) {
-        // quadrant g: d and the 16 quants [16 i, 16 i + 16) of block
-        // 8 sb + 4 h + g; five dwords from the quants' start rounded down
-        const int sb = col >> 2, h = (col >> 1) & 1, i = col & 1;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int bo = xo + (8 * sb + 4 * h + g) * 34;
-            const uint32_t dw = __builtin_amdgcn_raw_buffer_load_b32(rs, bo & ~3, 0, 0);
-            a.dx[g] = h2f(static_cast<uint16_t>((bo & 2) ? dw >> 16 : dw));
-            const int qs = bo + 2 + 16 * i, q4 = qs & ~3;
-            const bool odd = (qs & 2) != 0;
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, q4, 0, 0);
-            const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, q4 + 16, 0, 0);
-            const uint32_t wd[5] = {v.x, v.y, v.z, v.w, e};
-            int sum = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                a.q[g][t] = odd ? __builtin_amdgcn_alignbit(wd[t + 1], wd[t], 16) : wd[t];
-                sum = sdot4(a.q[g][t], 0x01010101u, sum);
-            }
-            a.start[g] = kBias - 32 * sum;
-            a.ndx[g] = -kBiasF * a.dx[g];
-        }
-    } else {
-        int s;
-        load_q8_rs(rs, xo + col * 34, a.q, &a.dx, &s);
-        a.start = (FMT == T_Q4_0) ? kBias - 8 * s : kBias;
-        a.ndx = -kBiasF * a.dx;
-        a.sdx = a.dx * static_cast<float>(s);
-    }
-}
-
+// ---- streaming kernel helpers: dword windows of a staged row ---------------
 // the dword at (even) byte offset O of a dword window
 template <int O>
 __device__ __forceinline__ uint32_t dw_at(const uint32_t* w) {
@@ -1372,7 +1306,11 @@ int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const u
     const int64_t ntiles = (n + p.RT - 1) / p.RT;
     const int per_cu = p.nw >= 4 ? 2 : 8 / p.nw;
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
-    if (grid > ntiles) grid = ntiles;
+    // small workgroups (one or two waves) and up to two tiles per slot: one
+    // workgroup per tile, so none runs a second tile after the others have
+    // finished (Q1_0 10240 x 5120, batch 1: 8.1 against 9.0 us); with larger
+    // workgroups the extra resident ones slowed long rows at batch 8
+    if (grid > ntiles || (p.nw <= 2 && ntiles <= 2 * grid)) grid = ntiles;
     const dim3 g(static_cast<unsigned>(grid)), b(p.nw * kWave);
     const size_t lds = static_cast<size_t>(p.tile_lds + p.red_bytes);
     switch (p.RT) {
