@@ -159,10 +159,11 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  *               aligned (both matrices of the same type and shape).
  *   xq          [batch][k/32] Q8_0 blocks, 16-byte aligned.
  *   h           fp32, row b at h + b*ldh, ldh >= n, 4-byte aligned.
- *   Shapes: the single-pass kernel needs one wave per row: k <= 4096 and
- *   k a multiple of 256 (whole 16-byte weight and activation rows; Q6_K:
- *   k a multiple of 2048); other shapes return CQ_ERR_SHAPE (use cq_gemv
- *   twice and cq_swiglu_quantize_q8_0).  An xq not 16-byte aligned returns
+ *   Shapes: whole 16-byte weight rows (k a multiple of 256; Q6_K: k a
+ *   multiple of 2048) with k <= 4096 (one wave per row), or rows of two to
+ *   four wave widths, 8192 <= k <= 16384 (the four waves of a workgroup
+ *   split k); other shapes return CQ_ERR_SHAPE (use cq_gemv twice and
+ *   cq_swiglu_quantize_q8_0).  An xq not 16-byte aligned returns
  *   CQ_ERR_ALIGNMENT.
  */
 int cq_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
@@ -237,8 +238,8 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
  *   expert_ids  device int32 [n_tokens][top_k]; ids outside [0, n_experts)
  *               are clamped into range (they cannot be checked on the host).
  *   xq          Q8_0 rows, 16-byte aligned; y fp32 [n_tokens*top_k][ldy].
- *   Shapes: as cq_gemv_swiglu (one wave per row), n_tokens*top_k <= 65535;
- *   else CQ_ERR_SHAPE.
+ *   Shapes: as cq_gemv_swiglu with one wave per row only (k <= 4096),
+ *   n_tokens*top_k <= 65535; else CQ_ERR_SHAPE.
  */
 int cq_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                 const void* xq, int x_per_pair, const int32_t* expert_ids,

@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy, const uint8_t* __restrict__ w2 = nullptr, MoeMap mm = {}) {
-    static_assert(KS == 1 || (!SW && !MOE && KS == kGW), "k-split: plain GEMV, one stream per workgroup");
+    static_assert(KS == 1 || (!MOE && KS == kGW), "k-split: plain or fused GEMV, one stream per workgroup");
     if constexpr (MOE) {
         static_assert(B == 1, "one activation row per token-expert pair");
         const int pr = static_cast<int>(blockIdx.y);
@@ -1175,9 +1175,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const int rt = static_cast<int>(rend - r < P ? rend - r : P);
-        if constexpr (SW) {
-            reduce_swiglu<P, B>(acc, rt, r, y, ldy, lane);
-        } else if constexpr (KS > 1) {
+        if constexpr (KS > 1) {
             // slice sums -> LDS; after one barrier the first wave adds them in
             // slice order and stores (double-buffered by group parity, so a
             // buffer is rewritten only after every wave passed the barrier
@@ -1188,14 +1186,30 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             float* pb = part + gpar * KS * V;
             if (idx < V) pb[slice * V + idx] = out;
             __syncthreads();
-            if (slice == 0 && idx < V) {
-                float sum = pb[idx];
+            if (slice == 0) {
+                float sum = 0.0f;
+                if (idx < V) {
+                    sum = pb[idx];
 #pragma unroll
-                for (int q = 1; q < KS; ++q) sum += pb[q * V + idx];
+                    for (int q = 1; q < KS; ++q) sum += pb[q * V + idx];
+                }
                 const int rr = idx / B, jj = idx - (idx / B) * B;
-                if (rr < rt) y[jj * ldy + r + rr] = sum;
+                if constexpr (SW) {
+                    // gate row rr (even) takes up row rr + 1 of the same batch
+                    // row from the lane that holds it (as in reduce_swiglu)
+                    const int pidx = (idx + B < V) ? idx + B : idx;
+                    const int pm = pidx & 3;
+                    const int plane = 16 * (pm == 1 ? 2 : (pm == 2 ? 1 : pm)) + (pidx >> 2);
+                    const float up = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * plane, __float_as_int(sum)));
+                    if (idx < V && (rr & 1) == 0 && rr < rt)
+                        y[jj * ldy + (r + rr) / 2] = swiglu1(sum, up);
+                } else {
+                    if (idx < V && rr < rt) y[jj * ldy + r + rr] = sum;
+                }
             }
             gpar ^= 1;
+        } else if constexpr (SW) {
+            reduce_swiglu<P, B>(acc, rt, r, y, ldy, lane);
         } else {
             reduce_store<P, B>(acc, rt, r, y, ldy, lane);
         }
@@ -1391,19 +1405,28 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
 }
 
 // ---- fused gate/up GEMV + SwiGLU (decode FFN) -------------------------------
-// Streaming kernel only: the shape must give one wave per row (k <= 4096 for
-// the 32-value formats, k <= 4096 for the super-block formats), whole 16-byte
-// weight and activation rows, and a 16-byte aligned xq.
+// Streaming kernel only: one wave per row (k <= 4096) with a 16-byte aligned
+// xq, or its k-split form (rows of two to four wave widths, k = 8192..16384),
+// and whole 16-byte weight rows.
 int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch) {
     if (gemv_shape_ok(wt, k, batch) != 0) return -3;
     const Plan p = make_plan(wt, k, k / block_elems_of(wt) * block_bytes_of(wt),
                              static_cast<int>(batch), true);
-    return p.SC > 0 && p.KS == 1 ? 0 : -3;
+    return p.SC > 0 ? 0 : -3;
 }
 
 template <int FMT, int B>
-int launch_sw_b(int SC, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb, int ncols,
-                const uint8_t* xq, int64_t xrb, float* h, int64_t ldh, hipStream_t stream) {
+int launch_sw_b(int SC, int KS, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb,
+                int ncols, const uint8_t* xq, int64_t xrb, float* h, int64_t ldh,
+                hipStream_t stream) {
+    if (KS == kGW) {
+        if (SC == 1)
+            return launch_stream<FMT, B, 1, true, false, kGW>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+        if constexpr (!kOneCol<FMT>)
+            if (SC == 2)
+                return launch_stream<FMT, B, 2, true, false, kGW>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+        return -3;
+    }
     if (SC == 1) return launch_stream<FMT, B, 1, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
     if constexpr (!kOneCol<FMT>)
         if (SC == 2) return launch_stream<FMT, B, 2, true>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
@@ -1411,17 +1434,17 @@ int launch_sw_b(int SC, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t
 }
 
 template <int FMT>
-int launch_sw(int SC, int b, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb,
+int launch_sw(int SC, int KS, int b, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb,
               int ncols, const uint8_t* xq, int64_t xrb, float* h, int64_t ldh, hipStream_t s) {
     switch (b) {
-        case 1: return launch_sw_b<FMT, 1>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 2: return launch_sw_b<FMT, 2>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 3: return launch_sw_b<FMT, 3>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 4: return launch_sw_b<FMT, 4>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 5: return launch_sw_b<FMT, 5>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 6: return launch_sw_b<FMT, 6>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        case 7: return launch_sw_b<FMT, 7>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
-        default: return launch_sw_b<FMT, 8>(SC, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 1: return launch_sw_b<FMT, 1>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 2: return launch_sw_b<FMT, 2>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 3: return launch_sw_b<FMT, 3>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 4: return launch_sw_b<FMT, 4>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 5: return launch_sw_b<FMT, 5>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 6: return launch_sw_b<FMT, 6>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        case 7: return launch_sw_b<FMT, 7>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
+        default: return launch_sw_b<FMT, 8>(SC, KS, wg, wu, n, rb, ncols, xq, xrb, h, ldh, s);
     }
 }
 
@@ -1436,23 +1459,24 @@ int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, 
     const int64_t xrb = k / 32 * 34;
     const int b = static_cast<int>(batch);
     switch (wt) {
-        case T_Q4_0: return launch_sw<T_Q4_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q4_1: return launch_sw<T_Q4_1>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q8_0: return launch_sw<T_Q8_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q4_K: return launch_sw<T_Q4_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q5_K: return launch_sw<T_Q5_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
-        case T_Q1_0: return launch_sw<T_Q1_0>(p.SC, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q4_0: return launch_sw<T_Q4_0>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q4_1: return launch_sw<T_Q4_1>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q8_0: return launch_sw<T_Q8_0>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q4_K: return launch_sw<T_Q4_K>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q5_K: return launch_sw<T_Q5_K>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_Q1_0: return launch_sw<T_Q1_0>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         default: return -2;
     }
 }
 
 // ---- routed experts at decode: one GEMV per token-expert pair ---------------
-// Same single-pass shapes as the fused FFN (one wave per row); pairs beyond
+// One wave per row (k <= 4096, whole 16-byte rows, aligned xq); pairs beyond
 // grid.y's range are refused.
 int moe_gemv_shape_ok(int wt, int64_t k, int64_t npairs) {
-    if (npairs > 65535) return -3;
-    return gemv_swiglu_shape_ok(wt, k, 1);
+    if (npairs > 65535 || gemv_swiglu_shape_ok(wt, k, 1) != 0) return -3;
+    const Plan p = make_plan(wt, k, k / block_elems_of(wt) * block_bytes_of(wt), 1, true);
+    return p.KS == 1 ? 0 : -3;
 }
 
 template <int FMT, bool SW>
