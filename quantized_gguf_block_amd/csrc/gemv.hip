@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ w, int64_t rows_q, int rows_r, int64_t rb, int ncols,
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy, const uint8_t* __restrict__ w2 = nullptr, MoeMap mm = {}) {
-    static_assert(KS == 1 || (!MOE && KS == kGW), "k-split: plain or fused GEMV, one stream per workgroup");
+    static_assert(KS == 1 || (!MOE && kGW % KS == 0), "k-split: plain or fused GEMV, whole streams per workgroup");
     if constexpr (MOE) {
         static_assert(B == 1, "one activation row per token-expert pair");
         const int pr = static_cast<int>(blockIdx.y);
@@ -967,7 +967,12 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // (no branch around these loads, even for a spare wave without rows,
     // whose loads read zeros: with a branch, the wait for the activation
     // copy below would also wait for these loads)
-    const bool has_rows = rbeg < rend;
+    // KS > 1: every wave of the workgroup runs the groups of its first
+    // stream (the one with the most rows), so all take the same barriers;
+    // a stream with fewer rows computes zeros past rend and stores nothing
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * NSTREAM;
+    const int64_t rows0 = U * (rows_q + (g0 < rows_r ? 1 : 0));
+    const bool has_rows = KS > 1 ? rows0 > 0 : rbeg < rend;
     u32x4 buf[P][NJ];
 #pragma unroll
     for (int j = 0; j < P; ++j) load_row(rbeg + j, buf[j]);
@@ -1105,7 +1110,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     }
 
     // per-row sums of the KS slices, by group parity (KS > 1)
-    __shared__ float part[KS > 1 ? 2 * KS * P * B : 1];
+    __shared__ float part[KS > 1 ? 2 * kGW * P * B : 1];
     int gpar = 0;
 
     // One group of P rows: stage each row in LDS, refill its registers with
@@ -1183,7 +1188,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
             constexpr int V = P * B;
             const float out = reduce_lanes<P, B>(acc, lane);
             const int idx = reduced_slot(lane);
-            float* pb = part + gpar * KS * V;
+            float* pb = part + (gpar * NSTREAM + wv / KS) * KS * V;
             if (idx < V) pb[slice * V + idx] = out;
             __syncthreads();
             if (slice == 0) {
@@ -1215,14 +1220,19 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         }
     };
     int64_t r = rbeg;
-    for (; r + P < rend; r += P) group(r, Bool<true>{});
+    if constexpr (KS > 1) {
+        const int64_t ng = (rows0 + P - 1) / P;   // workgroup-uniform
+        for (int64_t i = 1; i < ng; ++i, r += P) group(r, Bool<true>{});
+    } else {
+        for (; r + P < rend; r += P) group(r, Bool<true>{});
+    }
     group(r, Bool<false>{});
 }
 
 struct Plan {
     int ncols, C, nw, RT, tile_lds, red_bytes;
     int SC;  // > 0: streaming kernel with SC columns per lane
-    int KS;  // streaming kernel: waves per row (k-slices), 1 or kGW
+    int KS;  // streaming kernel: waves per row (k-slices), 1, 2 or kGW
 };
 
 constexpr int kRing = 4;  // rows in flight per wave in the streaming kernel
@@ -1263,7 +1273,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
         // k-split vs tile kernel, 4096 rows x 14336: Q8_0 b1 12.5 vs 17.1 us,
         // Q4_K b1 9.0 vs 15.1 us, Q4_K b8 18.2 vs 31.2 us.
         p.SC = p.C;
-        p.KS = kGW;
+        p.KS = p.ncols <= 2 * kWave * p.C ? 2 : kGW;
     }
     return p;
 }
@@ -1306,6 +1316,14 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
 template <int FMT, int B>
 int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const uint8_t* xq,
                  int64_t xrb, float* y, int64_t ldy, hipStream_t stream) {
+    if (p.KS == 2) {
+        if (p.SC == 1)
+            return launch_stream<FMT, B, 1, false, false, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+        if constexpr (!kOneCol<FMT>)
+            if (p.SC == 2)
+                return launch_stream<FMT, B, 2, false, false, 2>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
+        return -3;
+    }
     if (p.KS == kGW) {
         if (p.SC == 1)
             return launch_stream<FMT, B, 1, false, false, kGW>(w, n, rb, p.ncols, xq, xrb, y, ldy, stream);
@@ -1419,6 +1437,14 @@ template <int FMT, int B>
 int launch_sw_b(int SC, int KS, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t rb,
                 int ncols, const uint8_t* xq, int64_t xrb, float* h, int64_t ldh,
                 hipStream_t stream) {
+    if (KS == 2) {
+        if (SC == 1)
+            return launch_stream<FMT, B, 1, true, false, 2>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+        if constexpr (!kOneCol<FMT>)
+            if (SC == 2)
+                return launch_stream<FMT, B, 2, true, false, 2>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);
+        return -3;
+    }
     if (KS == kGW) {
         if (SC == 1)
             return launch_stream<FMT, B, 1, true, false, kGW>(wg, n, rb, ncols, xq, xrb, h, ldh, stream, wu);

@@ -49,7 +49,7 @@ def check_against_oracle(orc, fmt, wg_h, wu_h, n, k, xq_h, batch, h):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n,k", [(1, 2048), (37, 256), (300, 1024), (1001, 2048), (257, 4096),
-                                 (45, 8192), (130, 14336), (3, 16384)])
+                                 (45, 8192), (130, 14336), (3, 16384), (1, 8192), (3, 8192)])
 def test_gemv_swiglu_small(cq, orc, fmt, n, k):
     if k % 256 or gs.row_bytes(fmt, k) % 16:
         pytest.skip("no single-pass kernel for this (type, k)")

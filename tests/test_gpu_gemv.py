@@ -23,7 +23,7 @@ def run_gemv(cq, fmt, w, n, k, xq, batch):
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n,k", [(1, 256), (37, 256), (130, 2048), (67, 4096), (9, 8192),
                                  (21, 352), (45, 1056), (11, 4160), (13, 5120), (70, 14336),
-                                 (5, 16384), (3, 16416)])
+                                 (5, 16384), (3, 16416), (1, 8192), (3, 8192), (70, 8192)])
 def test_gemv_small_shapes(cq, orc, fmt, n, k):
     if k % gs.BLOCK_ELEMS[fmt]:
         pytest.skip("k not a whole number of blocks for this type")
