@@ -160,9 +160,9 @@ int cq_gemv(int wt, const void* w, int64_t n, int64_t k,
  *   xq          [batch][k/32] Q8_0 blocks, 16-byte aligned.
  *   h           fp32, row b at h + b*ldh, ldh >= n, 4-byte aligned.
  *   Shapes: whole 16-byte weight rows (k a multiple of 256; Q6_K: k a
- *   multiple of 2048) with k <= 4096 (one wave per row), or rows of two to
- *   four wave widths, 8192 <= k <= 16384 (the four waves of a workgroup
- *   split k); other shapes return CQ_ERR_SHAPE (use cq_gemv twice and
+ *   multiple of 2048) with k <= 16384 (up to 4096 one wave per row, longer
+ *   rows split over two or four waves); other shapes return CQ_ERR_SHAPE
+ *   (use cq_gemv twice and
  *   cq_swiglu_quantize_q8_0).  An xq not 16-byte aligned returns
  *   CQ_ERR_ALIGNMENT.
  */

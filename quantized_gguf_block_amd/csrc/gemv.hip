@@ -32,13 +32,13 @@
 //    output in turn and stores silu(gate)*up after the reduction; MOE makes
 //    grid.y a token-expert pair whose expert id, activation row and output
 //    row offset the pointers at kernel start.
-//  * k-split form (KS = 4, rows of two to four wave widths): the four waves
-//    of a workgroup stream the same rows, each over its own k-slice, load
+//  * k-split form (rows of one to four wave widths): KS = 2 or 4 waves
+//    stream the same rows, each over its own k-slice, load
 //    their slice's activations per lane from global memory, and add their
 //    per-row sums in slice order through LDS after each group of P rows.
 // Shapes the streaming kernel does not cover (longer rows, rows that are not
-// whole 16-byte pieces, unaligned activations at one wave per row, rows
-// just over one wave width) use the general kernel: several waves per row,
+// whole 16-byte pieces, unaligned activations at one wave per row) use the
+// general kernel: several waves per row,
 // cooperative staging of row tiles in LDS, per-wave sums added in wave
 // order.
 #include "cq_device.h"
@@ -1264,14 +1264,13 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
         !((super || wt == T_Q1_0) && sc == 2)) {
         p.SC = sc;
-    } else if (rb % 16 == 0 && p.ncols >= 2 * kWave * p.C &&
+    } else if (rb % 16 == 0 && p.ncols > kWave * p.C &&
                p.ncols <= kGW * kWave * p.C && p.ncols % p.C == 0) {
-        // rows of two to four wave widths: the four waves of a workgroup
-        // split k (activations loaded per lane, so xq's alignment does not
-        // matter).  Below two widths (e.g. Q1_0 at k = 5120) the multi-wave
-        // tile kernel is faster: most of a k-split workgroup would idle.
+        // rows of one to four wave widths: two or four waves split k
+        // (activations loaded per lane, so xq's alignment does not matter).
         // k-split vs tile kernel, 4096 rows x 14336: Q8_0 b1 12.5 vs 17.1 us,
-        // Q4_K b1 9.0 vs 15.1 us, Q4_K b8 18.2 vs 31.2 us.
+        // Q4_K b1 9.0 vs 15.1 us, Q4_K b8 18.2 vs 31.2 us; 13824 x 5120
+        // (1.25 widths, two waves): Q4_K b1 13.0 vs 17.3 us.
         p.SC = p.C;
         p.KS = p.ncols <= 2 * kWave * p.C ? 2 : kGW;
     }
@@ -1340,7 +1339,8 @@ int launch_fmt_b(const Plan& p, const uint8_t* w, int64_t n, int64_t rb, const u
     int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
     // small workgroups (one or two waves) and up to two tiles per slot: one
     // workgroup per tile, so none runs a second tile after the others have
-    // finished (Q1_0 10240 x 5120, batch 1: 8.1 against 9.0 us); with larger
+    // finished (Q1_0 10240 x 5120 on this kernel, batch 1: 8.1 against
+    // 9.0 us); with larger
     // workgroups the extra resident ones slowed long rows at batch 8
     if (grid > ntiles || (p.nw <= 2 && ntiles <= 2 * grid)) grid = ntiles;
     const dim3 g(static_cast<unsigned>(grid)), b(p.nw * kWave);
@@ -1424,8 +1424,8 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
 
 // ---- fused gate/up GEMV + SwiGLU (decode FFN) -------------------------------
 // Streaming kernel only: one wave per row (k <= 4096) with a 16-byte aligned
-// xq, or its k-split form (rows of two to four wave widths, k = 8192..16384),
-// and whole 16-byte weight rows.
+// xq, or its k-split form (rows of up to four wave widths, k <= 16384), and
+// whole 16-byte weight rows.
 int gemv_swiglu_shape_ok(int wt, int64_t k, int64_t batch) {
     if (gemv_shape_ok(wt, k, batch) != 0) return -3;
     const Plan p = make_plan(wt, k, k / block_elems_of(wt) * block_bytes_of(wt),

@@ -93,7 +93,6 @@ def test_gemv_swiglu_validation(lib):
     A = (P(FAKE), P(FAKE))
     assert f(7, *A, 8, 256, P(FAKE), 1, P(FAKE), 8, None) == UNSUPPORTED
     assert f(2, *A, 8, 20480, P(FAKE), 1, P(FAKE), 8, None) == SHAPE    # five waves per row
-    assert f(2, *A, 8, 5120, P(FAKE), 1, P(FAKE), 8, None) == SHAPE     # 1.25 waves per row
     assert f(2, *A, 8, 352, P(FAKE), 1, P(FAKE), 8, None) == SHAPE      # not 16-byte rows
     assert f(14, *A, 8, 1024, P(FAKE), 1, P(FAKE), 8, None) == SHAPE    # Q6_K needs k % 2048
     assert f(2, *A, 8, 256, P(FAKE), 0, P(FAKE), 8, None) == INVALID    # batch 0

@@ -49,7 +49,8 @@ def check_against_oracle(orc, fmt, wg_h, wu_h, n, k, xq_h, batch, h):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n,k", [(1, 2048), (37, 256), (300, 1024), (1001, 2048), (257, 4096),
-                                 (45, 8192), (130, 14336), (3, 16384), (1, 8192), (3, 8192)])
+                                 (45, 8192), (130, 14336), (3, 16384), (1, 8192), (3, 8192),
+                                 (33, 5120)])
 def test_gemv_swiglu_small(cq, orc, fmt, n, k):
     if k % 256 or gs.row_bytes(fmt, k) % 16:
         pytest.skip("no single-pass kernel for this (type, k)")
@@ -98,8 +99,9 @@ def test_gemv_swiglu_strided_and_refusals(cq, orc):
     assert np.all(hh[:, n:] == -3.0)
     check_against_oracle(orc, fmt, wg_h, wu_h, n, k, xq_h, 2, hh[:, :n])
     # k = 20480 needs five waves per row (beyond the k-split form's four),
-    # k = 5120 one and a quarter: refused, nothing launched
-    for kk in (20480, 5120):
+    # k = 4160 gives rows that are not whole 16-byte pieces: refused,
+    # nothing launched
+    for kk in (20480, 4160):
         w8 = to_dev(gs.weights(fmt, 4, kk, cfg=821))
         x8 = to_dev(orc.quantize_q8_0(gs.activations(1, kk, cfg=821)))
         with pytest.raises(RuntimeError, match="SHAPE"):
