@@ -336,6 +336,21 @@ def secondary(cq, gs, dev, stream):
                 "graph_us": round(us, 2), "GB/s": round(gbs, 1),
                 "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
         del wd
+    # Q4_K rows of 1.25 and 2 wave widths (two-wave k-split streams): the
+    # FFN-up 13824 x 5120 of 13B-class models, the gate 28672 x 8192 of
+    # 70B-class models
+    for n, k in ((13824, 5120), (28672, 8192)):
+        xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(5, k, cfg=17)).to(dev))
+        y = torch.empty((5, n), dtype=torch.float32, device=dev)
+        wd = copies(gs.weights(gs.Q4_K, n, k, cfg=17))
+        for b in (1, 5):
+            us = _graph_us(lambda i: cq.cq_gemv(gs.Q4_K, wd[i % len(wd)], n, k, xq, b, y=y), 8, 50,
+                           stream)
+            gbs = wd[0].numel() / us / 1e3
+            out[f"q4_k_gemv_{n}x{k}_b{b}"] = {
+                "graph_us": round(us, 2), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+        del wd
     n, k = 14336, 4096
     # decode FFN front half, Q4_K gate/up 14336 x 4096: fused gate + up +
     # SwiGLU GEMV then the Q8_0 of h, against two GEMVs and the SwiGLU +
