@@ -223,6 +223,74 @@ def test_quantize_dequant_error_bound(orc):
     assert np.all(np.abs(xh - x) <= 0.5 * dd + 127 * np.abs(dd - amax / 127) + 1e-12)
 
 
+def _f32(r):
+    """The fp32 value nearest to the rational r (ties to even), normal range:
+    the rounding of one IEEE single-precision operation."""
+    if r == 0:
+        return Fraction(0)
+    sign, a = (-1, -r) if r < 0 else (1, r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def _rne_q(v):
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return max(-127, min(127, fl))
+
+
+def test_quantize_fp32_reciprocal_multiply(orc):
+    # The page's recipe (alice-llm 2.0.0 README, "The CPU Optimization
+    # Journey", Phase 4) takes scale = 127/amax as one fp32 value and then
+    # one fp32 multiply per element before rounding.  Near a half-integer
+    # that differs from dividing by the fp32 amax/127 and from the exact
+    # x*127/amax; elements placed there (found here with exact rationals,
+    # every step rounded to fp32 as the page's code does) must quantize to
+    # the page's value.
+    rng = np.random.default_rng(20261203)
+    cases, diff_div, diff_exact = [], 0, 0
+    while len(cases) < 96 or diff_div < 8 or diff_exact < 8:
+        amax = np.float32(rng.uniform(0.5, 8.0))
+        A = Fraction(float(amax))
+        inv = _f32(Fraction(127) / A)
+        q = int(rng.integers(-126, 126))
+        x = np.float32(float((Fraction(q) + Fraction(1, 2)) / inv))
+        x = x if rng.integers(2) else np.nextafter(x, np.float32(np.inf))
+        if not abs(x) < amax:
+            continue
+        X = Fraction(float(x))
+        page = _rne_q(_f32(X * inv))
+        div = _rne_q(_f32(X / _f32(A / 127)))
+        exact = _rne_q(X * 127 / A)
+        if page != div or page != exact:
+            cases.append((amax, x, page))
+            diff_div += page != div
+            diff_exact += page != exact
+    blocks = np.zeros((len(cases), 32), np.float32)
+    for i, (amax, x, _) in enumerate(cases):
+        blocks[i, 0] = amax
+        blocks[i, 1 + i % 31] = x
+    out = orc.quantize_q8_0(blocks.reshape(1, -1)).reshape(-1, 34)
+    for i, (amax, x, page) in enumerate(cases):
+        q = out[i, 2:].view(np.int8)
+        assert q[0] == 127
+        assert int(q[1 + i % 31]) == page, (float(amax), float(x), page, int(q[1 + i % 31]))
+        d16 = int(out[i, 0]) | (int(out[i, 1]) << 8)
+        assert d16 == int(np.float16(np.float32(amax) / np.float32(127)).view(np.uint16))
+
+
 # ------------------------------------------------------- matmul formulations
 def one_hot_rows(k, cols, value=3.0):
     x = np.zeros((len(cols), k), np.float32)
