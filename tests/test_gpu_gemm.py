@@ -1,7 +1,7 @@
 """GPU parity of the prefill GEMM (cq_gemm, int8 MFMA) against the fp64
 oracle: |y - y_ref| <= 2e-5 * sum|w_hat*x_hat| per output; small shapes
 with ragged M and N tails for every weight type, the prefill workload at
-M = 512 in full and at M = 2048 on sampled outputs, and invariants
+M = 512 and M = 2048 in full, and invariants
 (determinism, power-of-two scaling, GEMM rows against the GEMV)."""
 import numpy as np
 import pytest
@@ -44,22 +44,19 @@ def test_gemm_prefill_512_full(cq, orc):
 
 @pytest.mark.parametrize("name", ["q4_0_gemm_prefill_2048", "q5_k_gemm_prefill_512",
                                   "q6_k_gemm_prefill_512"])
-def test_gemm_prefill_sampled(cq, orc, name):
+def test_gemm_prefill_full(cq, orc, name):
+    """The 2048-token Q4_0 prefill and the 512-token Q5_K / Q6_K prefills:
+    every output against the oracle."""
     c = gs.CONFIGS[name]
     n, k, m = c["n"], c["k"], c["m"]
     w = gs.weights(c["fmt"], n, k, cfg=c["cfg"])
     x = gs.activations(m, k, cfg=c["cfg"])
     xq = orc.quantize_q8_0(x)
-    note("gemm prefill sampled", name)
+    note("gemm prefill", name)
     y = to_host(cq.cq_gemm(c["fmt"], to_dev(w), n, k, to_dev(xq), m))
-    rng = np.random.default_rng(12)
-    # every output of the first and last 128 x 128 tiles, plus random ones
-    mi = np.concatenate([np.repeat(np.arange(128), 4), np.repeat(np.arange(m - 128, m), 4),
-                         rng.integers(0, m, 6000)])
-    ni = np.concatenate([np.tile([0, 63, 64, 127], 128), np.tile([n - 128, n - 65, n - 64, n - 1], 128),
-                         rng.integers(0, n, 6000)])
-    y_ref, s_ref = orc.matmul_sampled(c["fmt"], w, n, k, xq, m, mi, ni)
-    assert_close_to_oracle(y[mi, ni], y_ref, s_ref, what=f"{name} sampled")
+    y_ref, s_ref = orc.matmul(c["fmt"], w, n, k, xq, m)
+    r = assert_close_to_oracle(y, y_ref, s_ref, what=name)
+    print(f"{name}: max |err|/S = {r:.3e}")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])

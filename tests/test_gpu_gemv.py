@@ -61,28 +61,23 @@ def test_gemv_config_full(cq, orc, name):
 
 
 @pytest.mark.parametrize("name", ["q4_k_gemv_lm_head", "q6_k_gemv_lm_head"])
-def test_gemv_lm_head_sampled(cq, orc, name):
+def test_gemv_lm_head_full(cq, orc, name):
     """LM head 128256 x 4096 (Q4_K; Q6_K, the tied-embedding type) at batch 1
-    and 4: every output of the first and last row tiles plus 4000 random
-    outputs against the oracle (both batches), and the batch-4 rows equal the
-    batch-1 results bitwise."""
+    and 4: every output of both calls against the oracle, and each batch-4
+    row equals the batch-1 call on that row bitwise."""
     c, w, x = config_inputs(name)
     n, k = c["n"], c["k"]
     xq = orc.quantize_q8_0(x)
     wd, xd = to_dev(w), to_dev(xq)
     note("gemv lm head b4", name)
     y4 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 4))
-    note("gemv lm head b1")
+    note("gemv lm head b1", name)
     y1 = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd, 1))
+    y_ref, s_ref = orc.matmul(c["fmt"], w, n, k, xq, 4)
+    r4 = assert_close_to_oracle(y4, y_ref, s_ref, what=f"{name} b4")
+    r1 = assert_close_to_oracle(y1, y_ref[:1], s_ref[:1], what=f"{name} b1")
+    print(f"{name}: max |err|/S = {r1:.3e} (batch 1), {r4:.3e} (batch 4)")
     assert np.array_equal(y4[0], y1[0])
-    rng = np.random.default_rng(11)
-    rows = np.concatenate([np.arange(0, 64), np.arange(n - 64, n), rng.integers(0, n, 4000)])
-    bs = np.concatenate([np.arange(128) % 4, rng.integers(0, 4, 4000)])
-    y_ref, s_ref = orc.matmul_sampled(c["fmt"], w, n, k, xq, 4, bs, rows)
-    assert_close_to_oracle(y4[bs, rows], y_ref, s_ref, what="lm head b4")
-    b0 = bs == 0
-    assert_close_to_oracle(y1[0, rows[b0]], y_ref[b0], s_ref[b0], what="lm head b1")
-    # each batch row separately equals a batch-1 call on that row
     for b in range(1, 4):
         yb = to_host(cq.cq_gemv(c["fmt"], wd, n, k, xd[b:b + 1], 1))
         assert np.array_equal(yb[0], y4[b])
