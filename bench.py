@@ -444,6 +444,7 @@ def secondary(cq, gs, dev, stream):
     xq = torch.empty((T, H // 32 * 34), dtype=torch.uint8, device=dev)
     offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
     pairs = torch.empty(T * K, dtype=torch.int32, device=dev)
+    gst = torch.zeros(1, dtype=torch.int32, device=dev)
     g = torch.empty((T * K, F), dtype=torch.float32, device=dev)
     u = torch.empty_like(g)
     hq = torch.empty((T * K, F // 32 * 34), dtype=torch.uint8, device=dev)
@@ -453,11 +454,11 @@ def secondary(cq, gs, dev, stream):
     def ffn(i):
         wg_, wu_, wd_ = sets[i % len(sets)]
         cq.cq_quantize_q8_0(x, xq)
-        cq.cq_moe_group(ids, E, offs, pairs)
-        cq.cq_moe_gemm(gs.Q4_K, wg_, E, F, H, xq, False, offs, pairs, T, K, y=g)
-        cq.cq_moe_gemm(gs.Q4_K, wu_, E, F, H, xq, False, offs, pairs, T, K, y=u)
+        cq.cq_moe_group(ids, E, offs, pairs, gst)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wg_, E, F, H, xq, False, offs, pairs, T, K, y=g)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wu_, E, F, H, xq, False, offs, pairs, T, K, y=u)
         cq.cq_swiglu_quantize_q8_0(g, u, hq=hq)
-        cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq, True, offs, pairs, T, K, y=d)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wd_, E, H, F, hq, True, offs, pairs, T, K, y=d)
         cq.cq_moe_combine(d, rw, y=yt)
 
     us = _burst_us(ffn, 50, stream)
@@ -482,19 +483,19 @@ def secondary(cq, gs, dev, stream):
     def ffn_decode(i):
         wg_, wu_, wd_ = sets[i % len(sets)]
         cq.cq_quantize_q8_0(x1, xq[:1])
-        cq.cq_moe_gemv_swiglu(gs.Q4_K, wg_, wu_, E, F, H, xq[:1], ids1, h=h1)
+        cq.cq_moe_gemv_swiglu(gs.Q4_K, wg_, wu_, E, F, H, xq[:1], ids1, h=h1, status=gst)
         cq.cq_quantize_q8_0(h1, hq1)
-        cq.cq_moe_gemv(gs.Q4_K, wd_, E, H, F, hq1, True, ids1, y=d1)
+        cq.cq_moe_gemv(gs.Q4_K, wd_, E, H, F, hq1, True, ids1, y=d1, status=gst)
         cq.cq_moe_combine(d1, rw1, y=y1)
 
     def ffn_decode_grouped(i):
         wg_, wu_, wd_ = sets[i % len(sets)]
         cq.cq_quantize_q8_0(x1, xq[:1])
-        cq.cq_moe_group(ids1, E, offs, pairs[:K])
-        cq.cq_moe_gemm(gs.Q4_K, wg_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=g[:K])
-        cq.cq_moe_gemm(gs.Q4_K, wu_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=u[:K])
+        cq.cq_moe_group(ids1, E, offs, pairs[:K], gst)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wg_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=g[:K])
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wu_, E, F, H, xq[:1], False, offs, pairs[:K], 1, K, y=u[:K])
         cq.cq_swiglu_quantize_q8_0(g[:K], u[:K], hq=hq1)
-        cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq1, True, offs, pairs[:K], 1, K, y=d1)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wd_, E, H, F, hq1, True, offs, pairs[:K], 1, K, y=d1)
         cq.cq_moe_combine(d1, rw1, y=y1)
 
     us_dec = _graph_us(ffn_decode, len(sets), 20, stream)

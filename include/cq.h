@@ -93,7 +93,7 @@ typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q5_K = 13
                CQ_Q6_K = 14,
                CQ_Q1_0 = 41 /* library-assigned: the pages give no GGUF id */ } cq_type;
 
-#define CQ_ABI_VERSION 1
+#define CQ_ABI_VERSION 2
 #define CQ_GEMV_MAX_BATCH 8
 #define CQ_MAX_K 65536
 #define CQ_GEMV_MAX_K 32768   /* cq_gemv: up to 8 waves of 64 lanes per row */
@@ -188,42 +188,105 @@ int cq_gemm(int wt, const void* w, int64_t n, int64_t k,
             cq_stream_t stream);
 
 /*
+ * Flags of cq_moe_gemm (one value from each pair, OR-ed):
+ *   CQ_MOE_X_PER_TOKEN  pair p = t*top_k + s reads activation row t of xq
+ *                       (the gate and up projections);
+ *   CQ_MOE_X_PER_PAIR   pair p reads activation row p (the down projection,
+ *                       whose input is the pair's own SwiGLU output);
+ *   CQ_MOE_OUT_PER_PAIR y row p = the pair's product row;
+ *   CQ_MOE_OUT_COMBINE  y row t = sum over s = 0..top_k-1, in slot order, of
+ *                       route_w[t*top_k + s] times the pair's product row
+ *                       (fp32), the routed FFN's output.
+ */
+#define CQ_MOE_X_PER_TOKEN 0
+#define CQ_MOE_X_PER_PAIR 1
+#define CQ_MOE_OUT_PER_PAIR 0
+#define CQ_MOE_OUT_COMBINE 2
+
+/*
+ * cq_moe_workspace_bytes -- device workspace cq_moe_gemm needs: a status
+ * word, the grouping of the n_tokens*top_k pairs by expert, and with
+ * CQ_MOE_OUT_COMBINE the fp32 product rows [n_tokens*top_k][n] that the
+ * slot-order combine reads (a deterministic sum without floating-point
+ * atomics needs every product before the first addition).  0 on bad sizes
+ * or flags.
+ */
+size_t cq_moe_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t n,
+                              int flags);
+
+/*
+ * cq_moe_gemm -- one routed-expert projection of a chunk of tokens, grouped
+ * so that each expert's weight matrix is read once for all of its pairs
+ * (Cera README, "Supported models": lfm2moe routes each token to its own 4
+ * of 32 experts, and grouping tokens by expert is the follow-up it names;
+ * alice-llm 2.0.0 README, "The GPU Optimization Journey", phase 6: no
+ * allocation per call, the caller owns the workspace).  For every pair
+ * p = t*top_k + s with e = expert_ids[p]:
+ *     P[p][i] = sum_j W_e_hat[i][j] * x_hat[row][j],  i < n,
+ * row = t (CQ_MOE_X_PER_TOKEN) or p (CQ_MOE_X_PER_PAIR); then y[p*ldy + i]
+ * = P[p][i] (CQ_MOE_OUT_PER_PAIR) or y[t*ldy + i] = sum_s route_w[p] *
+ * P[p][i] in slot order (CQ_MOE_OUT_COMBINE).
+ *   wt          CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K
+ *               (Q6_K: each expert's matrix under 2 GiB, else CQ_ERR_SHAPE).
+ *   w_experts   n_experts matrices [n][k/qk] back to back, 16-byte aligned.
+ *   xq          Q8_0 rows of k/32 blocks (n_tokens rows, or n_tokens*top_k
+ *               rows with CQ_MOE_X_PER_PAIR), 2-byte aligned.
+ *   expert_ids  device int32 [n_tokens][top_k].
+ *   route_w     device fp32 [n_tokens][top_k]; read only with
+ *               CQ_MOE_OUT_COMBINE (may be NULL otherwise).
+ *   y           fp32, rows of ldy >= n: n_tokens*top_k rows (per pair) or
+ *               n_tokens rows (combined), 4-byte aligned.
+ *   workspace   device memory, 256-byte aligned, ws_bytes >=
+ *               cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags),
+ *               else CQ_ERR_WORKSPACE.  Scratch, overwritten by each call;
+ *               calls that share a workspace must be ordered on one stream.
+ *   n_experts 1..1024, top_k 1..n_experts, n_tokens*top_k <= 2^24,
+ *   k a multiple of 256, k <= CQ_MAX_K.  Accuracy as cq_gemv.
+ * Expert ids live on the device and cannot be checked before the launch.
+ * After the stream reaches the call, the int32 at workspace offset 0 holds
+ * the number of ids outside [0, n_experts): 0 means every result is
+ * complete; otherwise those pairs were computed by no expert (a combined
+ * row leaves their slots out, a per-pair row of theirs is left unwritten)
+ * and the caller must treat the call as failed.
+ */
+int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int flags, const int32_t* expert_ids, const float* route_w,
+                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, void* workspace,
+                size_t ws_bytes, cq_stream_t stream);
+
+/*
+ * The routed projection in separate steps (cq_moe_gemm runs these three on
+ * its workspace), for callers that share one grouping between the gate, up
+ * and down projections:
+ *
  * cq_moe_group -- group the (token, slot) pairs of a top-k routing table by
- * expert (stable counting sort; Cera README, "Supported models": grouping
- * tokens by expert so an expert's weights are read once per chunk).
- *   expert_ids  int32 [n_tokens][top_k], each in [0, n_experts).
+ * expert (stable counting sort).
+ *   expert_ids  int32 [n_tokens][top_k].
  *   offsets     out int32 [n_experts + 1]: pairs of expert e are
  *               pairs[offsets[e] .. offsets[e+1]).
  *   pairs       out int32 [n_tokens*top_k]: pair ids p = t*top_k + s,
  *               ascending within each expert.
+ *   status      out device int32: the number of ids outside [0, n_experts)
+ *               (such pairs are in no group; 0 when the grouping is whole).
  *   n_experts <= 1024, top_k <= n_experts, n_tokens*top_k <= 2^24.
- * Ids outside [0, n_experts) are not checked on the host (they live on the
- * device); the kernel drops such pairs and offsets[n_experts] then falls
- * short of n_tokens*top_k, which the caller can check.
  */
 int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
-                 int64_t n_experts, int32_t* offsets, int32_t* pairs,
+                 int64_t n_experts, int32_t* offsets, int32_t* pairs, int32_t* status,
                  cq_stream_t stream);
 
 /*
- * cq_moe_gemm -- grouped expert projection.  For every expert e and every
- * pair p in pairs[offsets[e] .. offsets[e+1]):
+ * cq_moe_gemm_grouped -- the grouped product of cq_moe_gemm on a grouping
+ * written by cq_moe_group.  For every expert e and every pair p in
+ * pairs[offsets[e] .. offsets[e+1]):
  *     y[p*ldy + i] = sum_j W_e_hat[i][j] * x_hat[row][j],  i < n,
  * where row = p / top_k (x_per_pair = 0: gate/up read the token row) or
- * row = p (x_per_pair = 1: down reads the pair row).  Each expert's weight
- * matrix is streamed once for all of its pairs.
- *   wt         CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K (Q6_K:
- *              each expert's matrix under 2 GiB, else CQ_ERR_SHAPE).
- *   w_experts  n_experts matrices [n][k/qk], back to back, 16-B aligned.
- *   xq         Q8_0 rows of k/32 blocks (n_tokens or n_tokens*top_k rows).
- *   offsets, pairs  as written by cq_moe_group.
- *   y          fp32 [n_tokens*top_k][ldy], ldy >= n.
- *   k multiple of 256, k <= CQ_MAX_K.  Accuracy as cq_gemv.
+ * row = p (x_per_pair = 1: down reads the pair row).
+ *   Types, w_experts, xq, k as cq_moe_gemm; y fp32 [n_tokens*top_k][ldy].
  */
-int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
-                const void* xq, int x_per_pair, const int32_t* offsets,
-                const int32_t* pairs, int64_t n_tokens, int64_t top_k,
-                float* y, int64_t ldy, cq_stream_t stream);
+int cq_moe_gemm_grouped(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                        const void* xq, int x_per_pair, const int32_t* offsets,
+                        const int32_t* pairs, int64_t n_tokens, int64_t top_k,
+                        float* y, int64_t ldy, cq_stream_t stream);
 
 /*
  * cq_moe_gemv -- routed experts at decode: the same product as cq_moe_gemm
@@ -235,26 +298,31 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
  * twice: meant for decode and verify batches (Cera README, "Supported
  * models": lfm2moe's routed FFN; 1 token x top-4), where the grouped MFMA
  * path would run 16-token tiles with one live row.
- *   expert_ids  device int32 [n_tokens][top_k]; ids outside [0, n_experts)
- *               are clamped into range (they cannot be checked on the host).
+ *   expert_ids  device int32 [n_tokens][top_k].
+ *   status      device int32, an error counter the caller zeroes once: each
+ *               pair whose id lies outside [0, n_experts) adds 1 to it, and
+ *               its output row is set to 0 (no weights are read for it).
+ *               The library never clears it, so one check after many calls
+ *               covers them all (and graph replays need no reset node).
  *   xq          Q8_0 rows, 16-byte aligned; y fp32 [n_tokens*top_k][ldy].
  *   Shapes: as cq_gemv_swiglu with one wave per row only (k <= 4096),
  *   n_tokens*top_k <= 65535; else CQ_ERR_SHAPE.
  */
 int cq_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                 const void* xq, int x_per_pair, const int32_t* expert_ids,
-                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy,
+                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, int32_t* status,
                 cq_stream_t stream);
 
 /*
  * cq_moe_gemv_swiglu -- cq_moe_gemv over the gate and up expert matrices
  * fused with SwiGLU, as cq_gemv_swiglu per pair (x row = the pair's token):
  *     h[p*ldh + i] = silu(g) * u for the pair's expert.
+ * status as cq_moe_gemv (an invalid id gives h = 0 for its pair).
  */
 int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_experts,
                        int64_t n_experts, int64_t n, int64_t k, const void* xq,
                        const int32_t* expert_ids, int64_t n_tokens, int64_t top_k,
-                       float* h, int64_t ldh, cq_stream_t stream);
+                       float* h, int64_t ldh, int32_t* status, cq_stream_t stream);
 
 /*
  * cq_argmax_workspace_bytes -- bytes of device workspace cq_argmax needs for
@@ -287,7 +355,7 @@ int cq_argmax(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx
  * expert id first) and w[t][s] = their softmax over the chosen top_k only,
  * exp(l_s - l_0) / sum_j exp(l_j - l_0) in fp64 summed in slot order,
  * rounded once to fp32.  The output feeds cq_moe_group / cq_moe_gemv
- * (ids) and cq_moe_combine (w).
+ * (ids) and cq_moe_gemm / cq_moe_combine (w).
  *   logits     fp32 [rows][ld], ld >= n_experts, 4-byte aligned, no NaN.
  *   n_experts  1..1024; top_k 1..min(16, n_experts).
  *   ids        int32 [rows][top_k]; w fp32 [rows][top_k].
@@ -300,18 +368,20 @@ int cq_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_
  * (alice-llm 2.0.0 README, "The GPU Optimization Journey", phase 4: fused
  * gate/up SwiGLU), evaluated in fp64 from the fp32 inputs and rounded once
  * to fp32, then quantized to Q8_0 exactly as cq_quantize_q8_0.
- *   g, u   fp32 [rows][ld], 16-byte aligned, ld % 4 == 0, ld >= k.
- *   h_opt  optional fp32 [rows][k] output of h (NULL to skip).
- *   hq     out: rows*(k/32) Q8_0 blocks.
+ *   g, u   fp32 [rows][k], contiguous, 16-byte aligned.
+ *   h_opt  optional fp32 [rows][k] output of h (NULL to skip), 16-byte
+ *          aligned.
+ *   hq     out: rows*(k/32) Q8_0 blocks, 2-byte aligned.
+ *   k      multiple of 32, k <= CQ_MAX_K.
  */
-int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld,
-                            int64_t rows, int64_t k, float* h_opt, void* hq,
-                            cq_stream_t stream);
+int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t rows, int64_t k,
+                            float* h_opt, void* hq, cq_stream_t stream);
 
 /*
  * cq_moe_combine -- y[t*ldy + i] = sum over s = 0..top_k-1, in slot order,
  * of route_w[t*top_k + s] * d[(t*top_k + s)*n + i], fp32.
- *   d  fp32 [n_tokens*top_k][n] (as written by cq_moe_gemm with ldy = n).
+ *   d  fp32 [n_tokens*top_k][n] (as written by cq_moe_gemm_grouped or
+ *      cq_moe_gemv with ldy = n).
  */
 int cq_moe_combine(const float* d, const float* route_w, int64_t n_tokens,
                    int64_t top_k, int64_t n, float* y, int64_t ldy,

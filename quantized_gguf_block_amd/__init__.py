@@ -25,10 +25,15 @@ STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",
 
 EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
-    "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_group", "cq_moe_gemm",
-    "cq_swiglu_quantize_q8_0", "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu",
-    "cq_argmax_workspace_bytes", "cq_argmax", "cq_topk_softmax",
+    "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_workspace_bytes",
+    "cq_moe_gemm", "cq_moe_group", "cq_moe_gemm_grouped", "cq_swiglu_quantize_q8_0",
+    "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu", "cq_argmax_workspace_bytes",
+    "cq_argmax", "cq_topk_softmax",
 ]
+
+# cq_moe_gemm flags
+MOE_X_PER_TOKEN, MOE_X_PER_PAIR = 0, 1
+MOE_OUT_PER_PAIR, MOE_OUT_COMBINE = 0, 2
 
 
 class CQError(RuntimeError):
@@ -66,15 +71,18 @@ def load():
         "cq_gemv": (I, [I, P, I64, I64, P, I64, P, I64, P]),
         "cq_gemv_swiglu": (I, [I, P, P, I64, I64, P, I64, P, I64, P]),
         "cq_gemm": (I, [I, P, I64, I64, P, I64, P, I64, P]),
-        "cq_moe_group": (I, [P, I64, I64, I64, P, P, P]),
-        "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
-        "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, I64, P, P, P]),
+        "cq_moe_group": (I, [P, I64, I64, I64, P, P, P, P]),
+        "cq_moe_gemm_grouped": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
+        "cq_moe_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64, I64, I]),
+        "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P,
+                            ctypes.c_size_t, P]),
+        "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, P, P, P]),
         "cq_moe_combine": (I, [P, P, I64, I64, I64, P, I64, P]),
-        "cq_moe_gemv": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, I64, P]),
+        "cq_moe_gemv": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, I64, P, P]),
         "cq_argmax_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
         "cq_argmax": (I, [P, I64, I64, I64, P, P, ctypes.c_size_t, P]),
         "cq_topk_softmax": (I, [P, I64, I64, I64, I64, P, P, P]),
-        "cq_moe_gemv_swiglu": (I, [I, P, P, I64, I64, I64, P, P, I64, I64, P, I64, P]),
+        "cq_moe_gemv_swiglu": (I, [I, P, P, I64, I64, I64, P, P, I64, I64, P, I64, P, P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -173,8 +181,9 @@ def cq_gemm(wt, w, n, k, xq, m, y=None, ldy=None, stream=None):
     return y
 
 
-def cq_moe_group(expert_ids, n_experts, offsets=None, pairs=None, stream=None):
-    """expert_ids: int32 [n_tokens][top_k] -> (offsets int32 [E+1], pairs int32 [T*k])."""
+def cq_moe_group(expert_ids, n_experts, offsets=None, pairs=None, status=None, stream=None):
+    """expert_ids: int32 [n_tokens][top_k] -> (offsets int32 [E+1], pairs int32 [T*k],
+    status int32 [1]: the number of ids outside [0, E) once the stream has run)."""
     import torch
     _dev_tensor(expert_ids, "expert_ids", torch.int32)
     n_tokens, top_k = expert_ids.shape
@@ -183,47 +192,93 @@ def cq_moe_group(expert_ids, n_experts, offsets=None, pairs=None, stream=None):
         offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
     if pairs is None:
         pairs = torch.empty(max(n_tokens * top_k, 1), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
     _check("cq_moe_group", load().cq_moe_group(_ptr(expert_ids), n_tokens, top_k, n_experts,
-                                                _ptr(offsets), _ptr(pairs), _stream(stream)))
-    return offsets, pairs
+                                                _ptr(offsets), _ptr(pairs), _ptr(status),
+                                                _stream(stream)))
+    return offsets, pairs, status
 
 
-def cq_moe_gemm(wt, w_experts, n_experts, n, k, xq, x_per_pair, offsets, pairs, n_tokens,
-                top_k, y=None, ldy=None, stream=None):
-    """Grouped expert projection -> y fp32 [n_tokens*top_k][n], row = pair id."""
+def cq_moe_gemm_grouped(wt, w_experts, n_experts, n, k, xq, x_per_pair, offsets, pairs,
+                        n_tokens, top_k, y=None, ldy=None, stream=None):
+    """Grouped expert projection on a cq_moe_group grouping -> y fp32
+    [n_tokens*top_k][n], row = pair id."""
     import torch
     _dev_tensor(w_experts, "w_experts", torch.uint8)
     _dev_tensor(xq, "xq", torch.uint8)
     if y is None:
         y = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_experts.device)
     ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
-    _check("cq_moe_gemm", load().cq_moe_gemm(
+    _check("cq_moe_gemm_grouped", load().cq_moe_gemm_grouped(
         wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), int(bool(x_per_pair)), _ptr(offsets),
         _ptr(pairs), n_tokens, top_k, _ptr(y), ldy, _stream(stream)))
     return y
 
 
+def cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags):
+    return load().cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags)
+
+
+def cq_moe_gemm(wt, w_experts, n_experts, n, k, xq, flags, expert_ids, route_w=None, y=None,
+                ldy=None, workspace=None, stream=None):
+    """One routed-expert projection (grouping, grouped product and, with
+    MOE_OUT_COMBINE, the slot-order combine) -> (y, status): y fp32
+    [n_tokens*top_k][n] per pair or [n_tokens][n] combined; status the int32
+    workspace word that counts out-of-range expert ids."""
+    import torch
+    _dev_tensor(w_experts, "w_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(expert_ids, "expert_ids", torch.int32)
+    n_tokens, top_k = expert_ids.shape
+    rows = n_tokens if flags & MOE_OUT_COMBINE else n_tokens * top_k
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=w_experts.device)
+    _dev_tensor(y, "y", torch.float32)
+    if route_w is not None:
+        _dev_tensor(route_w, "route_w", torch.float32)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    need = load().cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=w_experts.device)
+    _dev_tensor(workspace, "workspace", torch.uint8)
+    _check("cq_moe_gemm", load().cq_moe_gemm(
+        wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), flags, _ptr(expert_ids), _ptr(route_w),
+        n_tokens, top_k, _ptr(y), ldy, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y, workspace[:4].view(torch.int32)
+
+
 def cq_swiglu_quantize_q8_0(g, u, h=None, want_h=False, hq=None, stream=None):
-    """h = silu(g)*u (fp64 inside, fp32 out), quantized to Q8_0 -> (h or None, hq)."""
+    """h = silu(g)*u (fp64 inside, fp32 out), quantized to Q8_0 -> (h or None, hq).
+    g, u: contiguous fp32 [rows][k]."""
     import torch
     _dev_tensor(g, "g", torch.float32)
     _dev_tensor(u, "u", torch.float32)
     rows, k = g.shape
-    if u.shape != g.shape or u.stride() != g.stride() or g.stride(1) != 1:
-        raise ValueError("g and u must have the same shape and row stride")
+    if u.shape != g.shape or not g.is_contiguous() or not u.is_contiguous():
+        raise ValueError("g and u must be contiguous and of the same shape")
     if h is None and want_h:
         h = torch.empty((rows, k), dtype=torch.float32, device=g.device)
     if hq is None:
         hq = torch.empty((rows, k // 32 * 34), dtype=torch.uint8, device=g.device)
     _check("cq_swiglu_quantize_q8_0", load().cq_swiglu_quantize_q8_0(
-        _ptr(g), _ptr(u), g.stride(0) if rows > 1 else k, rows, k, _ptr(h), _ptr(hq),
-        _stream(stream)))
+        _ptr(g), _ptr(u), rows, k, _ptr(h), _ptr(hq), _stream(stream)))
     return h, hq
 
 
+def _status_counter(status, dev):
+    import torch
+    if status is None:
+        return torch.zeros(1, dtype=torch.int32, device=dev)
+    _dev_tensor(status, "status", torch.int32)
+    return status
+
+
 def cq_moe_gemv(wt, w_experts, n_experts, n, k, xq, x_per_pair, expert_ids, y=None, ldy=None,
-                stream=None):
-    """Decode routed experts: y[t*top_k+s] = W[ids[t][s]] x_hat[t or t*top_k+s] (one GEMV per pair)."""
+                status=None, stream=None):
+    """Decode routed experts: y[t*top_k+s] = W[ids[t][s]] x_hat[t or t*top_k+s]
+    (one GEMV per pair) -> (y, status): status is the int32 error counter (a
+    fresh zeroed one unless given) to which every out-of-range id adds 1."""
     import torch
     _dev_tensor(w_experts, "w_experts", torch.uint8)
     _dev_tensor(xq, "xq", torch.uint8)
@@ -232,16 +287,18 @@ def cq_moe_gemv(wt, w_experts, n_experts, n, k, xq, x_per_pair, expert_ids, y=No
     if y is None:
         y = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_experts.device)
     _dev_tensor(y, "y", torch.float32)
+    status = _status_counter(status, w_experts.device)
     ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
     _check("cq_moe_gemv", load().cq_moe_gemv(wt, _ptr(w_experts), n_experts, n, k, _ptr(xq),
                                               int(bool(x_per_pair)), _ptr(expert_ids), n_tokens,
-                                              top_k, _ptr(y), ldy, _stream(stream)))
-    return y
+                                              top_k, _ptr(y), ldy, _ptr(status), _stream(stream)))
+    return y, status
 
 
 def cq_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq, expert_ids,
-                       h=None, ldh=None, stream=None):
-    """Decode routed gate/up + SwiGLU: h[t*top_k+s] = silu(Wg_e x_t) * (Wu_e x_t), e = ids[t][s]."""
+                       h=None, ldh=None, status=None, stream=None):
+    """Decode routed gate/up + SwiGLU: h[t*top_k+s] = silu(Wg_e x_t) * (Wu_e x_t),
+    e = ids[t][s] -> (h, status) as cq_moe_gemv."""
     import torch
     _dev_tensor(w_gate_experts, "w_gate_experts", torch.uint8)
     _dev_tensor(w_up_experts, "w_up_experts", torch.uint8)
@@ -251,11 +308,12 @@ def cq_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq, ex
     if h is None:
         h = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=w_gate_experts.device)
     _dev_tensor(h, "h", torch.float32)
+    status = _status_counter(status, w_gate_experts.device)
     ldh = ldh if ldh is not None else (h.stride(0) if h.dim() == 2 else n)
     _check("cq_moe_gemv_swiglu", load().cq_moe_gemv_swiglu(
         wt, _ptr(w_gate_experts), _ptr(w_up_experts), n_experts, n, k, _ptr(xq), _ptr(expert_ids),
-        n_tokens, top_k, _ptr(h), ldh, _stream(stream)))
-    return h
+        n_tokens, top_k, _ptr(h), ldh, _ptr(status), _stream(stream)))
+    return h, status
 
 
 def cq_argmax(y, idx=None, workspace=None, stream=None):

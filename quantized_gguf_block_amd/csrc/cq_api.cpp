@@ -161,32 +161,33 @@ static int check_moe_gemv(int wt, const void* w, int64_t n_experts, int64_t n, i
 
 int cq_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                 const void* xq, int x_per_pair, const int32_t* expert_ids, int64_t n_tokens,
-                int64_t top_k, float* y, int64_t ldy, cq_stream_t stream) {
+                int64_t top_k, float* y, int64_t ldy, int32_t* status, cq_stream_t stream) {
     if (x_per_pair != 0 && x_per_pair != 1) return CQ_ERR_INVALID_ARG;
     if (int rc = check_moe_gemv(wt, w_experts, n_experts, n, k, expert_ids, n_tokens, top_k, ldy))
         return rc;
     if (n == 0 || n_tokens == 0) return CQ_OK;
-    if (!xq || !expert_ids || !y) return CQ_ERR_INVALID_ARG;
-    if (!aligned(xq, 16) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
+    if (!xq || !expert_ids || !y || !status) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(y, 4) || !aligned(status, 4)) return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
     return status_of(launch_moe_gemv(wt, w_experts, n_experts, n, k, xq, x_per_pair, expert_ids,
-                                     n_tokens, top_k, y, ldy, reinterpret_cast<hipStream_t>(stream)));
+                                     n_tokens, top_k, y, ldy, status,
+                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
 int cq_moe_gemv_swiglu(int wt, const void* w_gate_experts, const void* w_up_experts,
                        int64_t n_experts, int64_t n, int64_t k, const void* xq,
                        const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, float* h,
-                       int64_t ldh, cq_stream_t stream) {
+                       int64_t ldh, int32_t* status, cq_stream_t stream) {
     if (int rc = check_moe_gemv(wt, w_gate_experts, n_experts, n, k, expert_ids, n_tokens, top_k,
                                 ldh))
         return rc;
     if (int rc = check_weights(wt, w_up_experts, n, k)) return rc;
     if (n == 0 || n_tokens == 0) return CQ_OK;
-    if (!xq || !expert_ids || !h) return CQ_ERR_INVALID_ARG;
-    if (!aligned(xq, 16) || !aligned(h, 4)) return CQ_ERR_ALIGNMENT;
+    if (!xq || !expert_ids || !h || !status) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(h, 4) || !aligned(status, 4)) return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
     return status_of(launch_moe_gemv_swiglu(wt, w_gate_experts, w_up_experts, n_experts, n, k, xq,
-                                            expert_ids, n_tokens, top_k, h, ldh,
+                                            expert_ids, n_tokens, top_k, h, ldh, status,
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -237,27 +238,38 @@ int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t
 }
 
 int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
-                 int32_t* offsets, int32_t* pairs, cq_stream_t stream) {
+                 int32_t* offsets, int32_t* pairs, int32_t* status, cq_stream_t stream) {
     if (n_tokens < 0 || top_k < 1 || n_experts < 1 || n_experts > 1024 || top_k > n_experts)
         return CQ_ERR_INVALID_ARG;
     if (n_tokens * top_k > (int64_t(1) << 24)) return CQ_ERR_SHAPE;
-    if (!offsets || (n_tokens > 0 && (!expert_ids || !pairs))) return CQ_ERR_INVALID_ARG;
-    if (!aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(pairs, 4))
+    if (!offsets || !status || (n_tokens > 0 && (!expert_ids || !pairs))) return CQ_ERR_INVALID_ARG;
+    if (!aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(pairs, 4) ||
+        !aligned(status, 4))
         return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
     return status_of(launch_moe_group(expert_ids, n_tokens, top_k, n_experts, offsets, pairs,
-                                      reinterpret_cast<hipStream_t>(stream)));
+                                      status, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
-                const void* xq, int x_per_pair, const int32_t* offsets, const int32_t* pairs,
-                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, cq_stream_t stream) {
+// shared checks of the grouped expert products (one-call and split forms)
+static int check_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                          int64_t n_tokens, int64_t top_k, int64_t ldy) {
     if (int rc = check_weights(wt, w_experts, n, k)) return rc;
     if (wt == CQ_Q1_0) return CQ_ERR_UNSUPPORTED_TYPE;
-    if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || ldy < n ||
-        (x_per_pair != 0 && x_per_pair != 1))
+    if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || top_k > n_experts ||
+        ldy < n)
         return CQ_ERR_INVALID_ARG;
     if (k % 256 != 0 || moe_shape_ok(wt, n, k) != 0) return CQ_ERR_SHAPE;
+    if (n_tokens * top_k > (int64_t(1) << 24)) return CQ_ERR_SHAPE;
+    return CQ_OK;
+}
+
+int cq_moe_gemm_grouped(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                        const void* xq, int x_per_pair, const int32_t* offsets,
+                        const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
+                        int64_t ldy, cq_stream_t stream) {
+    if (x_per_pair != 0 && x_per_pair != 1) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_moe_gemm(wt, w_experts, n_experts, n, k, n_tokens, top_k, ldy)) return rc;
     if (n == 0 || n_tokens == 0) return CQ_OK;
     if (!xq || !offsets || !pairs || !y) return CQ_ERR_INVALID_ARG;
     if (!aligned(xq, 2) || !aligned(offsets, 4) || !aligned(pairs, 4) || !aligned(y, 4))
@@ -268,17 +280,52 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
-int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld, int64_t rows, int64_t k,
+static bool moe_flags_ok(int flags) {
+    return (flags & ~(CQ_MOE_X_PER_PAIR | CQ_MOE_OUT_COMBINE)) == 0;
+}
+
+size_t cq_moe_workspace_bytes(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t n,
+                              int flags) {
+    if (n_tokens < 0 || top_k < 1 || n_experts < 1 || n_experts > 1024 || top_k > n_experts ||
+        n < 0 || !moe_flags_ok(flags) || n_tokens * top_k > (int64_t(1) << 24) ||
+        n > (int64_t(1) << 24))
+        return 0;
+    return static_cast<size_t>(moe_layout(n_tokens, top_k, n_experts, n, flags).total);
+}
+
+int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                const void* xq, int flags, const int32_t* expert_ids, const float* route_w,
+                int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, void* workspace,
+                size_t ws_bytes, cq_stream_t stream) {
+    if (!moe_flags_ok(flags)) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_moe_gemm(wt, w_experts, n_experts, n, k, n_tokens, top_k, ldy)) return rc;
+    if (n > (int64_t(1) << 24)) return CQ_ERR_SHAPE;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    const bool combine = (flags & CQ_MOE_OUT_COMBINE) != 0;
+    if (!xq || !expert_ids || !y || !workspace || (combine && !route_w)) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(expert_ids, 4) || !aligned(y, 4) ||
+        (combine && !aligned(route_w, 4)))
+        return CQ_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256) ||
+        ws_bytes < cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags))
+        return CQ_ERR_WORKSPACE;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_routed(wt, w_experts, n_experts, n, k, xq, flags, expert_ids,
+                                       route_w, n_tokens, top_k, y, ldy,
+                                       static_cast<uint8_t*>(workspace),
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_swiglu_quantize_q8_0(const float* g, const float* u, int64_t rows, int64_t k,
                             float* h_opt, void* hq, cq_stream_t stream) {
-    if (rows < 0 || k <= 0 || ld < k) return CQ_ERR_INVALID_ARG;
+    if (rows < 0 || k <= 0) return CQ_ERR_INVALID_ARG;
     if (k % 32 != 0 || k > CQ_MAX_K) return CQ_ERR_SHAPE;
     if (rows == 0) return CQ_OK;
     if (!g || !u || !hq) return CQ_ERR_INVALID_ARG;
-    if (!aligned(g, 16) || !aligned(u, 16) || ld % 4 != 0 || !aligned(h_opt, 16) ||
-        !aligned(hq, 2))
+    if (!aligned(g, 16) || !aligned(u, 16) || !aligned(h_opt, 16) || !aligned(hq, 2))
         return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
-    return status_of(launch_swiglu_quantize_q8_0(g, u, ld, rows, k, h_opt, hq,
+    return status_of(launch_swiglu_quantize_q8_0(g, u, k, rows, k, h_opt, hq,
                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -289,7 +336,7 @@ int cq_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64
     if (!d || !route_w || !y) return CQ_ERR_INVALID_ARG;
     if (!aligned(d, 4) || !aligned(route_w, 4) || !aligned(y, 4)) return CQ_ERR_ALIGNMENT;
     if (int rc = check_device()) return rc;
-    return status_of(launch_moe_combine(d, route_w, n_tokens, top_k, n, y, ldy,
+    return status_of(launch_moe_combine(d, route_w, n_tokens, top_k, n, y, ldy, nullptr, 0,
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 

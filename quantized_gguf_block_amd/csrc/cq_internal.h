@@ -20,11 +20,11 @@ int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, 
                        const void* xq, int64_t batch, float* h, int64_t ldh, hipStream_t stream);
 int launch_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                     const void* xq, int x_per_pair, const int32_t* ids, int64_t n_tokens,
-                    int64_t top_k, float* y, int64_t ldy, hipStream_t stream);
+                    int64_t top_k, float* y, int64_t ldy, int32_t* status, hipStream_t stream);
 int launch_moe_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n_experts,
                            int64_t n, int64_t k, const void* xq, const int32_t* ids,
                            int64_t n_tokens, int64_t top_k, float* h, int64_t ldh,
-                           hipStream_t stream);
+                           int32_t* status, hipStream_t stream);
 int64_t argmax_chunks(int64_t n);
 int launch_argmax(const float* y, int64_t rows, int64_t n, int64_t ldy, int32_t* idx, void* ws,
                   hipStream_t stream);
@@ -33,12 +33,26 @@ int launch_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, in
 int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m,
                 float* y, int64_t ldy, hipStream_t stream);
 int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
-                     int32_t* offsets, int32_t* pairs, hipStream_t stream);
+                     int32_t* offsets, int32_t* pairs, int32_t* status, hipStream_t stream);
 int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
                     const void* xq, int x_per_pair, const int32_t* offsets,
                     const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
                     int64_t ldy, hipStream_t stream);
 int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
-                       int64_t n, float* y, int64_t ldy, hipStream_t stream);
+                       int64_t n, float* y, int64_t ldy, const int32_t* ids, int64_t n_experts,
+                       hipStream_t stream);
+
+// One-call routed projection: flag bits as CQ_MOE_* in cq.h.
+constexpr int kMoeXPerPair = 1;
+constexpr int kMoeOutCombine = 2;
+// Byte offsets of the parts of the one-call workspace, and its total size.
+struct MoeLayout {
+    int64_t status, offsets, pairs, prod, total;
+};
+MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t n, int flags);
+int launch_moe_routed(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                      const void* xq, int flags, const int32_t* ids, const float* route_w,
+                      int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, uint8_t* ws,
+                      hipStream_t stream);
 
 }  // namespace cq

@@ -839,14 +839,17 @@ template <int FMT, int B, int C>
 constexpr int kActMax = B * (kSuper<FMT> || FMT == T_Q1_0 ? 128 : 64) * C * 34;
 
 // Routed-expert addressing for decode (MOE): blockIdx.y is the
-// token-expert pair p = t*top_k + s; its matrix is expert ids[p] (clamped
-// to the expert count) of the n_experts back-to-back matrices of mat_bytes
-// each, its activation row is xq row p (x_per_pair) or t, and its output
-// row is y + p*ldy.
+// token-expert pair p = t*top_k + s; its matrix is expert ids[p] of the
+// n_experts back-to-back matrices of mat_bytes each, its activation row is
+// xq row p (x_per_pair) or t, and its output row is y + p*ldy.  An id
+// outside [0, n_experts) reads no weights (its rows stream as zeros, so its
+// outputs are exactly 0) and adds 1 to *status (once per pair, from the
+// pair's first workgroup).
 struct MoeMap {
     const int32_t* ids;
     int64_t mat_bytes;
     int n_experts, top_k, x_per_pair;
+    int32_t* status;
 };
 
 // SW: fused gate/up + SwiGLU.  Then w is the gate matrix, w2 the up matrix,
@@ -863,11 +866,16 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         const uint8_t* __restrict__ xq, int64_t xq_row_bytes, float* __restrict__ y,
         int64_t ldy, const uint8_t* __restrict__ w2 = nullptr, MoeMap mm = {}) {
     static_assert(KS == 1 || (!MOE && kGW % KS == 0), "k-split: plain or fused GEMV, whole streams per workgroup");
+    bool rows_live = true;   // false: every weight row reads as zeros
     if constexpr (MOE) {
         static_assert(B == 1, "one activation row per token-expert pair");
         const int pr = static_cast<int>(blockIdx.y);
         int e = mm.ids[pr];
-        e = e < 0 ? 0 : (e >= mm.n_experts ? mm.n_experts - 1 : e);
+        if (e < 0 || e >= mm.n_experts) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(mm.status, 1);
+            e = 0;
+            rows_live = false;
+        }
         w += static_cast<int64_t>(e) * mm.mat_bytes;
         if constexpr (SW) w2 += static_cast<int64_t>(e) * mm.mat_bytes;
         xq += static_cast<int64_t>(mm.x_per_pair ? pr : pr / mm.top_k) * xq_row_bytes;
@@ -933,7 +941,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // runs up to P-1 rows ahead of the wave's last row), read as zeros
     // without memory traffic; they are staged or computed and never stored.
     auto load_row = [&](int64_t r, u32x4* d) {
-        const bool in = r < rend;
+        const bool in = r < rend && rows_live;
         const uint8_t* base;
         if constexpr (SW) base = ((r & 1) ? w2 : w) + (in ? r >> 1 : 0) * rb;
         else base = w + (in ? r : 0) * rb;
@@ -1518,12 +1526,14 @@ int launch_moe_gemv_fmt(int SC, const uint8_t* w, const uint8_t* w2, int64_t n, 
 template <bool SW>
 int launch_moe_gemv_any(int wt, const void* w, const void* w2, int64_t n_experts, int64_t n,
                         int64_t k, const void* xq, int x_per_pair, const int32_t* ids,
-                        int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, hipStream_t s) {
+                        int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, int32_t* status,
+                        hipStream_t s) {
     const int64_t npairs = n_tokens * top_k;
     if (moe_gemv_shape_ok(wt, k, npairs) != 0) return -3;
     const int64_t rb = k / block_elems_of(wt) * block_bytes_of(wt);
     const Plan p = make_plan(wt, k, rb, 1, true);
-    const MoeMap mm{ids, n * rb, static_cast<int>(n_experts), static_cast<int>(top_k), x_per_pair};
+    const MoeMap mm{ids, n * rb, static_cast<int>(n_experts), static_cast<int>(top_k), x_per_pair,
+                    status};
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     const uint8_t* wp2 = static_cast<const uint8_t*>(w2);
     const uint8_t* xp = static_cast<const uint8_t*>(xq);
@@ -1543,17 +1553,17 @@ int launch_moe_gemv_any(int wt, const void* w, const void* w2, int64_t n_experts
 
 int launch_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                     const void* xq, int x_per_pair, const int32_t* ids, int64_t n_tokens,
-                    int64_t top_k, float* y, int64_t ldy, hipStream_t stream) {
+                    int64_t top_k, float* y, int64_t ldy, int32_t* status, hipStream_t stream) {
     return launch_moe_gemv_any<false>(wt, w_experts, nullptr, n_experts, n, k, xq, x_per_pair, ids,
-                                      n_tokens, top_k, y, ldy, stream);
+                                      n_tokens, top_k, y, ldy, status, stream);
 }
 
 int launch_moe_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n_experts,
                            int64_t n, int64_t k, const void* xq, const int32_t* ids,
                            int64_t n_tokens, int64_t top_k, float* h, int64_t ldh,
-                           hipStream_t stream) {
+                           int32_t* status, hipStream_t stream) {
     return launch_moe_gemv_any<true>(wt, w_gate, w_up, n_experts, n, k, xq, 0, ids, n_tokens,
-                                     top_k, h, ldh, stream);
+                                     top_k, h, ldh, status, stream);
 }
 
 }  // namespace cq

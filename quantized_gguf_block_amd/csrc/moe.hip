@@ -15,24 +15,34 @@ namespace cq {
 //       fill[e] + (same-expert pairs in earlier waves) + (lower lanes of its group)
 //     which is its rank in ascending pair order.  No step depends on thread
 //     timing, so the output is deterministic.
+// Pairs whose id lies outside [0, n_experts) are placed in no group; their
+// count is stored to *status (0 when every id is valid), so a caller that
+// reads it after the stream reaches this kernel knows whether the grouping
+// is whole.
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kMaxExperts = 1024;
 
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
         const int32_t* __restrict__ ids, int np, int n_experts, int32_t* __restrict__ offsets,
-        int32_t* __restrict__ pairs) {
+        int32_t* __restrict__ pairs, int32_t* __restrict__ status) {
     __shared__ int fill[kMaxExperts];
     __shared__ uint16_t wcnt[kGroupWaves][kMaxExperts];
+    __shared__ int invalid;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
 
     for (int e = t; e < n_experts; e += kGroupThreads) fill[e] = 0;
+    if (t == 0) invalid = 0;
     __syncthreads();
+    int bad = 0;
     for (int p = t; p < np; p += kGroupThreads) {
         const int e = ids[p];
         if (e >= 0 && e < n_experts) atomicAdd(&fill[e], 1);
+        else ++bad;
     }
+    if (bad) atomicAdd(&invalid, bad);
     __syncthreads();
+    if (t == 0) *status = invalid;
     // exclusive scan of the counts by wave 0, 64 experts at a time (a
     // wave-level inclusive scan plus the running carry)
     if (wv == 0) {
@@ -95,21 +105,25 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(
 }
 
 int launch_moe_group(const int32_t* ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
-                     int32_t* offsets, int32_t* pairs, hipStream_t stream) {
+                     int32_t* offsets, int32_t* pairs, int32_t* status, hipStream_t stream) {
     const int np = static_cast<int>(n_tokens * top_k);
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, stream, ids, np,
-                       static_cast<int>(n_experts), offsets, pairs);
+                       static_cast<int>(n_experts), offsets, pairs, status);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 // ---- combine: y[t] = sum_s w[t,s] * d[t*k+s] in slot order ---------------
 // Workgroup (column chunk, tokens blockIdx.y, + gridDim.y, ...): each thread
 // four consecutive columns, with 16-byte loads and stores when d and y allow
-// them; the route weights of a token are wave-uniform.
+// them; the route weights of a token are wave-uniform.  With ids given (the
+// one-call routed projection), a slot whose id lies outside [0, n_experts)
+// has no product row and adds nothing.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ d,
                                                           const float* __restrict__ rw,
                                                           int64_t n_tokens, int top_k, int64_t n,
-                                                          float* __restrict__ y, int64_t ldy) {
+                                                          float* __restrict__ y, int64_t ldy,
+                                                          const int32_t* __restrict__ ids,
+                                                          int n_experts) {
     const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (c >= n) return;
     const bool vec = (n & 3) == 0 && (ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(d) & 15) == 0 &&
@@ -119,6 +133,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
         if (vec) {
             float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             for (int s = 0; s < top_k; ++s) {
+                if (ids) {
+                    const int e = ids[t * top_k + s];
+                    if (e < 0 || e >= n_experts) continue;
+                }
                 const float wgt = rw[t * top_k + s];
                 const float4 v = *reinterpret_cast<const float4*>(dp + s * n + c);
                 acc.x = fmaf(wgt, v.x, acc.x);
@@ -130,7 +148,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
         } else {
             for (int64_t cc = c; cc < c + 4 && cc < n; ++cc) {
                 float acc = 0.0f;
-                for (int s = 0; s < top_k; ++s) acc = fmaf(rw[t * top_k + s], dp[s * n + cc], acc);
+                for (int s = 0; s < top_k; ++s) {
+                    if (ids) {
+                        const int e = ids[t * top_k + s];
+                        if (e < 0 || e >= n_experts) continue;
+                    }
+                    acc = fmaf(rw[t * top_k + s], dp[s * n + cc], acc);
+                }
                 y[t * ldy + cc] = acc;
             }
         }
@@ -138,13 +162,53 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
 }
 
 int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
-                       int64_t n, float* y, int64_t ldy, hipStream_t stream) {
+                       int64_t n, float* y, int64_t ldy, const int32_t* ids, int64_t n_experts,
+                       hipStream_t stream) {
     const int64_t gx = (n + 1023) / 1024;
     const int64_t gy = n_tokens < 4096 ? n_tokens : 4096;
     if (gx > 0x7FFFFFFF) return -3;
     hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                       dim3(256), 0, stream, d, route_w, n_tokens, static_cast<int>(top_k), n, y, ldy);
+                       dim3(256), 0, stream, d, route_w, n_tokens, static_cast<int>(top_k), n, y, ldy,
+                       ids, static_cast<int>(n_experts));
     return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// ---- the one-call routed projection ------------------------------------------
+// Workspace layout (each part 256-byte aligned): the status word, the
+// offsets [n_experts + 1], the grouped pair list [n_tokens * top_k] and,
+// when the per-pair products are combined, those products fp32
+// [n_tokens * top_k][n].
+static int64_t align256(int64_t b) { return (b + 255) & ~static_cast<int64_t>(255); }
+
+MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t n, int flags) {
+    MoeLayout L;
+    const int64_t np = n_tokens * top_k;
+    L.status = 0;
+    L.offsets = 256;
+    L.pairs = L.offsets + align256(4 * (n_experts + 1));
+    L.prod = L.pairs + align256(4 * (np > 0 ? np : 1));
+    L.total = (flags & kMoeOutCombine) ? L.prod + align256(4 * np * n) : L.prod;
+    return L;
+}
+
+int launch_moe_routed(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                      const void* xq, int flags, const int32_t* ids, const float* route_w,
+                      int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, uint8_t* ws,
+                      hipStream_t stream) {
+    const MoeLayout L = moe_layout(n_tokens, top_k, n_experts, n, flags);
+    int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
+    const bool combine = (flags & kMoeOutCombine) != 0;
+    if (int rc = launch_moe_group(ids, n_tokens, top_k, n_experts, offsets, pairs, status, stream))
+        return rc;
+    float* prod = combine ? reinterpret_cast<float*>(ws + L.prod) : y;
+    if (int rc = launch_moe_gemm(wt, w, n_experts, n, k, xq, (flags & kMoeXPerPair) ? 1 : 0,
+                                 offsets, pairs, n_tokens, top_k, prod, combine ? n : ldy, stream))
+        return rc;
+    if (combine)
+        return launch_moe_combine(prod, route_w, n_tokens, top_k, n, y, ldy, ids, n_experts, stream);
+    return 0;
 }
 
 }  // namespace cq

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cq_abi_version() == 1
+    assert lib.cq_abi_version() == 2
     for code, name in cq.STATUS.items():
         assert lib.cq_status_string(code).decode().startswith(name)
     assert b"unknown" in lib.cq_status_string(12345)
@@ -105,19 +105,24 @@ def test_gemv_swiglu_validation(lib):
 def test_moe_gemv_validation(lib):
     f = lib.cq_moe_gemv
     A = (P(FAKE), 32, 64, 2048)
-    assert f(7, *A, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == UNSUPPORTED
-    assert f(12, *A, P(FAKE), 2, P(FAKE), 1, 4, P(FAKE), 64, None) == INVALID   # x_per_pair
-    assert f(12, *A, P(FAKE), 0, P(FAKE), 1, 40, P(FAKE), 64, None) == INVALID  # top_k > E
-    assert f(12, P(FAKE), 32, 64, 8192, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == SHAPE
-    assert f(12, *A, P(FAKE), 0, P(FAKE), 20000, 4, P(FAKE), 64, None) == SHAPE  # > 65535 pairs
-    assert f(12, *A, P(FAKE + 2), 0, P(FAKE), 1, 4, P(FAKE), 64, None) == ALIGN  # xq
-    assert f(12, *A, P(FAKE), 0, P(FAKE + 2), 1, 4, P(FAKE), 64, None) == ALIGN  # ids
-    assert f(12, *A, P(FAKE), 0, P(FAKE), 0, 4, P(FAKE), 64, None) == OK         # no tokens
+    S = P(FAKE + 64)   # status counter
+    assert f(7, *A, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, S, None) == UNSUPPORTED
+    assert f(12, *A, P(FAKE), 2, P(FAKE), 1, 4, P(FAKE), 64, S, None) == INVALID   # x_per_pair
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 1, 40, P(FAKE), 64, S, None) == INVALID  # top_k > E
+    assert f(12, P(FAKE), 32, 64, 8192, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, S, None) == SHAPE
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 20000, 4, P(FAKE), 64, S, None) == SHAPE  # > 65535 pairs
+    assert f(12, *A, P(FAKE + 2), 0, P(FAKE), 1, 4, P(FAKE), 64, S, None) == ALIGN  # xq
+    assert f(12, *A, P(FAKE), 0, P(FAKE + 2), 1, 4, P(FAKE), 64, S, None) == ALIGN  # ids
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, None, None) == INVALID  # no status
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 1, 4, P(FAKE), 64, P(FAKE + 2), None) == ALIGN
+    assert f(12, *A, P(FAKE), 0, P(FAKE), 0, 4, P(FAKE), 64, S, None) == OK         # no tokens
     g = lib.cq_moe_gemv_swiglu
     assert g(12, P(FAKE), P(FAKE + 8), 32, 64, 2048, P(FAKE), P(FAKE), 1, 4, P(FAKE), 64,
-             None) == ALIGN                                                      # w_up
+             S, None) == ALIGN                                                      # w_up
     assert g(12, P(FAKE), P(FAKE), 32, 64, 2048, P(FAKE), P(FAKE), 1, 4, P(FAKE), 63,
-             None) == INVALID                                                    # ldh < n
+             S, None) == INVALID                                                    # ldh < n
+    assert g(12, P(FAKE), P(FAKE), 32, 64, 2048, P(FAKE), P(FAKE), 1, 4, P(FAKE), 64,
+             None, None) == INVALID                                                 # no status
 
 
 def test_argmax_and_router_validation(lib):
@@ -155,11 +160,14 @@ def test_gemm_validation(lib):
 
 def test_moe_validation(lib):
     g = lib.cq_moe_group
-    assert g(P(FAKE), 4, 0, 32, P(FAKE), P(FAKE), None) == INVALID          # top_k 0
-    assert g(P(FAKE), 4, 4, 2000, P(FAKE), P(FAKE), None) == INVALID        # > 1024 experts
-    assert g(P(FAKE), 4, 8, 4, P(FAKE), P(FAKE), None) == INVALID           # top_k > E
-    assert g(P(FAKE + 2), 4, 4, 32, P(FAKE), P(FAKE), None) == ALIGN
-    m = lib.cq_moe_gemm
+    S = P(FAKE + 64)
+    assert g(P(FAKE), 4, 0, 32, P(FAKE), P(FAKE), S, None) == INVALID          # top_k 0
+    assert g(P(FAKE), 4, 4, 2000, P(FAKE), P(FAKE), S, None) == INVALID        # > 1024 experts
+    assert g(P(FAKE), 4, 8, 4, P(FAKE), P(FAKE), S, None) == INVALID           # top_k > E
+    assert g(P(FAKE), 4, 4, 32, P(FAKE), P(FAKE), None, None) == INVALID       # no status
+    assert g(P(FAKE + 2), 4, 4, 32, P(FAKE), P(FAKE), S, None) == ALIGN
+    assert g(P(FAKE), 4, 4, 32, P(FAKE), P(FAKE), P(FAKE + 1), None) == ALIGN
+    m = lib.cq_moe_gemm_grouped
     assert m(12, P(FAKE), 32, 64, 256, P(FAKE), 2, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
              None) == INVALID                                                # x_per_pair
     assert m(12, P(FAKE), 32, 64, 288, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, P(FAKE), 64,
@@ -171,9 +179,54 @@ def test_moe_validation(lib):
     assert m(14, P(FAKE), 2, 1 << 20, 2560, P(FAKE), 0, P(FAKE), P(FAKE), 4, 2, P(FAKE),
              1 << 20, None) == SHAPE                                         # Q6_K expert >= 2 GiB
     s = lib.cq_swiglu_quantize_q8_0
-    assert s(P(FAKE), P(FAKE), 64, 2, 48, None, P(FAKE), None) == SHAPE
-    assert s(P(FAKE), P(FAKE + 4), 64, 2, 64, None, P(FAKE), None) == ALIGN
-    assert s(P(FAKE), P(FAKE), 64, 2, 64, P(FAKE + 8), P(FAKE), None) == ALIGN
+    assert s(P(FAKE), P(FAKE), 2, 48, None, P(FAKE), None) == SHAPE
+    assert s(P(FAKE), P(FAKE + 4), 2, 64, None, P(FAKE), None) == ALIGN
+    assert s(P(FAKE), P(FAKE), 2, 64, P(FAKE + 8), P(FAKE), None) == ALIGN
+    assert s(P(FAKE), P(FAKE), 2, 64, None, P(FAKE + 1), None) == ALIGN
+    assert s(None, None, 0, 64, None, None, None) == OK
     c = lib.cq_moe_combine
     assert c(P(FAKE), P(FAKE), 4, 4, 64, P(FAKE), 32, None) == INVALID      # ldy < n
     assert c(P(FAKE), P(FAKE), 0, 4, 64, P(FAKE), 64, None) == OK
+
+
+def test_moe_workspace_bytes(lib):
+    """Status word, offsets, pair list and (combined output) the per-pair
+    product rows, each part 256-byte aligned."""
+    wb = lib.cq_moe_workspace_bytes
+    assert wb(256, 4, 32, 2048, 0) == 256 + 256 + 4096
+    assert wb(256, 4, 32, 2048, 1) == 256 + 256 + 4096
+    assert wb(256, 4, 32, 2048, 2) == 256 + 256 + 4096 + 4 * 1024 * 2048
+    assert wb(256, 4, 32, 2048, 3) == 256 + 256 + 4096 + 4 * 1024 * 2048
+    assert wb(1, 1, 1024, 5, 2) == 256 + 4352 + 256 + 256
+    assert wb(0, 4, 32, 2048, 0) == 256 + 256 + 256
+    assert wb(256, 4, 32, 2048, 4) == 0                                     # unknown flag
+    assert wb(256, 0, 32, 2048, 0) == 0
+    assert wb(256, 40, 32, 2048, 0) == 0                                    # top_k > E
+    assert wb(256, 4, 2000, 2048, 0) == 0
+
+
+def test_moe_one_call_validation(lib):
+    f = lib.cq_moe_gemm
+    WS = 256 + 256 + 4096 + 4 * 1024 * 2048
+    W = P(1 << 20)  # 256-byte aligned fake workspace
+
+    def call(wt=12, n=2048, k=1536, flags=3, ids=P(FAKE), rw=P(FAKE), T=256, top_k=4, y=P(FAKE),
+             ldy=2048, ws=W, wsb=WS, xq=P(FAKE)):
+        return f(wt, P(FAKE), 32, n, k, xq, flags, ids, rw, T, top_k, y, ldy, ws, wsb, None)
+
+    assert call(flags=4) == INVALID
+    assert call(flags=-1) == INVALID
+    assert call(wt=41) == UNSUPPORTED
+    assert call(wt=7) == UNSUPPORTED
+    assert call(k=1000) == SHAPE
+    assert call(top_k=40) == INVALID
+    assert call(ldy=100) == INVALID
+    assert call(rw=None) == INVALID                      # combine needs the route weights
+    assert call(ids=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(wsb=WS - 1) == -5
+    assert call(ws=P((1 << 20) + 16)) == -5              # 256-byte alignment
+    assert call(ids=P(FAKE + 2)) == ALIGN
+    assert call(rw=P(FAKE + 1)) == ALIGN
+    assert call(T=0) == OK                               # no tokens: nothing launched
+    assert call(n=0) == OK

@@ -36,13 +36,14 @@ def test_decode_steps_graph_replays(cq, orc):
     lg = torch.empty((1, n_lm), dtype=torch.float32, device="cuda")
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
     ws = torch.empty(cq.load().cq_argmax_workspace_bytes(1, n_lm), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def step():
         cq.cq_topk_softmax(logits, K, ids=ids, w=rw)
         cq.cq_quantize_q8_0(x, xq)
-        cq.cq_moe_gemv_swiglu(fmt, wg, wu, E, F, H, xq, ids, h=h)
+        cq.cq_moe_gemv_swiglu(fmt, wg, wu, E, F, H, xq, ids, h=h, status=st)
         cq.cq_quantize_q8_0(h, hq)
-        cq.cq_moe_gemv(fmt, wd, E, H, F, hq, True, ids, y=d)
+        cq.cq_moe_gemv(fmt, wd, E, H, F, hq, True, ids, y=d, status=st)
         cq.cq_moe_combine(d, rw, y=y)
         cq.cq_quantize_q8_0(y, yq)
         cq.cq_gemv(fmt, wl, n_lm, H, yq, 1, y=lg)
@@ -76,5 +77,6 @@ def test_decode_steps_graph_replays(cq, orc):
         got = [to_host(t) for t in (ids, rw, h, d, y, lg, tok)]
         for a, b in zip(got, ref):
             assert np.array_equal(a, b), r
+    assert to_host(st)[0] == 0        # no out-of-range expert id in any call
     # and the step's result is the oracle's arg-max of its own logits
     assert ref[-1][0] == orc.argmax_rows(ref[-2])[0]

@@ -7,9 +7,12 @@ the seeded generator), never from the GPU:
               the oracle's per-pair dots: |y - y_ref| <= 2e-5 * S;
   down        grouped GEMM on the oracle's requantized SwiGLU output;
   combine     slot-order combine of the oracle's expert outputs;
-then the whole GPU pipeline end to end against the oracle pipeline with a
-bound derived from the oracle's values, and the reduction to dense GEMMs
-when every token picks the same experts (bitwise)."""
+then the one-call routed projection (cq_moe_gemm: grouping, grouped product
+and slot-order combine in one call on a caller workspace) per stage, the
+whole GPU pipeline end to end through it against the oracle pipeline with a
+bound derived from the oracle's values, its status word on out-of-range
+expert ids, and the reduction to dense GEMMs when every token picks the same
+experts."""
 import functools
 
 import numpy as np
@@ -59,7 +62,7 @@ def test_moe_gate_up(cq):
     xq = to_dev(ref["xq"])
     for name, w, yr, sr in (("gate", wg, ref["g"], ref["sg"]), ("up", wu, ref["u"], ref["su"])):
         note("moe", name)
-        y = to_host(cq.cq_moe_gemm(FMT, to_dev(w), E, F, H, xq, False, offs, pairs, T, K))
+        y = to_host(cq.cq_moe_gemm_grouped(FMT, to_dev(w), E, F, H, xq, False, offs, pairs, T, K))
         r = assert_close_to_oracle(y, yr, sr, what=name)
         print(f"{name}: max |err|/S = {r:.3e}")
 
@@ -68,8 +71,8 @@ def test_moe_down(cq):
     wg, wu, wd, x, ids, rw = inputs()
     ref = oracle_pipeline()
     note("moe down")
-    y = to_host(cq.cq_moe_gemm(FMT, to_dev(wd), E, H, F, to_dev(ref["hq"]), True,
-                               to_dev(ref["offs"]), to_dev(ref["pairs"]), T, K))
+    y = to_host(cq.cq_moe_gemm_grouped(FMT, to_dev(wd), E, H, F, to_dev(ref["hq"]), True,
+                                       to_dev(ref["offs"]), to_dev(ref["pairs"]), T, K))
     r = assert_close_to_oracle(y, ref["d"], ref["sd"], what="down")
     print(f"down: max |err|/S = {r:.3e}")
 
@@ -85,15 +88,81 @@ def test_moe_combine_stage(cq, orc):
     assert np.all(np.abs(y - y_ref) <= 4 * 2.0 ** -24 * mag + 1e-30)
 
 
-def run_gpu_pipeline(cq, wg, wu, wd, x, ids, rw, want_stages=False):
+def one_call(cq, w, n, k, xq, flags, ids, rw=None):
+    """cq_moe_gemm on a workspace of exactly the size it asks for; returns
+    (y, status) on the host."""
+    import torch
+    n_tokens, top_k = ids.shape
+    need = cq.cq_moe_workspace_bytes(n_tokens, top_k, E, n, flags)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y, st = cq.cq_moe_gemm(FMT, w, E, n, k, xq, flags, ids, route_w=rw, workspace=ws)
+    return y, int(to_host(st)[0])
+
+
+def run_gpu_pipeline(cq, wg, wu, wd, x, ids, rw):
+    """The routed FFN through the one-call entry point: gate and up per pair,
+    SwiGLU + requantization, down combined over each token's slots."""
+    idd = to_dev(ids)
     xq = cq.cq_quantize_q8_0(to_dev(x))
-    offs, pairs = cq.cq_moe_group(to_dev(ids), E)
-    g = cq.cq_moe_gemm(FMT, to_dev(wg), E, F, H, xq, False, offs, pairs, T, K)
-    u = cq.cq_moe_gemm(FMT, to_dev(wu), E, F, H, xq, False, offs, pairs, T, K)
+    g, s1 = one_call(cq, to_dev(wg), F, H, xq, cq.MOE_X_PER_TOKEN | cq.MOE_OUT_PER_PAIR, idd)
+    u, s2 = one_call(cq, to_dev(wu), F, H, xq, cq.MOE_X_PER_TOKEN | cq.MOE_OUT_PER_PAIR, idd)
     _, hq = cq.cq_swiglu_quantize_q8_0(g, u)
-    d = cq.cq_moe_gemm(FMT, to_dev(wd), E, H, F, hq, True, offs, pairs, T, K)
-    y = cq.cq_moe_combine(d, to_dev(rw))
+    y, s3 = one_call(cq, to_dev(wd), H, F, hq, cq.MOE_X_PER_PAIR | cq.MOE_OUT_COMBINE, idd,
+                     to_dev(rw))
+    assert (s1, s2, s3) == (0, 0, 0)
     return to_host(y)
+
+
+def test_moe_one_call_stages(cq, orc):
+    """cq_moe_gemm per stage on the oracle's inputs: the gate projection per
+    pair (2e-5 * S), and the down projection combined over slots: each
+    product within 2e-5 * S_down of the oracle, then four fp32 FMAs in slot
+    order, so |y - y_ref| <= 2e-5 * sum_s |w| S_down + 4 ulp of sum_s |w D|."""
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    idd = to_dev(ids)
+    note("moe one-call gate")
+    g, st = one_call(cq, to_dev(wg), F, H, to_dev(ref["xq"]),
+                     cq.MOE_X_PER_TOKEN | cq.MOE_OUT_PER_PAIR, idd)
+    assert st == 0
+    r = assert_close_to_oracle(to_host(g), ref["g"], ref["sg"], what="one-call gate")
+    print(f"one-call gate: max |err|/S = {r:.3e}")
+    note("moe one-call down + combine")
+    y, st = one_call(cq, to_dev(wd), H, F, to_dev(ref["hq"]),
+                     cq.MOE_X_PER_PAIR | cq.MOE_OUT_COMBINE, idd, to_dev(rw))
+    assert st == 0
+    mag, _ = orc.moe_combine(np.abs(ref["d"]), None, np.abs(rw))
+    err = np.abs(to_host(y) - ref["y"])
+    assert np.all(err <= 2e-5 * ref["sy"] + 4 * 2.0 ** -24 * mag + 1e-30)
+    print(f"one-call down + combine: max |err|/S = {(err / ref['sy']).max():.3e}")
+
+
+def test_moe_one_call_invalid_ids(cq, orc):
+    """Expert ids outside [0, E) are counted in the workspace status word;
+    combined rows leave those slots out, and every other output is right."""
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    bad = ids[:16].copy()
+    bad[3, 1] = -1
+    bad[9, 3] = E
+    bad[9, 0] = 1 << 30
+    note("moe one-call invalid ids")
+    y, st = one_call(cq, to_dev(wd), H, F, to_dev(ref["hq"][:16 * K]),
+                     cq.MOE_X_PER_PAIR | cq.MOE_OUT_COMBINE, to_dev(bad), to_dev(rw[:16]))
+    assert st == 3
+    d = ref["d"][:16 * K].copy()
+    sd = ref["sd"][:16 * K].copy()
+    for t, s in ((3, 1), (9, 3), (9, 0)):
+        d[t * K + s] = 0.0
+        sd[t * K + s] = 0.0
+    y_ref, s_ref = orc.moe_combine(d, sd, rw[:16])
+    mag, _ = orc.moe_combine(np.abs(d), None, np.abs(rw[:16]))
+    assert np.all(np.abs(to_host(y) - y_ref) <= 2e-5 * s_ref + 4 * 2.0 ** -24 * mag + 1e-30)
+    note("moe one-call per pair, valid ids")
+    yp, st = one_call(cq, to_dev(wd), H, F, to_dev(ref["hq"][:16 * K]),
+                      cq.MOE_X_PER_PAIR | cq.MOE_OUT_PER_PAIR, to_dev(ids[:16]))
+    assert st == 0
+    assert_close_to_oracle(to_host(yp), ref["d"][:16 * K], ref["sd"][:16 * K], what="per pair")
 
 
 def test_moe_end_to_end(cq):
@@ -142,8 +211,8 @@ def test_moe_reduces_to_dense(cq, orc):
     ids2 = np.tile(np.array([[5, 17, 2, 31]], np.int32), (tok, 1))
     xq = cq.cq_quantize_q8_0(to_dev(x[:tok]))
     note("moe dense reduction")
-    offs, pairs = cq.cq_moe_group(to_dev(ids2), E)
-    g = to_host(cq.cq_moe_gemm(FMT, to_dev(wg), E, F, H, xq, False, offs, pairs, tok, K))
+    offs, pairs, _ = cq.cq_moe_group(to_dev(ids2), E)
+    g = to_host(cq.cq_moe_gemm_grouped(FMT, to_dev(wg), E, F, H, xq, False, offs, pairs, tok, K))
     xq_h = to_host(xq)
     for s, e in enumerate([5, 17, 2, 31]):
         we = wg[e * F:(e + 1) * F]
@@ -166,8 +235,9 @@ def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
         xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=701))
         offs, pairs = orc.moe_group(ids, n_experts)
         note("moe gemm shape", n_tokens, n_experts, top_k, n, k, x_per_pair)
-        y = to_host(cq.cq_moe_gemm(FMT, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
-                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y = to_host(cq.cq_moe_gemm_grouped(FMT, to_dev(w), n_experts, n, k, to_dev(xq),
+                                           x_per_pair, to_dev(offs), to_dev(pairs), n_tokens,
+                                           top_k))
         y_ref, s_ref = orc.moe_matmul(FMT, w, n_experts, n, k, xq, x_per_pair, ids)
         assert_close_to_oracle(y, y_ref, s_ref, what="moe shape")
 
@@ -185,8 +255,9 @@ def test_moe_gemm_other_formats(cq, orc, fmt, n_tokens, n_experts, top_k, n, k):
         rows = n_tokens * top_k if x_per_pair else n_tokens
         xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=721))
         note("moe gemm", gs.NAMES[fmt], n_tokens, n_experts, top_k, n, k, x_per_pair)
-        y = to_host(cq.cq_moe_gemm(fmt, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
-                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y = to_host(cq.cq_moe_gemm_grouped(fmt, to_dev(w), n_experts, n, k, to_dev(xq),
+                                           x_per_pair, to_dev(offs), to_dev(pairs), n_tokens,
+                                           top_k))
         y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
         assert_close_to_oracle(y, y_ref, s_ref, what=f"moe {gs.NAMES[fmt]}")
 
@@ -203,7 +274,8 @@ def test_moe_gemm_max_k(cq, orc, fmt):
         rows = n_tokens * top_k if x_per_pair else n_tokens
         xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=731))
         note("moe gemm max k", gs.NAMES[fmt], x_per_pair)
-        y = to_host(cq.cq_moe_gemm(fmt, to_dev(w), n_experts, n, k, to_dev(xq), x_per_pair,
-                                   to_dev(offs), to_dev(pairs), n_tokens, top_k))
+        y = to_host(cq.cq_moe_gemm_grouped(fmt, to_dev(w), n_experts, n, k, to_dev(xq),
+                                           x_per_pair, to_dev(offs), to_dev(pairs), n_tokens,
+                                           top_k))
         y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
         assert_close_to_oracle(y, y_ref, s_ref, what=f"moe max k {gs.NAMES[fmt]}")

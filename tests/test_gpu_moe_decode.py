@@ -7,7 +7,8 @@ Checks: each pair's output against the fp64 oracle's per-pair dots
 (|y - y_ref| <= 2e-5*S); each pair bitwise equal to cq_gemv (cq_gemv_swiglu)
 on that expert's matrix and activation row (the same single-pass kernel);
 the fused gate/up output equal to the oracle SwiGLU of the two unfused
-outputs within one fp32 ulp; ids outside [0, E) clamped; and the whole
+outputs within one fp32 ulp; ids outside [0, E) counted in the status
+word with zero outputs for their pairs; and the whole
 decode FFN (quantize, gate/up + SwiGLU, requantize, down, combine) against
 the oracle's combine of the GPU's down outputs."""
 import functools
@@ -46,25 +47,27 @@ def test_moe_gemv_decode(cq, orc, fmt, n_tokens):
     xq_h = orc.quantize_q8_0(x)
     wgd, wud, wdd, xq, idd = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(xq_h), to_dev(ids)
     note("moe gemv gate", gs.NAMES[fmt], n_tokens)
-    g = to_host(cq.cq_moe_gemv(fmt, wgd, E, F, H, xq, False, idd))
+    g, st = cq.cq_moe_gemv(fmt, wgd, E, F, H, xq, False, idd)
+    g = to_host(g)
     g_ref, sg = orc.moe_matmul(fmt, wg, E, F, H, xq_h, False, ids)
     assert_close_to_oracle(g, g_ref, sg, what="moe gemv gate")
-    u = to_host(cq.cq_moe_gemv(fmt, wud, E, F, H, xq, False, idd))
+    u = to_host(cq.cq_moe_gemv(fmt, wud, E, F, H, xq, False, idd, status=st)[0])
     # bitwise: pair p is cq_gemv on expert ids[p] and token p // K
     for p in range(n_tokens * K):
         e, t = int(ids.flat[p]), p // K
         yp = to_host(cq.cq_gemv(fmt, wgd[e * F:(e + 1) * F], F, H, xq[t:t + 1], 1))
         assert np.array_equal(yp[0], g[p]), p
     note("moe gemv swiglu", gs.NAMES[fmt], n_tokens)
-    h = to_host(cq.cq_moe_gemv_swiglu(fmt, wgd, wud, E, F, H, xq, idd))
+    h = to_host(cq.cq_moe_gemv_swiglu(fmt, wgd, wud, E, F, H, xq, idd, status=st)[0])
     d = ulp_diff(h, orc.swiglu(g.astype(np.float32), u.astype(np.float32)))
     assert d.max() <= 1 and np.count_nonzero(d) <= max(2, d.size // 1000)
     # down: per-pair activation rows (the requantized h)
     hq_h = orc.quantize_q8_0(h)
     note("moe gemv down", gs.NAMES[fmt], n_tokens)
-    dn = to_host(cq.cq_moe_gemv(fmt, wdd, E, H, F, to_dev(hq_h), True, idd))
+    dn = to_host(cq.cq_moe_gemv(fmt, wdd, E, H, F, to_dev(hq_h), True, idd, status=st)[0])
     d_ref, sd = orc.moe_matmul(fmt, wd, E, H, F, hq_h, True, ids)
     assert_close_to_oracle(dn, d_ref, sd, what="moe gemv down")
+    assert to_host(st)[0] == 0
 
 
 def test_moe_gemv_q6k_needs_whole_16_byte_rows(cq, orc):
@@ -79,21 +82,38 @@ def test_moe_gemv_q6k_needs_whole_16_byte_rows(cq, orc):
         cq.cq_moe_gemv(gs.Q6_K, wd, 4, H, F, hq, True, ids)
     wg_h = gs.weights(gs.Q6_K, 4 * F, H, cfg=846)
     xq_h = orc.quantize_q8_0(gs.activations(1, H, cfg=846))
-    g = to_host(cq.cq_moe_gemv(gs.Q6_K, to_dev(wg_h), 4, F, H, to_dev(xq_h), False, ids))
+    g = to_host(cq.cq_moe_gemv(gs.Q6_K, to_dev(wg_h), 4, F, H, to_dev(xq_h), False, ids)[0])
     g_ref, sg = orc.moe_matmul(gs.Q6_K, wg_h, 4, F, H, xq_h, False, ids_h)
     assert_close_to_oracle(g, g_ref, sg, what="moe gemv q6_k gate")
 
 
-def test_moe_gemv_ids_clamped(cq, orc):
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_moe_gemv_invalid_ids(cq, orc, swiglu):
+    """Ids outside [0, E): their pairs read no weights and give exact zeros,
+    each adds 1 to the caller's status counter (which the library never
+    clears), and the valid pairs are unaffected (bitwise)."""
     fmt = gs.Q4_K
-    wg, _, _ = experts(fmt)
+    wg, wu, _ = experts(fmt)
     ids = np.array([[3, -5, 99, 31]], np.int32)
-    xq_h = orc.quantize_q8_0(gs.activations(1, H, cfg=840))
-    note("moe gemv clamped ids")
-    g = to_host(cq.cq_moe_gemv(fmt, to_dev(wg), E, F, H, to_dev(xq_h), False, to_dev(ids)))
-    ref = to_host(cq.cq_moe_gemv(fmt, to_dev(wg), E, F, H, to_dev(xq_h), False,
-                                 to_dev(np.clip(ids, 0, E - 1).astype(np.int32))))
-    assert np.array_equal(g, ref)
+    good = np.array([[3, 3, 31, 31]], np.int32)
+    xq = to_dev(orc.quantize_q8_0(gs.activations(1, H, cfg=840)))
+    note("moe gemv invalid ids", swiglu)
+    if swiglu:
+        run = (lambda i, st: cq.cq_moe_gemv_swiglu(fmt, to_dev(wg), to_dev(wu), E, F, H, xq,
+                                                   to_dev(i), status=st))
+    else:
+        run = (lambda i, st: cq.cq_moe_gemv(fmt, to_dev(wg), E, F, H, xq, False, to_dev(i),
+                                            status=st))
+    y, st = run(ids, None)
+    y = to_host(y)
+    assert to_host(st)[0] == 2
+    ref, st2 = run(good, None)
+    ref = to_host(ref)
+    assert to_host(st2)[0] == 0
+    assert np.array_equal(y[0], ref[0]) and np.array_equal(y[3], ref[3])
+    assert not y[1].any() and not y[2].any()
+    run(ids, st)                       # the counter accumulates
+    assert to_host(st)[0] == 4
 
 
 def test_moe_decode_ffn_end_to_end(cq, orc):
@@ -107,9 +127,10 @@ def test_moe_decode_ffn_end_to_end(cq, orc):
     note("moe decode ffn")
     xq = cq.cq_quantize_q8_0(to_dev(x))
     idd = to_dev(ids)
-    h = cq.cq_moe_gemv_swiglu(fmt, to_dev(wg), to_dev(wu), E, F, H, xq, idd)
+    h, st = cq.cq_moe_gemv_swiglu(fmt, to_dev(wg), to_dev(wu), E, F, H, xq, idd)
     hq = cq.cq_quantize_q8_0(h)
-    dn = cq.cq_moe_gemv(fmt, to_dev(wd), E, H, F, hq, True, idd)
+    dn, _ = cq.cq_moe_gemv(fmt, to_dev(wd), E, H, F, hq, True, idd, status=st)
+    assert to_host(st)[0] == 0
     y = to_host(cq.cq_moe_combine(dn, to_dev(rw)))
     assert np.array_equal(to_host(hq), orc.quantize_q8_0(to_host(h)))
     d_ref, sd = orc.moe_matmul(fmt, wd, E, H, F, to_host(hq), True, ids)

@@ -18,8 +18,9 @@ def test_moe_group_bit_exact(cq, orc, n_tokens, n_experts, top_k):
         ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=500 + n_experts)
     else:
         ids = np.zeros((0, top_k), np.int32)
-    off, pairs = cq.cq_moe_group(to_dev(ids), n_experts)
+    off, pairs, st = cq.cq_moe_group(to_dev(ids), n_experts)
     off, pairs = to_host(off), to_host(pairs)
+    assert to_host(st)[0] == 0
     off_ref, pairs_ref = orc.moe_group(ids, n_experts) if n_tokens else (
         np.zeros(n_experts + 1, np.int32), np.zeros(0, np.int32))
     assert np.array_equal(off, off_ref)
@@ -32,10 +33,31 @@ def test_moe_group_skewed(cq, orc):
     ids[:, 1] = 7
     ids[::3, 2] = 31
     ids[:, 3] = np.arange(1500) % 32
-    off, pairs = cq.cq_moe_group(to_dev(ids), 32)
+    off, pairs, st = cq.cq_moe_group(to_dev(ids), 32)
     off_ref, pairs_ref = orc.moe_group(ids, 32)
     assert np.array_equal(to_host(off), off_ref)
     assert np.array_equal(to_host(pairs), pairs_ref)
+    assert to_host(st)[0] == 0
+
+
+def test_moe_group_invalid_ids(cq, orc):
+    """Ids outside [0, n_experts) are counted in the status word and placed in
+    no group; the valid pairs are grouped exactly as the oracle groups them
+    once the invalid pairs are removed."""
+    note("moe group invalid ids")
+    ids, _ = gs.routing(300, 32, 4, cfg=502)
+    ids[5, 2] = -7
+    ids[100, 0] = 32
+    ids[299, 3] = 2 ** 31 - 1
+    off, pairs, st = cq.cq_moe_group(to_dev(ids), 32)
+    assert to_host(st)[0] == 3
+    valid = (ids >= 0) & (ids < 32)
+    flat = ids.reshape(-1)
+    ok = np.flatnonzero(valid.reshape(-1))
+    order = ok[np.argsort(flat[ok], kind="stable")]
+    counts = np.bincount(flat[ok], minlength=32)
+    assert np.array_equal(to_host(off), np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    assert np.array_equal(to_host(pairs)[:ok.size], order.astype(np.int32))
 
 
 def test_moe_combine(cq, orc):

@@ -84,6 +84,7 @@ def test_router_feeds_the_moe(cq, orc):
     logits = np.random.default_rng(930).standard_normal((rows, E)).astype(np.float32)
     note("router -> group")
     ids, _ = cq.cq_topk_softmax(to_dev(logits), K)
-    offs, pairs = cq.cq_moe_group(ids, E)
+    offs, pairs, st = cq.cq_moe_group(ids, E)
     offs_ref, pairs_ref = orc.moe_group(orc.topk_softmax(logits, K)[0], E)
     assert np.array_equal(to_host(offs), offs_ref) and np.array_equal(to_host(pairs), pairs_ref)
+    assert to_host(st)[0] == 0
