@@ -85,7 +85,8 @@ typedef enum {
     CQ_ERR_ALIGNMENT = -4,        /* pointer or leading dim misaligned       */
     CQ_ERR_WORKSPACE = -5,        /* caller workspace too small or misaligned */
     CQ_ERR_HIP = -6,              /* a HIP runtime call failed               */
-    CQ_ERR_NO_DEVICE = -7         /* no gfx950 device current                */
+    CQ_ERR_NO_DEVICE = -7,        /* no gfx950 device current                */
+    CQ_ERR_SCRATCH_LIMIT = -8     /* exceeds the fixed no-allocation scratch */
 } cq_status;
 
 /* Weight types, numbered as the GGUF tensor type ids. */
@@ -253,6 +254,30 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
                 const void* xq, int flags, const int32_t* expert_ids, const float* route_w,
                 int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, void* workspace,
                 size_t ws_bytes, cq_stream_t stream);
+
+/*
+ * cq_moe_gemm_noalloc -- cq_moe_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with the workspace in a
+ * fixed scratch array that the library holds on each GPU it runs on from
+ * first use until the process ends, and the status word (the number of
+ * expert ids outside [0, n_experts), stored by the call) in the caller's
+ * `status` (device int32, 4-byte aligned).  The call allocates and frees
+ * nothing.
+ *   Limit: cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags) must
+ *   not exceed CQ_MOE_NOALLOC_MAX_BYTES (16 MiB, e.g. 2048 pairs of 2048
+ *   combined outputs), else CQ_ERR_SCRATCH_LIMIT and nothing is launched.
+ *   Every call on one GPU uses that GPU's one scratch array: calls on
+ *   different streams that overlap in time race and give wrong results;
+ *   order them on one stream (or with events).  The array keeps the last
+ *   call's contents; each call writes everything it later reads.
+ * Other arguments, results and errors as cq_moe_gemm.
+ */
+#define CQ_MOE_NOALLOC_MAX_BYTES (16 << 20)
+int cq_moe_gemm_noalloc(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                        const void* xq, int flags, const int32_t* expert_ids,
+                        const float* route_w, int64_t n_tokens, int64_t top_k,
+                        float* y, int64_t ldy, int32_t* status, cq_stream_t stream);
 
 /*
  * The routed projection in separate steps (cq_moe_gemm runs these three on

@@ -21,12 +21,13 @@ GEMV_MAX_BATCH = 8
 
 STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",
           -3: "CQ_ERR_SHAPE", -4: "CQ_ERR_ALIGNMENT", -5: "CQ_ERR_WORKSPACE",
-          -6: "CQ_ERR_HIP", -7: "CQ_ERR_NO_DEVICE"}
+          -6: "CQ_ERR_HIP", -7: "CQ_ERR_NO_DEVICE", -8: "CQ_ERR_SCRATCH_LIMIT"}
+MOE_NOALLOC_MAX_BYTES = 16 << 20
 
 EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
     "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_workspace_bytes",
-    "cq_moe_gemm", "cq_moe_group", "cq_moe_gemm_grouped", "cq_swiglu_quantize_q8_0",
+    "cq_moe_gemm", "cq_moe_gemm_noalloc", "cq_moe_group", "cq_moe_gemm_grouped", "cq_swiglu_quantize_q8_0",
     "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu", "cq_argmax_workspace_bytes",
     "cq_argmax", "cq_topk_softmax",
 ]
@@ -76,6 +77,7 @@ def load():
         "cq_moe_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64, I64, I]),
         "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P,
                             ctypes.c_size_t, P]),
+        "cq_moe_gemm_noalloc": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P, P]),
         "cq_swiglu_quantize_q8_0": (I, [P, P, I64, I64, P, P, P]),
         "cq_moe_combine": (I, [P, P, I64, I64, I64, P, I64, P]),
         "cq_moe_gemv": (I, [I, P, I64, I64, I64, P, I, P, I64, I64, P, I64, P, P]),
@@ -246,6 +248,31 @@ def cq_moe_gemm(wt, w_experts, n_experts, n, k, xq, flags, expert_ids, route_w=N
         wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), flags, _ptr(expert_ids), _ptr(route_w),
         n_tokens, top_k, _ptr(y), ldy, _ptr(workspace), workspace.numel(), _stream(stream)))
     return y, workspace[:4].view(torch.int32)
+
+
+def cq_moe_gemm_noalloc(wt, w_experts, n_experts, n, k, xq, flags, expert_ids, route_w=None,
+                        y=None, ldy=None, status=None, stream=None):
+    """cq_moe_gemm without a workspace: the library's fixed device scratch
+    serves instead (at most MOE_NOALLOC_MAX_BYTES) -> (y, status)."""
+    import torch
+    _dev_tensor(w_experts, "w_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    _dev_tensor(expert_ids, "expert_ids", torch.int32)
+    n_tokens, top_k = expert_ids.shape
+    rows = n_tokens if flags & MOE_OUT_COMBINE else n_tokens * top_k
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=w_experts.device)
+    _dev_tensor(y, "y", torch.float32)
+    if route_w is not None:
+        _dev_tensor(route_w, "route_w", torch.float32)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=w_experts.device)
+    _dev_tensor(status, "status", torch.int32)
+    ldy = ldy if ldy is not None else (y.stride(0) if y.dim() == 2 else n)
+    _check("cq_moe_gemm_noalloc", load().cq_moe_gemm_noalloc(
+        wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), flags, _ptr(expert_ids), _ptr(route_w),
+        n_tokens, top_k, _ptr(y), ldy, _ptr(status), _stream(stream)))
+    return y, status
 
 
 def cq_swiglu_quantize_q8_0(g, u, h=None, want_h=False, hq=None, stream=None):

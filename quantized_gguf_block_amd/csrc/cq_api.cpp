@@ -99,6 +99,7 @@ const char* cq_status_string(int status) {
         case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE: workspace smaller than required or misaligned";
         case CQ_ERR_HIP: return "CQ_ERR_HIP: a HIP runtime call failed";
         case CQ_ERR_NO_DEVICE: return "CQ_ERR_NO_DEVICE: no HIP device is current";
+        case CQ_ERR_SCRATCH_LIMIT: return "CQ_ERR_SCRATCH_LIMIT: the call needs more than the fixed device scratch of the no-allocation entry point (CQ_MOE_NOALLOC_MAX_BYTES)";
         default: return "unknown cq status";
     }
 }
@@ -312,7 +313,32 @@ int cq_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int
     if (int rc = check_device()) return rc;
     return status_of(launch_moe_routed(wt, w_experts, n_experts, n, k, xq, flags, expert_ids,
                                        route_w, n_tokens, top_k, y, ldy,
-                                       static_cast<uint8_t*>(workspace),
+                                       static_cast<uint8_t*>(workspace), nullptr,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int cq_moe_gemm_noalloc(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
+                        const void* xq, int flags, const int32_t* expert_ids,
+                        const float* route_w, int64_t n_tokens, int64_t top_k, float* y,
+                        int64_t ldy, int32_t* status, cq_stream_t stream) {
+    static_assert(CQ_MOE_NOALLOC_MAX_BYTES == kMoeScratchBytes, "one scratch size");
+    if (!moe_flags_ok(flags)) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_moe_gemm(wt, w_experts, n_experts, n, k, n_tokens, top_k, ldy)) return rc;
+    if (n > (int64_t(1) << 24)) return CQ_ERR_SHAPE;
+    if (static_cast<int64_t>(cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags)) >
+        kMoeScratchBytes)
+        return CQ_ERR_SCRATCH_LIMIT;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    const bool combine = (flags & CQ_MOE_OUT_COMBINE) != 0;
+    if (!xq || !expert_ids || !y || !status || (combine && !route_w)) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(expert_ids, 4) || !aligned(y, 4) || !aligned(status, 4) ||
+        (combine && !aligned(route_w, 4)))
+        return CQ_ERR_ALIGNMENT;
+    if (int rc = check_device()) return rc;
+    uint8_t* ws = nullptr;
+    if (int rc = moe_scratch_address(&ws)) return status_of(rc);
+    return status_of(launch_moe_routed(wt, w_experts, n_experts, n, k, xq, flags, expert_ids,
+                                       route_w, n_tokens, top_k, y, ldy, ws, status,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

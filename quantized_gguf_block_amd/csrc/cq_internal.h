@@ -50,9 +50,18 @@ struct MoeLayout {
     int64_t status, offsets, pairs, prod, total;
 };
 MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t n, int flags);
+// status: where the count of invalid expert ids goes (NULL: the workspace's
+// own status word).
 int launch_moe_routed(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
                       const void* xq, int flags, const int32_t* ids, const float* route_w,
                       int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, uint8_t* ws,
-                      hipStream_t stream);
+                      int32_t* status, hipStream_t stream);
+
+// The fixed device scratch of the no-allocation routed projection: its size,
+// and its address on the current device (resolved once per device; returns
+// 0, or -7 without a usable current device, -6 if HIP cannot resolve it).
+constexpr int64_t kMoeScratchBytes = int64_t(16) << 20;
+constexpr int kMaxScratchDevices = 64;
+int moe_scratch_address(uint8_t** ptr);
 
 }  // namespace cq

@@ -2,6 +2,8 @@
 #include "cq_device.h"
 #include "cq_internal.h"
 
+#include <mutex>
+
 namespace cq {
 
 // ---- grouping: stable counting sort of (token, slot) pairs by expert ------
@@ -194,9 +196,9 @@ MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t
 int launch_moe_routed(int wt, const void* w, int64_t n_experts, int64_t n, int64_t k,
                       const void* xq, int flags, const int32_t* ids, const float* route_w,
                       int64_t n_tokens, int64_t top_k, float* y, int64_t ldy, uint8_t* ws,
-                      hipStream_t stream) {
+                      int32_t* status, hipStream_t stream) {
     const MoeLayout L = moe_layout(n_tokens, top_k, n_experts, n, flags);
-    int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+    if (!status) status = reinterpret_cast<int32_t*>(ws + L.status);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
     const bool combine = (flags & kMoeOutCombine) != 0;
@@ -208,6 +210,32 @@ int launch_moe_routed(int wt, const void* w, int64_t n_experts, int64_t n, int64
         return rc;
     if (combine)
         return launch_moe_combine(prod, route_w, n_tokens, top_k, n, y, ldy, ids, n_experts, stream);
+    return 0;
+}
+
+// ---- fixed device scratch for callers that cannot allocate ------------------
+// One array per device, the size of the largest workspace the no-allocation
+// routed projection accepts.  In host code its name is only a stand-in: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept here.
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+int moe_scratch_address(uint8_t** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -7;
+    if (dev >= kMaxScratchDevices) return -7;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -6;
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = static_cast<uint8_t*>(g_scratch_dev[dev]);
     return 0;
 }
 

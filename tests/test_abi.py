@@ -230,3 +230,27 @@ def test_moe_one_call_validation(lib):
     assert call(rw=P(FAKE + 1)) == ALIGN
     assert call(T=0) == OK                               # no tokens: nothing launched
     assert call(n=0) == OK
+
+
+def test_moe_noalloc_validation(lib):
+    """The no-allocation routed projection refuses, before any launch, a call
+    whose workspace would exceed its fixed scratch, and checks the rest as
+    cq_moe_gemm does."""
+    f = lib.cq_moe_gemm_noalloc
+    S = P(FAKE + 64)
+
+    def call(n=2048, T=256, top_k=4, flags=3, status=S, rw=P(FAKE), k=1536):
+        return f(12, P(FAKE), 32, n, k, P(FAKE), flags, P(FAKE), rw, T, top_k, P(FAKE), n,
+                 status, None)
+
+    # 256 tokens x 4 pairs x 2048 combined outputs (8.4 MB) fit; 1024 tokens (33.6 MB) do not
+    assert lib.cq_moe_workspace_bytes(1024, 4, 32, 2048, 3) > cq.MOE_NOALLOC_MAX_BYTES
+    assert call(T=1024) == -8
+    assert call(T=1024, flags=1) != -8          # per-pair output needs no product rows
+    assert call(flags=8) == INVALID
+    assert call(status=None) == INVALID
+    assert call(status=P(FAKE + 2)) == ALIGN
+    assert call(rw=None) == INVALID
+    assert call(k=1000) == SHAPE
+    assert call(T=0) == OK
+    assert lib.cq_status_string(-8).decode().startswith("CQ_ERR_SCRATCH_LIMIT")
