@@ -493,7 +493,9 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
     }
 }
 
-// Dense GEMM: 128 x 128 tiles, 2 x 2 waves of 64 x 64.
+// Dense GEMM with one LDS buffer (the formats whose scale tables do not
+// leave room for two buffers at two workgroups per CU): 128 x 128 tiles,
+// 2 x 2 waves of 64 x 64.
 template <int FMT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
@@ -519,6 +521,197 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     // every token sub-tile is computed (rows past m hold row 0's data and are
     // not stored): straight-line MFMA code keeps the accumulators in place
     mma_tile<FMT, 2, 2, 2, 2, true>(s, w, n, k, rb, n0, xq, rows, y, ldy);
+}
+
+// ---- dense GEMM, double-buffered LDS -----------------------------------------
+// The same 128 x 128 workgroup tile, 2 x 2 waves of 64 x 64 and k step of
+// four blocks, with two LDS buffers: while step ks is computed from one, the
+// decoded weights and split activations of step ks+1 are stored into the
+// other (their global loads were issued a step earlier), so each step needs
+// one barrier instead of two.  Two buffers of padded rows (the 16-byte pad
+// keeps the MFMA operand reads of eight rows at one offset on distinct
+// banks) and the two scale tables take 80 KB, so two workgroups share a CU:
+// this path serves Q4_0 and Q8_0 (Q4_1 / K-quants need more tables).
+constexpr int RW2 = KB * 32 + 16;
+
+template <int FMT>
+struct Smem2 {
+    int8_t w[128 * RW2];
+    int8_t x[128 * RW2];
+    float dw[KB][128];
+    float dx[KB][128];
+};
+
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * RW2 + (chunk << 4); }  // byte offset of 16-byte chunk
+
+template <int FMT>
+__device__ __forceinline__ void store_w2(Smem2<FMT>& s, const WRaw<FMT>& r) {
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+    constexpr int BS = WRaw<FMT>::BS;
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl) {
+        const int b = 2 * half + bl;
+        uint32_t o[8];
+        s.dw[b][row] = h2f(half_at(r.v, bl * BS));
+        if constexpr (FMT == T_Q8_0) {
+            extract<8>(r.v, bl * BS + 2, o);
+        } else {
+            uint32_t q[4];
+            extract<4>(r.v, bl * BS + 2, q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = nib_lo_s8(q[i]);
+                o[4 + i] = nib_hi_s8(q[i]);
+            }
+        }
+        *reinterpret_cast<uint4*>(s.w + lds_off(row, 2 * b)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(s.w + lds_off(row, 2 * b + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_x2(Smem2<FMT>& s, const XRaw& r) {
+    const int t = threadIdx.x, row = t >> 1, half = t & 1;
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl) {
+        const int b = 2 * half + bl;
+        uint32_t o[8];
+        extract<8>(r.v, bl * 34 + 2, o);
+        s.dx[b][row] = h2f(half_at(r.v, bl * 34));
+        *reinterpret_cast<uint4*>(s.x + lds_off(row, 2 * b)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(s.x + lds_off(row, 2 * b + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+__device__ __forceinline__ void load_x2(XRaw& r, const uint8_t* __restrict__ xq, int64_t xrb,
+                                        int64_t gm, int kstep) {
+    const int half = threadIdx.x & 1;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(
+        xq + gm * xrb + (static_cast<int64_t>(kstep) * KB + 2 * half) * 34);
+#pragma unroll
+    for (int i = 0; i < 17; ++i) r.v[i] = p[i];
+}
+
+// one 32-value block of the step: 2 x 2 MFMA tiles of this wave, rescaled
+template <int FMT>
+__device__ __forceinline__ void mma_block2(const Smem2<FMT>& s, int b, int wm, int wn, int l32, int h,
+                                           const v16i& bias, v16f (&acc)[2][2]) {
+    v4i A[2], Bv[2];
+    float dx[2], ndx[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int r = (wn * 2 + ni) * 32 + l32;
+        A[ni] = *reinterpret_cast<const v4i*>(s.w + lds_off(r, 2 * b + h));
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int r = (wm * 2 + mi) * 32 + l32;
+        Bv[mi] = *reinterpret_cast<const v4i*>(s.x + lds_off(r, 2 * b + h));
+        dx[mi] = s.dx[b][r];
+        ndx[mi] = -kBiasF * dx[mi];
+    }
+    float dwv[2][16];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 d4 = *reinterpret_cast<const float4*>(&s.dw[b][(wn * 2 + ni) * 32 + 8 * q + 4 * h]);
+            dwv[ni][4 * q] = d4.x; dwv[ni][4 * q + 1] = d4.y;
+            dwv[ni][4 * q + 2] = d4.z; dwv[ni][4 * q + 3] = d4.w;
+        }
+    v16i D[2];
+    D[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], Bv[0], bias, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int ni = p / 2, mi = p % 2;
+        if (p + 1 < 4)
+            D[(p + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(p + 1) / 2], Bv[(p + 1) % 2], bias, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float tq = fmaf(__int_as_float(D[p & 1][r]), dx[mi], ndx[mi]);
+            acc[mi][ni][r] = fmaf(tq, dwv[ni][r], acc[mi][ni][r]);
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 2) void gemm2_kernel(
+        const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
+        const uint8_t* __restrict__ xq, int64_t m, float* __restrict__ y, int64_t ldy,
+        int tiles_m, int tiles_total) {
+    __shared__ __align__(16) Smem2<FMT> sm[2];
+    const int G = gridDim.x, g = blockIdx.x;
+    const int per_xcd = G / 8;
+    const int tile = (g < 8 * per_xcd) ? (g % 8) * per_xcd + g / 8 : g;
+    if (tile >= tiles_total) return;
+    const int64_t m0 = static_cast<int64_t>(tile % tiles_m) * 128;
+    const int64_t n0 = static_cast<int64_t>(tile / tiles_m) * 128;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t xrb = k / 32 * 34;
+    const int64_t gm = m0 + (threadIdx.x >> 1) < m ? m0 + (threadIdx.x >> 1) : m - 1;
+    const int ksteps = static_cast<int>(k / (32 * KB));
+
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = kBias;
+    v16f acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    WRaw<FMT> wr;
+    XRaw xr;
+    load_weights<FMT>(wr, w, n, rb, n0, 0);
+    load_x2(xr, xq, xrb, gm, 0);
+    store_w2<FMT>(sm[0], wr);
+    store_x2<FMT>(sm[0], xr);
+    const int k1 = ksteps > 1 ? 1 : 0;
+    load_weights<FMT>(wr, w, n, rb, n0, k1);
+    load_x2(xr, xq, xrb, gm, k1);
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) {
+        const Smem2<FMT>& cur = sm[ks & 1];
+        if (ks + 1 < ksteps) {
+            store_w2<FMT>(sm[(ks + 1) & 1], wr);
+            store_x2<FMT>(sm[(ks + 1) & 1], xr);
+        }
+        const int kn = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
+        load_weights<FMT>(wr, w, n, rb, n0, kn);
+        load_x2(xr, xq, xrb, gm, kn);
+#pragma unroll 2
+        for (int b = 0; b < KB; ++b) mma_block2<FMT>(cur, b, wm, wn, l32, h, bias, acc);
+        __syncthreads();
+    }
+    // epilogue: lane holds token row (wm*2 + mi)*32 + l32 and weight rows
+    // n0 + (wn*2 + ni)*32 + 8q + 4h + e (register 4q + e)
+    const bool vec = (ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int64_t gr = m0 + (wm * 2 + mi) * 32 + l32;
+        if (gr >= m) continue;
+        float* yr = y + gr * ldy;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gn = n0 + (wn * 2 + ni) * 32 + 8 * q + 4 * h;
+                if (vec && gn + 3 < n) {
+                    *reinterpret_cast<float4*>(yr + gn) =
+                        make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                                    acc[mi][ni][4 * q + 3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gn + e < n) yr[gn + e] = acc[mi][ni][4 * q + e];
+                }
+            }
+        }
+    }
 }
 
 // Grouped expert GEMM: workgroup (n tile, expert); 64 x 128 tiles, 1 x 4
@@ -851,9 +1044,9 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
     const uint8_t* xp = static_cast<const uint8_t*>(xq);
     const int tm = static_cast<int>(tiles_m), tt = static_cast<int>(tiles);
     switch (wt) {
-        case T_Q4_0: hipLaunchKernelGGL(gemm_kernel<T_Q4_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
+        case T_Q4_0: hipLaunchKernelGGL(gemm2_kernel<T_Q4_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q4_1: hipLaunchKernelGGL(gemm_kernel<T_Q4_1>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
-        case T_Q8_0: hipLaunchKernelGGL(gemm_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
+        case T_Q8_0: hipLaunchKernelGGL(gemm2_kernel<T_Q8_0>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q4_K: hipLaunchKernelGGL(gemm_kernel<T_Q4_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q5_K: hipLaunchKernelGGL(gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
         case T_Q6_K: hipLaunchKernelGGL(gemm_kernel<T_Q6_K>, g, b, 0, stream, wp, n, k, rb, xp, m, y, ldy, tm, tt); break;
