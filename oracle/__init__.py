@@ -20,11 +20,16 @@ _lib = None
 
 
 def lib():
+    """The oracle library (ORACLE_LIB names another build of it, such as the
+    sanitized one the test suite makes)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         sig = {
             "oracle_abi_version": (I, []),

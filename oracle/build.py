@@ -23,5 +23,21 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized(verbose=False):
+    """The same library built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (gcc runtimes) for the CPU test tier; returns
+    its path.  Load it with gcc's libasan preloaded."""
+    out_dir = os.path.join(HERE, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "liboracle_san.so")
+    cmd = ["g++", *FLAGS, "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", SRC, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -61,8 +61,17 @@ def load():
     # first would put a second HIP runtime into the process.
     import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in signatures().items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def signatures():
+    """ctypes result and argument types of every exported function."""
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    sigs = {
+    return {
         "cq_abi_version": (I, []),
         "cq_status_string": (ctypes.c_char_p, [I]),
         "cq_block_elems": (I64, [I]),
@@ -86,11 +95,6 @@ def load():
         "cq_topk_softmax": (I, [P, I64, I64, I64, I64, P, P, P]),
         "cq_moe_gemv_swiglu": (I, [I, P, P, I64, I64, I64, P, P, I64, I64, P, I64, P, P]),
     }
-    for name, (res, args) in sigs.items():
-        f = getattr(L, name)
-        f.restype, f.argtypes = res, args
-    _lib = L
-    return L
 
 
 def _check(fn, rc):

@@ -50,5 +50,34 @@ def build(verbose=False, jobs=8):
     return LIB
 
 
+def build_host_sanitized(verbose=False):
+    """Debug build for the CPU test tier: cq_api.cpp (the argument validation
+    of every entry point) compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code, linked with the regular
+    objects of the other translation units.  Needs build() first; returns
+    the library path.  Load it with clang's ASan runtime preloaded."""
+    objs = [os.path.join(OBJ_DIR, s + ".o") for s in SOURCES if s != "cq_api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"build() first: missing {missing}")
+    san_obj = os.path.join(OBJ_DIR, "cq_api.cpp.san.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    cmd = [HIPCC, *FLAGS, *san, "-x", "hip", "-c", os.path.join(CSRC, "cq_api.cpp"), "-o", san_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized cq_api.cpp:\n" + r.stdout + r.stderr)
+    out = os.path.join(OBJ_DIR, "libcq_hostsan.so")
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libsan",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            san_obj, *objs, "-o", out]
+    if verbose:
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True, capture_output=not verbose)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

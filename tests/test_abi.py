@@ -24,7 +24,17 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    return cq.load()
+    """libcq through its binding, or (CQ_TEST_LIB set: the sanitized
+    host-validation build) that library through ctypes with the binding's
+    signatures."""
+    path = os.environ.get("CQ_TEST_LIB")
+    if not path:
+        return cq.load()
+    L = ctypes.CDLL(path)
+    for name, (res, args) in cq.signatures().items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
 
 
 def test_every_declared_symbol_is_exported(lib):
