@@ -9,7 +9,10 @@ quants and, for Q4_K, uniform independent 6-bit scales and mins, because
 the 12 scale bytes carry each of their 96 bits in exactly one of the 16
 six-bit fields; for Q5_K the same plus uniform 5-bit quants (each qh bit
 is the top bit of exactly one quant); for Q6_K, uniform 6-bit quants (every bit of ql and qh
-belongs to exactly one quant) and uniform signed 8-bit scales.
+belongs to exactly one quant) and uniform signed 8-bit scales.  TQ2 (2-bit ternary)
+codes follow 8:16 structured sparsity: in every 16 consecutive values exactly 8
+are non-zero (a uniformly drawn 8-of-16 pattern) with uniform random signs, code
+01 for +1 and 11 for -1, 00 for zero, four codes per byte from the low bits up.
 
 Streams: numpy.random.default_rng([20261202, cfg, tensor]) with tensor ids
 0 = scales, 1 = quants, 2 = activations, 3 = expert ids, 4 = router logits,
@@ -19,12 +22,12 @@ import numpy as np
 
 SEED = 20261202
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0 = 2, 3, 8, 12, 13, 14, 41
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0, TQ2 = 2, 3, 8, 12, 13, 14, 41, 42
 FORMATS = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K,
-           "q1_0": Q1_0}
+           "q1_0": Q1_0, "tq2": TQ2}
 NAMES = {v: k for k, v in FORMATS.items()}
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q1_0: 128}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q1_0: 18}
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q1_0: 128, TQ2: 128}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q1_0: 18, TQ2: 34}
 
 # scale distributions (fp64 uniform draws, rounded to fp16 by numpy)
 D_RANGE = (1e-3, 2e-2)
@@ -42,6 +45,33 @@ def row_bytes(fmt, k):
 
 def _f16_field(g, count, lo, hi):
     return g.uniform(lo, hi, size=count).astype(np.float16).view(np.uint8).reshape(count, 2)
+
+
+_NM_PATTERNS = None
+_SPREAD8 = None
+
+
+def _nm_patterns():
+    """The 12870 16-bit masks with exactly 8 bits set, ascending."""
+    global _NM_PATTERNS
+    if _NM_PATTERNS is None:
+        allm = np.arange(1 << 16, dtype=np.uint32)
+        bits = np.unpackbits(allm.astype("<u2").view(np.uint8).reshape(-1, 2), axis=1).sum(axis=1)
+        _NM_PATTERNS = allm[bits == 8]
+    return _NM_PATTERNS
+
+
+def _spread16(x):
+    """Bit i of each 16-bit value moved to bit 2i (a 32-bit result)."""
+    global _SPREAD8
+    if _SPREAD8 is None:
+        v = np.arange(256, dtype=np.uint32)
+        sp = np.zeros(256, np.uint32)
+        for i in range(8):
+            sp |= ((v >> i) & 1) << (2 * i)
+        _SPREAD8 = sp
+    x = x.astype(np.uint32)
+    return _SPREAD8[x & 0xFF] | (_SPREAD8[x >> 8] << 16)
 
 
 def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
@@ -74,6 +104,13 @@ def weights(fmt, n, k, cfg, tensor=0, d_range=D_RANGE, m_range=M_RANGE):
     elif fmt == Q1_0:
         out[:, 0:2] = _f16_field(gs, nblk, *d_range)
         out[:, 2:18] = gq.integers(0, 256, size=(nblk, 16), dtype=np.uint8)   # sign bits
+    elif fmt == TQ2:
+        out[:, 0:2] = _f16_field(gs, nblk, *d_range)
+        ng = nblk * 8                                    # 16-value groups
+        mask = _nm_patterns()[gq.integers(0, 12870, size=ng)]
+        sign = gq.integers(0, 1 << 16, size=ng).astype(np.uint32)
+        code = _spread16(mask) | (_spread16(mask & sign) << 1)   # 01 = +1, 11 = -1
+        out[:, 2:34] = code.astype("<u4").view(np.uint8).reshape(nblk, 32)
     elif fmt == Q6_K:
         # ql[128], qh[64], 16 signed scale bytes: uniform random bytes;
         # d (fp16) last
@@ -130,4 +167,7 @@ CONFIGS = {
     "q4_0_gemm_prefill_2048": dict(cfg=13, kind="gemm", fmt=Q4_0, n=14336, k=4096, m=2048),
     "q4_k_moe_ffn": dict(cfg=4, kind="moe", fmt=Q4_K, n_tokens=256, hidden=2048, ffn=1536,
                          n_experts=32, top_k=4),
+    # 2-bit sparse ternary (8:16): the FFN gate projection of a 70B-class
+    # model, 28672 x 8192, at batch 1 and 4
+    "tq2_gemv_70b_gate": dict(cfg=42, kind="gemv", fmt=TQ2, n=28672, k=8192, batches=(1, 4)),
 }

@@ -12,9 +12,9 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0 = 2, 3, 8, 12, 13, 14, 41
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0, TQ2 = 2, 3, 8, 12, 13, 14, 41, 42
 TYPES = {"q4_0": Q4_0, "q4_1": Q4_1, "q8_0": Q8_0, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K,
-         "q1_0": Q1_0}
+         "q1_0": Q1_0, "tq2": TQ2}
 
 _lib = None
 

@@ -82,7 +82,7 @@ int64_t elems_of(int type) {
     switch (type) {
         case ORACLE_Q4_0: case ORACLE_Q4_1: case ORACLE_Q8_0: return 32;
         case ORACLE_Q4_K: case ORACLE_Q5_K: case ORACLE_Q6_K: return 256;
-        case ORACLE_Q1_0: return 128;
+        case ORACLE_Q1_0: case ORACLE_TQ2: return 128;
         default: return -1;
     }
 }
@@ -96,6 +96,7 @@ int64_t bytes_of(int type) {
         case ORACLE_Q5_K: return 176;  /* 2 + 2 + 12 + 32 + 128 [alice-Q5K] */
         case ORACLE_Q1_0: return 18;   /* 2 + 16 [alice-Q10]              */
         case ORACLE_Q6_K: return 210;  /* 128 + 64 + 16 + 2 [alice-Q6K]   */
+        case ORACLE_TQ2: return 34;    /* 2 + 32 (2 bits x 128) [alice-TQ] */
         default: return -1;
     }
 }
@@ -140,6 +141,13 @@ void q6k_element(const uint8_t* b, int e, int* q, int* scale) {
     *scale = sc[8 * h + 2 * g + l / 16];
 }
 
+/* TQ2: the value (0, +1 or -1) of 2-bit code i of the block at b, through
+ * the expansion table [0, +1, 0, -1] [alice-TQ]. */
+int tq2_value(const uint8_t* b, int i) {
+    static const int table[4] = {0, 1, 0, -1};
+    return table[(b[2 + i / 4] >> (2 * (i % 4))) & 3];
+}
+
 /* Decode one block to its elems_of(type) exact fp64 values. */
 void decode_block(int type, const uint8_t* b, double* out) {
     switch (type) {
@@ -168,6 +176,11 @@ void decode_block(int type, const uint8_t* b, double* out) {
         case ORACLE_Q8_0: {
             const double d = half_value(rd16(b));
             for (int i = 0; i < 32; ++i) out[i] = d * static_cast<int8_t>(b[2 + i]);
+            break;
+        }
+        case ORACLE_TQ2: {
+            const double d = half_value(rd16(b));
+            for (int i = 0; i < 128; ++i) out[i] = d * tq2_value(b, i);
             break;
         }
         case ORACLE_Q4_K: {
@@ -330,6 +343,21 @@ double factored_dot(int type, const uint8_t* wrow, const uint8_t* xrow, int64_t 
                 const uint8_t* xb = xrow + (blk * 4 + j) * 34;
                 const double dx = half_value(rd16(xb));
                 acc += d * dx * static_cast<double>(idot32(s, reinterpret_cast<const int8_t*>(xb + 2)));
+            }
+        }
+        return acc;
+    }
+    if (type == ORACLE_TQ2) {
+        /* per 32-value activation block: d*dx*sum(t*qx), t in {0, +1, -1} */
+        for (int64_t blk = 0; blk < k / 128; ++blk) {
+            const uint8_t* b = wrow + blk * 34;
+            const double d = half_value(rd16(b));
+            for (int j = 0; j < 4; ++j) {
+                int t[32];
+                for (int i = 0; i < 32; ++i) t[i] = tq2_value(b, 32 * j + i);
+                const uint8_t* xb = xrow + (blk * 4 + j) * 34;
+                const double dx = half_value(rd16(xb));
+                acc += d * dx * static_cast<double>(idot32(t, reinterpret_cast<const int8_t*>(xb + 2)));
             }
         }
         return acc;

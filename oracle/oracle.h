@@ -42,6 +42,11 @@
  *   [alice-Q5K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
  *                 a Q5_K super-block is 176 bytes for 256 values (5.5 bpw),
  *                 fields d (fp16), dmin (fp16), scales[12], qh[32], qs[128].
+ *   [alice-TQ]    alice-llm 2.0.0 README, "Sparse Ternary Quantization" and
+ *                 "The CPU Optimization Journey", Phase 5: packed 2-bit
+ *                 weights, four per byte, 00 = 0, 01 = +1, 11 = -1, expanded
+ *                 through a table [0, +1, 0, -1]; N:M structured sparsity
+ *                 (8 non-zero of every 16 values).
  *   [alice-Q6K]   alice-llm 2.0.0 README, "Quantization Block Specs" table:
  *                 a Q6_K super-block is 210 bytes for 256 values, fields
  *                 ql[128], qh[64], scales[16], d (fp16); and the NEON matvec
@@ -74,6 +79,13 @@
  *     4-5 (the four shift-masks above); element l + 32*g takes the signed
  *     scale byte scales[8h + 2g + l/16]; value d*scale*(q-32).  This is the
  *     GGUF layout, so real GGUF tensors decode as stored.
+ *   - TQ2 (2-bit ternary): 128 values in 34 bytes, an fp16 scale d then
+ *     32 bytes of 2-bit codes, four per byte; value i is code
+ *     (byte 2 + i/4 >> 2*(i%4)) & 3, least significant pair first.  Codes
+ *     00, 01, 11 are 0, +1, -1 [alice-TQ]; code 10, which the encoding never
+ *     produces, reads as 0 (the expansion table printed with it maps index 2
+ *     to 0).  Value = d * code value.  The pages print no scale placement;
+ *     one scale per 128 values is this build's reading.
  *   - Greedy arg-max: the first index of the largest value (NaN-free rows;
  *     -0 and +0 compare equal).
  *   - Router: the top_k largest logits in descending order (equal logits:
@@ -102,7 +114,8 @@ enum {
     ORACLE_Q4_K = 12,
     ORACLE_Q5_K = 13,
     ORACLE_Q1_0 = 41,   /* library-assigned id (the pages give no GGUF type id) */
-    ORACLE_Q6_K = 14
+    ORACLE_Q6_K = 14,
+    ORACLE_TQ2 = 42     /* 2-bit ternary, library-assigned id */
 };
 
 int oracle_abi_version(void);

@@ -387,7 +387,8 @@ def test_q4k_subblock_equals_q4_1(orc):
     assert np.array_equal(yk, y1)
 
 
-@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0])
+@pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0,
+                                 gs.TQ2])
 def test_two_formulations_agree(orc, fmt):
     n, m, k = 33, 5, 1024
     w = gs.weights(fmt, n, k, cfg=914)
@@ -403,7 +404,7 @@ def test_two_formulations_agree(orc, fmt):
 
 @pytest.mark.parametrize("fmt,k", [(gs.Q4_0, 32), (gs.Q4_1, 64), (gs.Q8_0, 96), (gs.Q4_K, 256),
                                    (gs.Q4_K, 512), (gs.Q5_K, 256), (gs.Q6_K, 256),
-                                   (gs.Q1_0, 128), (gs.Q1_0, 384)])
+                                   (gs.Q1_0, 128), (gs.Q1_0, 384), (gs.TQ2, 128), (gs.TQ2, 384)])
 def test_exact_rational_brute_force(orc, fmt, k):
     """Tiny shapes in exact rational arithmetic: the fp64 sums must agree
     with the exact value to within the fp64 summation bound."""
@@ -790,3 +791,67 @@ def test_q1_0_equals_q8_0_of_signs(orc):
     y1, _ = orc.matmul(gs.Q1_0, w1.reshape(n, -1), n, k, xq, 2)
     y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
     assert np.array_equal(y1, y8)
+
+
+# ------------------------------------------------ TQ2 (2-bit sparse ternary)
+def _tq2_block(d, codes):
+    """fp16 d, then the 128 2-bit codes four per byte, lowest pair first."""
+    codes = np.asarray(codes, np.uint8).reshape(32, 4)
+    packed = codes[:, 0] | (codes[:, 1] << 2) | (codes[:, 2] << 4) | (codes[:, 3] << 6)
+    return np.concatenate([np.array([d], np.float16).view(np.uint8), packed.astype(np.uint8)])
+
+
+def test_tq2_block_size(orc):
+    # four weights per byte (alice-llm 2.0.0 README, "Sparse Ternary
+    # Quantization"): 128 codes in 32 bytes after the 2-byte scale
+    assert orc.block_elems(gs.TQ2) == 128 and orc.block_bytes(gs.TQ2) == 34
+    assert orc.block_bytes(gs.TQ2) * 8 / orc.block_elems(gs.TQ2) == 2.125
+
+
+@pytest.mark.parametrize("code,value", [(0, 0.0), (1, 1.0), (3, -1.0), (2, 0.0)])
+def test_tq2_codes(orc, code, value):
+    # 00 = 0, 01 = +1, 11 = -1 (the page's encoding); 10 expands to 0 through
+    # the page's table [0, +1, 0, -1]
+    v = orc.dequantize(gs.TQ2, _tq2_block(0.75, np.full(128, code)), 128)
+    assert np.all(v == 0.75 * value)
+
+
+def test_tq2_code_order(orc):
+    """Code i sits in bits 2*(i%4) of byte 2 + i/4: a single 01 at position i
+    makes exactly value i equal to +d, a single 11 makes it -d."""
+    for i in [0, 1, 2, 3, 4, 31, 64, 126, 127]:
+        for code, sign in ((1, 1.0), (3, -1.0)):
+            c = np.zeros(128, np.uint8)
+            c[i] = code
+            blk = _tq2_block(2.0, c)
+            assert blk[2 + i // 4] == code << (2 * (i % 4))
+            v = orc.dequantize(gs.TQ2, blk, 128)
+            assert np.flatnonzero(v).tolist() == [i] and v[i] == 2.0 * sign
+
+
+def test_tq2_equals_q8_0_of_codes(orc):
+    """A TQ2 row equals the Q8_0 row with the same d and quants 0 / +1 / -1,
+    built in the test from the codes with numpy (exact in fp64)."""
+    n, k = 3, 1024
+    wt = gs.weights(gs.TQ2, n, k, cfg=950).reshape(-1, 34)
+    bits = np.unpackbits(wt[:, 2:34], axis=1, bitorder="little").reshape(-1, 128, 2)
+    codes = bits[:, :, 0] + 2 * bits[:, :, 1]
+    vals = np.array([0, 1, 0, -1], np.int8)[codes]
+    w8 = np.zeros((wt.shape[0] * 4, 34), np.uint8)
+    for j in range(4):
+        w8[j::4, 0:2] = wt[:, 0:2]
+        w8[j::4, 2:34] = vals[:, 32 * j: 32 * j + 32].view(np.uint8)
+    xq = orc.quantize_q8_0(gs.activations(2, k, cfg=950))
+    yt, _ = orc.matmul(gs.TQ2, wt.reshape(n, -1), n, k, xq, 2)
+    y8, _ = orc.matmul(gs.Q8_0, w8.reshape(n, -1), n, k, xq, 2)
+    assert np.array_equal(yt, y8)
+
+
+def test_tq2_generator_is_8_of_16_sparse():
+    """The synthetic TQ2 weights keep the pages' 8:16 structure: exactly 8
+    non-zero codes in every 16 consecutive values, only codes 00/01/11."""
+    w = gs.weights(gs.TQ2, 17, 2048, cfg=951).reshape(-1, 34)
+    bits = np.unpackbits(w[:, 2:34], axis=1, bitorder="little").reshape(-1, 128, 2)
+    codes = (bits[:, :, 0] + 2 * bits[:, :, 1]).reshape(-1, 16)
+    assert not (codes == 2).any()
+    assert np.all((codes != 0).sum(axis=1) == 8)
