@@ -319,8 +319,11 @@ def secondary(cq, gs, dev, stream):
         "python_burst_us": round(us_b, 2)}
     del big, mats
 
-    # FFN-up decode GEMVs 14336 x 4096: Q8_0 and Q4_1 at batch 1 and 5, Q5_K
-    for name in ("q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up", "q5_k_gemv_ffn_up"):
+    # FFN-up decode GEMVs 14336 x 4096: Q8_0 and Q4_1 at batch 1 and 5, Q5_K;
+    # the Q1_0 27B QKV projection 10240 x 5120 and the 2-bit ternary 70B gate
+    # projection 28672 x 8192 at batch 1 and 4
+    for name in ("q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up", "q5_k_gemv_ffn_up", "q1_0_gemv_qkv",
+                 "tq2_gemv_70b_gate"):
         c = gs.CONFIGS[name]
         n, k = c["n"], c["k"]
         wl = copies_of(gs.weights(c["fmt"], n, k, cfg=c["cfg"]), dev, 512 * 2**20)

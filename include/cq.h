@@ -40,6 +40,11 @@
  *   Q1_0  128 values, 18 B: d, then 16 bytes of sign bits; value i is bit
  *         i % 8 of byte 2 + i/8 (LSB first), +d when set, -d when clear
  *         (alice-llm 2.0.0 README, Bonsai 27B notes).  GEMV entry points only.
+ *   TQ2   128 values, 34 B: d, then 32 bytes of 2-bit codes, four per byte;
+ *         value i is code (byte 2 + i/4 >> 2*(i%4)) & 3, low pair first;
+ *         codes 00, 01, 11 give 0, +d, -d (alice-llm 2.0.0 README, "Sparse
+ *         Ternary Quantization"); 10, which that encoding never writes,
+ *         reads as 0.  GEMV entry points only.
  *   Q6_K  256 values, 210 B: ql[128], qh[64], 16 signed 8-bit scales, d.
  *         In half h (128 values), element l + 32g (l < 32, quadrant g) takes
  *         a nibble of ql[64h + l] (g = 0 low, g = 2 high) or ql[64h + 32 + l]
@@ -92,7 +97,8 @@ typedef enum {
 /* Weight types, numbered as the GGUF tensor type ids. */
 typedef enum { CQ_Q4_0 = 2, CQ_Q4_1 = 3, CQ_Q8_0 = 8, CQ_Q4_K = 12, CQ_Q5_K = 13,
                CQ_Q6_K = 14,
-               CQ_Q1_0 = 41 /* library-assigned: the pages give no GGUF id */ } cq_type;
+               CQ_Q1_0 = 41, /* library-assigned: the pages give no GGUF id */
+               CQ_TQ2 = 42   /* library-assigned: the pages give no GGUF id */ } cq_type;
 
 #define CQ_ABI_VERSION 2
 #define CQ_GEMV_MAX_BATCH 8
@@ -131,13 +137,14 @@ int cq_quantize_q8_0(const float* x, int64_t ldx, int64_t rows, int64_t k,
 /*
  * cq_gemv -- decode GEMV for 1..8 activation rows (speculative verify
  * rows included): y[b*ldy + i] = sum_j w_hat[i][j] * x_hat[b][j].
- *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K / CQ_Q1_0.
+ *   wt     CQ_Q4_0 / CQ_Q4_1 / CQ_Q8_0 / CQ_Q4_K / CQ_Q5_K / CQ_Q6_K / CQ_Q1_0 /
+ *          CQ_TQ2.
  *   w      [n][k/qk] blocks, 16-byte aligned.
  *   xq     [batch][k/32] Q8_0 blocks (as written by cq_quantize_q8_0),
  *          2-byte aligned.
  *   batch  1..CQ_GEMV_MAX_BATCH.
  *   y      fp32, row b at y + b*ldy, ldy >= n, 4-byte aligned.
- *   k      multiple of 32 (of 256 for Q4_K, Q5_K and Q6_K; of 128 for Q1_0),
+ *   k      multiple of 32 (of 256 for Q4_K, Q5_K and Q6_K; of 128 for Q1_0 and TQ2),
  *          k <= CQ_GEMV_MAX_K (a longer row returns CQ_ERR_SHAPE).
  * Each row b of a batched call is bitwise equal to the batch-1 call on that
  * row alone.  Accuracy: |y - y_exact| <= 2e-5 * sum_j |w_hat*x_hat|.

@@ -14,9 +14,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcq.so")
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0 = 2, 3, 8, 12, 13, 14, 41
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q1_0: 128}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q1_0: 18}
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K, Q1_0, TQ2 = 2, 3, 8, 12, 13, 14, 41, 42
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q1_0: 128, TQ2: 128}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q1_0: 18, TQ2: 34}
 GEMV_MAX_BATCH = 8
 
 STATUS = {0: "CQ_OK", -1: "CQ_ERR_INVALID_ARG", -2: "CQ_ERR_UNSUPPORTED_TYPE",

@@ -30,7 +30,7 @@ int64_t elems(int t) {
     switch (t) {
         case CQ_Q4_0: case CQ_Q4_1: case CQ_Q8_0: return 32;
         case CQ_Q4_K: case CQ_Q5_K: case CQ_Q6_K: return 256;
-        case CQ_Q1_0: return 128;
+        case CQ_Q1_0: case CQ_TQ2: return 128;
         default: return -1;
     }
 }
@@ -42,6 +42,7 @@ int64_t bytes(int t) {
         case CQ_Q4_K: return 144;
         case CQ_Q5_K: return 176;
         case CQ_Q1_0: return 18;
+        case CQ_TQ2: return 34;
         case CQ_Q6_K: return 210;
         default: return -1;
     }
@@ -93,7 +94,7 @@ const char* cq_status_string(int status) {
     switch (status) {
         case CQ_OK: return "CQ_OK";
         case CQ_ERR_INVALID_ARG: return "CQ_ERR_INVALID_ARG: null pointer, negative size or bad flag";
-        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K; Q1_0 in the GEMV entry points)";
+        case CQ_ERR_UNSUPPORTED_TYPE: return "CQ_ERR_UNSUPPORTED_TYPE: weight type not supported by this call (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K; Q1_0 and TQ2 in the GEMV entry points)";
         case CQ_ERR_SHAPE: return "CQ_ERR_SHAPE: k is not a whole number of blocks or exceeds the kernel's limit";
         case CQ_ERR_ALIGNMENT: return "CQ_ERR_ALIGNMENT: pointer or leading dimension misaligned";
         case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE: workspace smaller than required or misaligned";
@@ -228,7 +229,7 @@ int cq_topk_softmax(const float* logits, int64_t rows, int64_t n_experts, int64_
 int cq_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t m, float* y,
             int64_t ldy, cq_stream_t stream) {
     if (int rc = check_weights(wt, w, n, k)) return rc;
-    if (wt == CQ_Q1_0) return CQ_ERR_UNSUPPORTED_TYPE;
+    if (wt == CQ_Q1_0 || wt == CQ_TQ2) return CQ_ERR_UNSUPPORTED_TYPE;
     if (m < 0 || ldy < n) return CQ_ERR_INVALID_ARG;
     if (k % 256 != 0 || gemm_shape_ok(wt, n, k) != 0) return CQ_ERR_SHAPE;
     if (n == 0 || m == 0) return CQ_OK;
@@ -256,7 +257,7 @@ int cq_moe_group(const int32_t* expert_ids, int64_t n_tokens, int64_t top_k, int
 static int check_moe_gemm(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,
                           int64_t n_tokens, int64_t top_k, int64_t ldy) {
     if (int rc = check_weights(wt, w_experts, n, k)) return rc;
-    if (wt == CQ_Q1_0) return CQ_ERR_UNSUPPORTED_TYPE;
+    if (wt == CQ_Q1_0 || wt == CQ_TQ2) return CQ_ERR_UNSUPPORTED_TYPE;
     if (n_experts < 1 || n_experts > 1024 || n_tokens < 0 || top_k < 1 || top_k > n_experts ||
         ldy < n)
         return CQ_ERR_INVALID_ARG;

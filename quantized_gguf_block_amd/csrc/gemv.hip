@@ -47,15 +47,19 @@
 namespace cq {
 namespace {
 
-enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_Q1_0 = 41 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14, T_Q1_0 = 41,
+       T_TQ2 = 42 };
 
 // Q4_K and Q5_K share the super-block header (d, dmin, 6-bit scales and
 // mins) and the nibble chunks; Q5_K adds one high bit per value from qh.
 template <int FMT> constexpr bool kK45 = (FMT == T_Q4_K || FMT == T_Q5_K);
 // super-block formats: a lane column spans 64 values
 template <int FMT> constexpr bool kSuper = kK45<FMT> || FMT == T_Q6_K;
+// 128-value blocks whose lane column is half a block (64 values, two Q8_0
+// activation blocks): Q1_0 and the 2-bit ternary TQ2
+template <int FMT> constexpr bool kHalf128 = FMT == T_Q1_0 || FMT == T_TQ2;
 // one column per lane (no two-column streaming instantiation)
-template <int FMT> constexpr bool kOneCol = kSuper<FMT> || FMT == T_Q1_0;
+template <int FMT> constexpr bool kOneCol = kSuper<FMT> || kHalf128<FMT>;
 
 // columns per lane: a super-block column already spans 64 values, and a
 // Q1_0 column (64 values, 9 bytes) carries two activation blocks, so one
@@ -105,6 +109,15 @@ template <> struct Act<T_Q1_0> {
     float dx[2];
     float ndx[2];      // -12582912 * dx
     int start[2];      // kBias - sum(q): start of the dot with the 0/2 sign bytes
+};
+
+// TQ2 column (64 values): half col & 1 of block col >> 1, i.e. Q8_0
+// activation blocks 2 col and 2 col + 1, each quant word transposed per 16
+// values (see tq2_perm16) to match the code fields of the weight bytes.
+template <> struct Act<T_TQ2> {
+    uint32_t q[2][8];
+    float dx[2];
+    float ndx[2];      // -12582912 * dx
 };
 
 // Q6_K column (64 values): half h of super-block sb, l in [16 i, 16 i + 16)
@@ -199,6 +212,20 @@ __device__ __forceinline__ void load_q8_rs(__amdgpu_buffer_rsrc_t rs, int bo, ui
     *sum = acc;
 }
 
+// TQ2: the 16 activation quants of values v..v+15 (four words, value v+4i+p
+// in byte p of word i) rearranged so that word p holds values v+p, v+4+p,
+// v+8+p, v+12+p: the order of the code fields p of four weight bytes.
+__device__ __forceinline__ void tq2_perm16(const uint32_t* w, uint32_t* o) {
+    const uint32_t a01l = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+    const uint32_t a01h = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+    const uint32_t a23l = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    o[0] = __builtin_amdgcn_perm(a23l, a01l, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(a23l, a01l, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(a23h, a01h, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(a23h, a01h, 0x07060302u);
+}
+
 // The Q8_0 activation of lane column col (its blocks and the per-block
 // terms the dot chains start from) for one batch row, whose first byte is
 // at offset xo from the resource base.
@@ -218,6 +245,16 @@ __device__ __forceinline__ void load_act_rs(__amdgpu_buffer_rsrc_t rs, int xo, i
             int sum;
             load_q8_rs(rs, xo + (2 * col + j) * 34, a.q[j], &a.dx[j], &sum);
             a.start[j] = kBias - sum;
+            a.ndx[j] = -kBiasF * a.dx[j];
+        }
+    } else if constexpr (FMT == T_TQ2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int sum;
+            uint32_t q[8];
+            load_q8_rs(rs, xo + (2 * col + j) * 34, q, &a.dx[j], &sum);
+            tq2_perm16(q, a.q[j]);
+            tq2_perm16(q + 4, a.q[j] + 4);
             a.ndx[j] = -kBiasF * a.dx[j];
         }
     } else if constexpr (FMT == T_Q6_K) {
@@ -260,6 +297,7 @@ __device__ __forceinline__ int col_offset(int row_base, int col) {
     else if constexpr (FMT == T_Q5_K) return row_base + (col >> 2) * 176;
     else if constexpr (FMT == T_Q6_K) return row_base + (col >> 2) * 210;
     else if constexpr (FMT == T_Q1_0) return row_base + (col >> 1) * 18;
+    else if constexpr (FMT == T_TQ2) return row_base + (col >> 1) * 34;
     else return row_base + col * Fmt<FMT>::BS;
 }
 
@@ -378,6 +416,40 @@ __device__ __forceinline__ void q10_column_dot(const uint8_t* lds, int off, int 
     }
 }
 
+// acc[j] += one TQ2 column (see Act<T_TQ2>) of the block at LDS byte offset
+// off (2-byte aligned).  Codes 10 become 00 first (each high bit is kept only
+// where its low bit is set), then the code field p of every byte is shifted
+// to the top two bits of the byte, where as a signed byte it reads 64 times
+// the code value (01: 64, 11: -64, 00: 0); four such words against the
+// transposed activation words give 64 * sum(t * qx) from kBias, then dx, then
+// d / 64 (exact).
+template <int B>
+__device__ __forceinline__ void tq2_column_dot(const uint8_t* lds, int off, int col,
+                                               const Act<T_TQ2>* a, float* acc) {
+    const float d64 = h2f(lds_u16(lds, off)) * 0.015625f;
+    uint32_t code[4];
+    lds_dwords_a2<4>(lds, off + 2 + 16 * (col & 1), code);
+    const int bias = bias_sgpr();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint32_t f[8];   // 16 values per code word: fields 0..3
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t c = code[2 * j + h] & ((code[2 * j + h] << 1) | 0x55555555u);
+            f[4 * h + 0] = (c << 6) & 0xC0C0C0C0u;
+            f[4 * h + 1] = (c << 4) & 0xC0C0C0C0u;
+            f[4 * h + 2] = (c << 2) & 0xC0C0C0C0u;
+            f[4 * h + 3] = c & 0xC0C0C0C0u;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int s = dot8<B == 1, true>(f, a[b].q[j], bias);
+            const float sx = fmaf(__int_as_float(s), a[b].dx[j], a[b].ndx[j]);
+            acc[b] = fmaf(sx, d64, acc[b]);
+        }
+    }
+}
+
 // acc[j] += dot of one column of one weight row with activation row j.
 template <int FMT, int B>
 __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Act<FMT>* a,
@@ -453,6 +525,8 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         q6k_column_dot<B>(lds, off, col, a, acc);
     } else if constexpr (FMT == T_Q1_0) {
         q10_column_dot<B>(lds, off, col, a, acc);
+    } else if constexpr (FMT == T_TQ2) {
+        tq2_column_dot<B>(lds, off, col, a, acc);
     } else if constexpr (FMT == T_Q5_K) {  // chunk c, its 32 qh bytes at off + 16
         const int c = col & 3;
         const uint4 h4 = *reinterpret_cast<const uint4*>(lds + off);  // 16-aligned
@@ -741,6 +815,10 @@ template <int C> struct Win<T_Q1_0, C> {                 // (reads LDS directly)
     static constexpr bool kMis = false;
     static constexpr int NDW = 1;
 };
+template <int C> struct Win<T_TQ2, C> {                  // (reads LDS directly)
+    static constexpr bool kMis = false;
+    static constexpr int NDW = 1;
+};
 template <int C> struct Win<T_Q6_K, C> {                 // (reads LDS directly)
     static constexpr bool kMis = false;
     static constexpr int NDW = 1;
@@ -820,6 +898,7 @@ template <int FMT> constexpr int col_bytes() {
     else if constexpr (FMT == T_Q5_K) return 44;
     else if constexpr (FMT == T_Q6_K) return 53;
     else if constexpr (FMT == T_Q1_0) return 9;
+    else if constexpr (FMT == T_TQ2) return 17;
     else return Fmt<FMT>::BS;
 }
 
@@ -829,6 +908,7 @@ template <int FMT, int C> constexpr int slice_bytes() {
     else if constexpr (FMT == T_Q5_K) return kWave * C / 4 * 176;
     else if constexpr (FMT == T_Q6_K) return kWave * C / 4 * 210;
     else if constexpr (FMT == T_Q1_0) return kWave * C / 2 * 18;
+    else if constexpr (FMT == T_TQ2) return kWave * C / 2 * 34;
     else return kWave * C * Fmt<FMT>::BS;
 }
 
@@ -836,7 +916,7 @@ constexpr int kGW = 4;  // waves per workgroup of the streaming kernel (one per 
 
 // Largest activation bytes (all batch rows) one streaming workgroup stages.
 template <int FMT, int B, int C>
-constexpr int kActMax = B * (kSuper<FMT> || FMT == T_Q1_0 ? 128 : 64) * C * 34;
+constexpr int kActMax = B * (kSuper<FMT> || kHalf128<FMT> ? 128 : 64) * C * 34;
 
 // Routed-expert addressing for decode (MOE): blockIdx.y is the
 // token-expert pair p = t*top_k + s; its matrix is expert ids[p] of the
@@ -890,7 +970,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     // batch row j sits at index (j*NS + h)*NP + 64*i + l, so a wave's lanes
     // read consecutive words (no bank conflicts).  A slot is one Q8_0 block
     // (Q6_K: the 16 values of one quadrant that the column covers).
-    constexpr int NS = (kK45<FMT> || FMT == T_Q1_0) ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
+    constexpr int NS = (kK45<FMT> || kHalf128<FMT>) ? 2 : FMT == T_Q6_K ? 4 : 1;  // slots per column
     constexpr int NP = kWave * C;                                  // column positions per row
     constexpr int NBMAX = KS == 1 ? B * NS * NP : 1;              // slots, all rows
     constexpr int STG = NJ * 1024 + 16;                          // staging bytes per wave
@@ -932,6 +1012,9 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
     } else if constexpr (FMT == T_Q1_0) {
         c0 = valid ? C * lane : 0;               // first column; block c0 / 2
         off = (c0 >> 1) * 18;
+    } else if constexpr (FMT == T_TQ2) {
+        c0 = valid ? C * lane : 0;
+        off = (c0 >> 1) * 34;
     } else {
         off = valid ? C * lane * Fmt<FMT>::BS : 0;
     }
@@ -1038,6 +1121,13 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     for (int u = 0; u < 8; ++u) q[u] = __builtin_amdgcn_alignbit(wd[u + 1], wd[u], sh);
                     dx = h2f(*reinterpret_cast<const uint16_t*>(xs + bo));
                 }
+                if constexpr (FMT == T_TQ2) {   // code-field order, once per workgroup
+                    uint32_t t[8];
+                    tq2_perm16(q, t);
+                    tq2_perm16(q + 4, t + 4);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) q[u] = t[u];
+                }
                 xq0[gi] = u32x4{q[0], q[1], q[2], q[3]};
                 xq1[gi] = u32x4{q[4], q[5], q[6], q[7]};
                 xda[gi] = dx;
@@ -1046,7 +1136,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
 #pragma unroll
                     for (int u = 0; u < 4; ++u) sum = sdot4(q[u], 0x01010101u, sum);
                     xau[gi] = __int_as_float(sum);
-                } else if constexpr (FMT != T_Q8_0) {
+                } else if constexpr (FMT != T_Q8_0 && FMT != T_TQ2) {
                     int sum = 0;
 #pragma unroll
                     for (int u = 0; u < 8; ++u) sum = sdot4(q[u], 0x01010101u, sum);
@@ -1073,6 +1163,17 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     a.dx[h] = xda[gi];
                     a.ndx[h] = -kBiasF * a.dx[h];
                     a.start[h] = kBias - __float_as_int(xau[gi]);
+                }
+            } else if constexpr (FMT == T_TQ2) {
+                Act<T_TQ2>& a = act[i][j];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int gi = (j * NS + h) * NP + kWave * i + lane;
+                    const u32x4 q0 = xq0[gi], q1 = xq1[gi];
+                    a.q[h][0] = q0.x; a.q[h][1] = q0.y; a.q[h][2] = q0.z; a.q[h][3] = q0.w;
+                    a.q[h][4] = q1.x; a.q[h][5] = q1.y; a.q[h][6] = q1.z; a.q[h][7] = q1.w;
+                    a.dx[h] = xda[gi];
+                    a.ndx[h] = -kBiasF * a.dx[h];
                 }
             } else if constexpr (FMT == T_Q6_K) {
                 Act<T_Q6_K>& a = act[i][j];
@@ -1158,6 +1259,10 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
 #pragma unroll
                 for (int cc = 0; cc < C; ++cc)
                     q10_column_dot<B>(stage, ((c0 + cc) >> 1) * 18, c0 + cc, act[cc], acc[i]);
+            } else if constexpr (FMT == T_TQ2) {
+#pragma unroll
+                for (int cc = 0; cc < C; ++cc)
+                    tq2_column_dot<B>(stage, ((c0 + cc) >> 1) * 34, c0 + cc, act[cc], acc[i]);
             } else if constexpr (kK45<FMT>) {
                 // header (and Q5_K's 32 qh bytes), then the C nibble chunks
                 constexpr int NH = FMT == T_Q4_K ? 1 : 3;
@@ -1182,7 +1287,7 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     v[W::NDW - 1] >>= mis;
                 }
             }
-            if constexpr (FMT != T_Q6_K && FMT != T_Q1_0) row_dot<FMT, B, C>(v, act, c0, acc[i]);
+            if constexpr (FMT != T_Q6_K && !kHalf128<FMT>) row_dot<FMT, B, C>(v, act, c0, acc[i]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1252,8 +1357,9 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     const int64_t xrb = k / 32 * 34;
     Plan p{};
     const bool super = wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K;
-    p.ncols = static_cast<int>(super || wt == T_Q1_0 ? k / 64 : k / 32);   // Q1_0: half blocks
-    p.C = (super || wt == T_Q1_0 || p.ncols <= kWave) ? 1 : 2;
+    const bool half128 = wt == T_Q1_0 || wt == T_TQ2;
+    p.ncols = static_cast<int>(super || half128 ? k / 64 : k / 32);   // Q1_0, TQ2: half blocks
+    p.C = (super || half128 || p.ncols <= kWave) ? 1 : 2;
     p.nw = (p.ncols + kWave * p.C - 1) / (kWave * p.C);
     // general kernel: about 16 KiB of weights per tile, at most 32 live
     // accumulators per lane
@@ -1270,7 +1376,7 @@ Plan make_plan(int wt, int64_t k, int64_t rb, int batch, bool stream_ok) {
     const int sc = (p.ncols + kWave - 1) / kWave;
     p.KS = 1;
     if (stream_ok && rb % 16 == 0 && xrb % 16 == 0 && sc <= 2 && p.ncols % sc == 0 &&
-        !((super || wt == T_Q1_0) && sc == 2)) {
+        !((super || half128) && sc == 2)) {
         p.SC = sc;
     } else if (rb % 16 == 0 && p.ncols > kWave * p.C &&
                p.ncols <= kGW * kWave * p.C && p.ncols % p.C == 0) {
@@ -1387,11 +1493,11 @@ int launch_fmt(const Plan& p, int batch, const uint8_t* w, int64_t n, int64_t rb
 }
 
 int64_t block_bytes_of(int wt) {
-    return wt == T_Q4_0 || wt == T_Q1_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 ? 34
+    return wt == T_Q4_0 || wt == T_Q1_0 ? 18 : wt == T_Q4_1 ? 20 : wt == T_Q8_0 || wt == T_TQ2 ? 34
            : wt == T_Q4_K ? 144 : wt == T_Q5_K ? 176 : 210;
 }
 int64_t block_elems_of(int wt) {
-    return wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : wt == T_Q1_0 ? 128 : 32;
+    return wt == T_Q4_K || wt == T_Q5_K || wt == T_Q6_K ? 256 : wt == T_Q1_0 || wt == T_TQ2 ? 128 : 32;
 }
 
 }  // namespace
@@ -1426,6 +1532,7 @@ int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
         case T_Q5_K: return launch_fmt<T_Q5_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q6_K: return launch_fmt<T_Q6_K>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         case T_Q1_0: return launch_fmt<T_Q1_0>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
+        case T_TQ2: return launch_fmt<T_TQ2>(p, b, wp, n, rb, xp, xrb, y, ldy, stream);
         default: return -2;
     }
 }
@@ -1500,6 +1607,7 @@ int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, 
         case T_Q5_K: return launch_sw<T_Q5_K>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         case T_Q6_K: return launch_sw<T_Q6_K>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         case T_Q1_0: return launch_sw<T_Q1_0>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
+        case T_TQ2: return launch_sw<T_TQ2>(p.SC, p.KS, b, wg, wu, n, rb, p.ncols, xp, xrb, h, ldh, stream);
         default: return -2;
     }
 }
@@ -1547,6 +1655,7 @@ int launch_moe_gemv_any(int wt, const void* w, const void* w2, int64_t n_experts
         case T_Q5_K: return launch_moe_gemv_fmt<T_Q5_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         case T_Q6_K: return launch_moe_gemv_fmt<T_Q6_K, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         case T_Q1_0: return launch_moe_gemv_fmt<T_Q1_0, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
+        case T_TQ2: return launch_moe_gemv_fmt<T_TQ2, SW>(p.SC, wp, wp2, n, rb, p.ncols, xp, xrb, y, ldy, mm, np, s);
         default: return -2;
     }
 }

@@ -57,6 +57,8 @@ def test_block_geometry(lib):
     assert [lib.cq_block_bytes(t) for t in (2, 3, 8, 12, 13, 14)] == [18, 20, 34, 144, 176, 210]
     assert lib.cq_row_bytes(13, 4096) == 2816
     assert (lib.cq_block_elems(41), lib.cq_block_bytes(41), lib.cq_row_bytes(41, 5120)) == (128, 18, 720)
+    assert (lib.cq_block_elems(42), lib.cq_block_bytes(42), lib.cq_row_bytes(42, 8192)) == (128, 34, 2176)
+    assert lib.cq_row_bytes(42, 8160) == -1
     assert lib.cq_row_bytes(14, 4096) == 3360
     assert lib.cq_row_bytes(12, 4096) == 2304
     assert lib.cq_row_bytes(8, 4096) == 4352
@@ -164,6 +166,7 @@ def test_gemm_validation(lib):
     assert f(5, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
     assert f(7, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED
     assert f(41, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED  # Q1_0: GEMV only
+    assert f(42, P(FAKE), 8, 256, P(FAKE), 4, P(FAKE), 8, None) == UNSUPPORTED  # TQ2: GEMV only
     # Q6_K rows are read with 31-bit offsets: a matrix of 2 GiB or more is refused
     assert f(14, P(FAKE), 1 << 20, 2560, P(FAKE), 4, P(FAKE), 1 << 20, None) == SHAPE
 
@@ -227,6 +230,7 @@ def test_moe_one_call_validation(lib):
     assert call(flags=4) == INVALID
     assert call(flags=-1) == INVALID
     assert call(wt=41) == UNSUPPORTED
+    assert call(wt=42) == UNSUPPORTED
     assert call(wt=7) == UNSUPPORTED
     assert call(k=1000) == SHAPE
     assert call(top_k=40) == INVALID

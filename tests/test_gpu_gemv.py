@@ -13,7 +13,7 @@ from gpu_common import assert_close_to_oracle, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0]
+FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K, gs.Q1_0, gs.TQ2]
 
 
 def run_gemv(cq, fmt, w, n, k, xq, batch):
@@ -46,7 +46,7 @@ def config_inputs(name):
 
 
 @pytest.mark.parametrize("name", ["q4_0_gemv_2048", "q8_0_gemv_ffn_up", "q4_1_gemv_ffn_up",
-                                  "q5_k_gemv_ffn_up", "q1_0_gemv_qkv"])
+                                  "q5_k_gemv_ffn_up", "q1_0_gemv_qkv", "tq2_gemv_70b_gate"])
 def test_gemv_config_full(cq, orc, name):
     c, w, x = config_inputs(name)
     xq = orc.quantize_q8_0(x)
@@ -175,7 +175,8 @@ def test_gemv_zero_weights_exact(cq, orc):
     assert not y.any()
 
 
-@pytest.mark.parametrize("fmt", [gs.Q8_0, gs.Q4_K, gs.Q6_K, gs.Q1_0], ids=lambda f: gs.NAMES[f])
+@pytest.mark.parametrize("fmt", [gs.Q8_0, gs.Q4_K, gs.Q6_K, gs.Q1_0, gs.TQ2],
+                         ids=lambda f: gs.NAMES[f])
 def test_gemv_max_k(cq, orc, fmt):
     """k = CQ_GEMV_MAX_K (32768): the multi-wave kernel at its largest row
     (8 waves), with a ragged row count, at batch 1 and 8; one block more per
