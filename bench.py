@@ -19,7 +19,8 @@ Printed: one JSON line.
              null once the GEMV source has changed since it was taken.
   gemm       the prefill GEMM (Q4_0, 14336 x 4096) at 2048 and 512 tokens,
              weights rotated through copies, in int8 TOPS; its roofline
-             against the int8 MFMA peak, with the MFMA-busy fraction from the
+             against the int8 MFMA peak (each launch between its own pair of
+             HIP events), with the MFMA-busy fraction from the
              committed counter summary (null once the GEMM source changed).
   cpu_baseline  the CPU oracle (fp64, plain C++) on the same step, on all
              the cores this process may use and on one core.
@@ -74,8 +75,8 @@ def profile_record(fname, tag, kernel, sha):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM line")
@@ -102,6 +103,23 @@ def burst_us(fn, reps, stream, warm=3):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps * 1e3
+
+
+def bracketed_us(fn, reps, stream, warm=3):
+    """Average duration of one call fn(i) over `reps` calls, each between its
+    own pair of HIP events on the launch stream (what a kernel trace reports
+    per dispatch, plus the event packets' own few microseconds)."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [events() for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
 
 
 def graph_us(fn, nsteps, reps, stream):
@@ -145,7 +163,7 @@ def lm_head_kernel(batch):
 
 
 def gemm_kernel_name():
-    return "gemm_kernel<2>"
+    return "gemm2_kernel<2>"
 
 
 def main():
@@ -201,12 +219,14 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
     value = 2 * wbytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: the batch-4 GEMV, a burst of back-to-back launches on
-    # rotating copies (per-launch duration, the figure the profiler's kernel
-    # duration corresponds to); the batch-1 GEMV and the quantizer beside it
+    # dominant kernel: the batch-4 GEMV, right after the timed steps, as a
+    # burst of back-to-back launches on the rotating copies between two HIP
+    # events on the launch stream (an event pair around every launch would
+    # add the event packets' own few microseconds to each); the batch-1 GEMV
+    # and the quantizer beside it
     us_b4 = burst_us(lambda i: gemv(B), 60, stream)
     us_b1 = burst_us(lambda i: gemv(1), 60, stream)
-    us_q = burst_us(lambda i: cq.cq_quantize_q8_0(xd, xq), 200, stream)
+    us_q = graph_us(lambda i: cq.cq_quantize_q8_0(xd, xq), 50, 10, stream)
     alg = {b: wbytes + b * (k // 32 * 34) + b * n * 4 for b in (1, B)}
     achieved = alg[B] / (us_b4 * 1e-6) / 1e9
     gsha = source_sha(GEMV_SOURCES)
@@ -244,7 +264,8 @@ def main():
                      "avg_launch_us": round(us_b4, 3),
                      "alg_bytes_per_launch": alg[B],
                      "traffic_over_alg": round(traffic / alg[B], 4) if traffic else None,
-                     "rocprof_avg_kernel_us": kt["avg_us"] if kt else None},
+                     "rocprof_avg_kernel_us": kt["avg_us"] if kt else None,
+                     "rocprof_timed_steps_avg_us": kt.get("timed_steps_avg_us") if kt else None},
         "step_kernels_us": {"quantize_4_rows": round(us_q, 2),
                             "gemv_b1": round(us_b1, 2), "gemv_b4": round(us_b4, 2),
                             "gemv_b1_GB/s": round(alg[1] / us_b1 / 1e3, 1),
@@ -270,8 +291,8 @@ def prefill_gemm(cq, gs, dev, stream):
         wl = copies_of(gs.weights(c["fmt"], n, k, cfg=c["cfg"]), dev, 512 * 2**20)
         xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c["cfg"])).to(dev))
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        us = burst_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y),
-                      40 if m == 2048 else 100, stream)
+        us = bracketed_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y),
+                          40 if m == 2048 else 100, stream)
         tops = 2 * m * n * k / us / 1e6
         res[m] = (us, tops)
         out[f"q4_0_gemm_{m}x{n}x{k}"] = {"us": round(us, 2), "TOPS": round(tops, 1),
