@@ -459,12 +459,33 @@ def secondary(cq, gs, dev, stream):
         cq.cq_moe_gemm(gs.Q4_K, wd_, E, H, F, hq, f_dn, ids, route_w=rw, y=yt, workspace=ws)
 
     us = graph_us(ffn, len(sets), 10, stream)
+
+    # the same FFN with the grouping computed once and shared by the three
+    # projections (split form), D per pair, then the slot-order combine
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    prs = torch.empty(T * K, dtype=torch.int32, device=dev)
+    gst = torch.empty(1, dtype=torch.int32, device=dev)
+    dpp = torch.empty((T * K, H), dtype=torch.float32, device=dev)
+
+    def ffn_grouped(i):
+        wg_, wu_, wd_ = sets[i % len(sets)]
+        cq.cq_quantize_q8_0(x, xq)
+        cq.cq_moe_group(ids, E, offsets=offs, pairs=prs, status=gst)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wg_, E, F, H, xq, False, offs, prs, T, K, y=g)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wu_, E, F, H, xq, False, offs, prs, T, K, y=u)
+        cq.cq_swiglu_quantize_q8_0(g, u, hq=hq)
+        cq.cq_moe_gemm_grouped(gs.Q4_K, wd_, E, H, F, hq, True, offs, prs, T, K, y=dpp)
+        cq.cq_moe_combine(dpp, rw, y=yt)
+
+    us_g = graph_us(ffn_grouped, len(sets), 10, stream)
     ops = 2 * T * K * (2 * F * H + H * F)
     out["q4_k_moe_ffn_256tok_32x_top4"] = {
-        "graph_us": round(us, 2), "expert_weight_GB/s": round(wbytes / us / 1e3, 1),
-        "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
-        "int8_TOPS": round(ops / us / 1e6, 1),
-        "pct_int8_mfma_peak": round(100 * ops / us / 1e6 / MFMA_I8_PEAK_TOPS, 2),
+        "graph_us": round(us_g, 2), "expert_weight_GB/s": round(wbytes / us_g / 1e3, 1),
+        "pct_hbm_peak": round(100 * wbytes / us_g / 1e3 / HBM_PEAK_GBS, 1),
+        "int8_TOPS": round(ops / us_g / 1e6, 1),
+        "pct_int8_mfma_peak": round(100 * ops / us_g / 1e6 / MFMA_I8_PEAK_TOPS, 2),
+        "sequence": "quantize, group once, gate, up, SwiGLU+requant, down, combine",
+        "one_call_per_projection_graph_us": round(us, 2),
         "weight_sets": len(sets)}
 
     # router: top 4 of 32 with softmax, 256 tokens
