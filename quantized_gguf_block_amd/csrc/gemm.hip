@@ -496,6 +496,24 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
 // Dense GEMM with one LDS buffer (the formats whose scale tables do not
 // leave room for two buffers at two workgroups per CU): 128 x 128 tiles,
 // 2 x 2 waves of 64 x 64.
+// Workgroup g of G -> tile index (token tile = tile % tiles_m, weight tile =
+// tile / tiles_m).  Workgroups are dealt round-robin over the 8 XCDs; each
+// XCD takes a contiguous range of weight tiles with all their token tiles,
+// walked in bands of two token tiles across the XCD's weight tiles, so the
+// workgroups resident on an XCD at once share a few token tiles and all of
+// its weight tiles in that XCD's L2 (the L2 fetches at 2048 tokens drop from
+// about 3.0x to 1.9x the operand bytes).  Grids that do not split evenly keep
+// the plain contiguous order.
+__device__ __forceinline__ int tile_of(int g, int G, int tiles_m) {
+    const int per_xcd = G / 8;
+    if (g >= 8 * per_xcd) return g;
+    const int l = g / 8;
+    if (per_xcd % tiles_m != 0 || tiles_m % 2 != 0) return (g % 8) * per_xcd + l;
+    const int nl = per_xcd / tiles_m;          // weight tiles of this XCD
+    const int band = l / (2 * nl), rem = l % (2 * nl);
+    return ((g % 8) * nl + rem / 2) * tiles_m + 2 * band + (rem & 1);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         const uint8_t* __restrict__ w, int64_t n, int64_t k, int64_t rb,
@@ -503,12 +521,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
         int tiles_m, int tiles_total) {
     using T = Tile<2, 2, 2, 2>;
     __shared__ __align__(16) Smem<T::BM, 128> s;
-    // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin,
-    // so give each XCD a contiguous run of tiles (the M tiles of one weight
-    // tile then share that XCD's L2).
     const int G = gridDim.x, g = blockIdx.x;
-    const int per_xcd = G / 8;
-    const int tile = (g < 8 * per_xcd) ? (g % 8) * per_xcd + g / 8 : g;
+    const int tile = tile_of(g, G, tiles_m);
     if (tile >= tiles_total) return;
     const int64_t m0 = static_cast<int64_t>(tile % tiles_m) * T::BM;
     const int64_t n0 = static_cast<int64_t>(tile / tiles_m) * T::BN;
@@ -641,8 +655,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_kernel(
         int tiles_m, int tiles_total) {
     __shared__ __align__(16) Smem2<FMT> sm[2];
     const int G = gridDim.x, g = blockIdx.x;
-    const int per_xcd = G / 8;
-    const int tile = (g < 8 * per_xcd) ? (g % 8) * per_xcd + g / 8 : g;
+    const int tile = tile_of(g, G, tiles_m);
     if (tile >= tiles_total) return;
     const int64_t m0 = static_cast<int64_t>(tile % tiles_m) * 128;
     const int64_t n0 = static_cast<int64_t>(tile / tiles_m) * 128;

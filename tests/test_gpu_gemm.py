@@ -16,7 +16,10 @@ FMTS = [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q4_K, gs.Q5_K, gs.Q6_K]
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("m,n,k", [(1, 1, 256), (37, 130, 256), (128, 128, 512), (200, 300, 1024),
-                                   (5, 257, 4096), (129, 64, 768)])
+                                   (5, 257, 4096), (129, 64, 768),
+                                   # grids dealt to the XCDs in bands of two token
+                                   # tiles (ragged m and n), with and without tail tiles
+                                   (250, 1000, 512), (250, 1100, 512), (500, 2000, 256)])
 def test_gemm_small_shapes(cq, orc, fmt, m, n, k):
     note("gemm", gs.NAMES[fmt], m, n, k)
     w = gs.weights(fmt, n, k, cfg=600 + m)
