@@ -781,7 +781,10 @@ __global__ __launch_bounds__(kThreads, 2) void moe_gemm_kernel(
 // bits), acc = fma(t, dx, acc); the -dmin*m * dx*sum(qx) term goes through
 // v_mfma_f32_16x16x4_f32, four sub-blocks at a time.
 constexpr int kSbTok = 64;             // tokens per pass
-constexpr int kSbRow = 8 * 32 + 16;    // LDS row stride of the activation tile
+// LDS row stride of the activation tile: 264 bytes (66 dwords) puts the
+// 8-byte MFMA operand reads of 16 consecutive token rows on distinct banks
+// (the 272-byte stride paired rows j and j + 8 on one bank)
+constexpr int kSbRow = 8 * 32 + 8;
 constexpr int kSbRows = 64;            // weight rows per workgroup (16 per wave)
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -789,7 +792,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 struct ActTile {
     int8_t x[kSbTok * kSbRow];
     float dx[8][kSbTok];
-    float sx[8][kSbTok];
+    float sx[8][kSbTok + 16];   // rows padded: the four sub-block rows one
+                                // read instruction touches fall on distinct banks
 };
 
 struct StreamSmem {
@@ -860,9 +864,11 @@ __device__ __forceinline__ void store_acts(ActTile& at, const ARegs& a) {
         for (int i = 0; i < 8; ++i) sum = sdot4(o[i], 0x01010101u, sum);
         at.dx[b][r] = dx;
         at.sx[b][r] = dx * static_cast<float>(sum);
-        uint4* d4 = reinterpret_cast<uint4*>(at.x + r * kSbRow + 32 * b);
-        d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        uint2* d2 = reinterpret_cast<uint2*>(at.x + r * kSbRow + 32 * b);   // 8-byte aligned rows
+        d2[0] = make_uint2(o[0], o[1]);
+        d2[1] = make_uint2(o[2], o[3]);
+        d2[2] = make_uint2(o[4], o[5]);
+        d2[3] = make_uint2(o[6], o[7]);
     }
 }
 
