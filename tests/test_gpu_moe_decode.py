@@ -87,6 +87,37 @@ def test_moe_gemv_q6k_needs_whole_16_byte_rows(cq, orc):
     assert_close_to_oracle(g, g_ref, sg, what="moe gemv q6_k gate")
 
 
+@pytest.mark.parametrize("fmt", [gs.Q1_0, gs.TQ2], ids=lambda f: gs.NAMES[f])
+def test_moe_gemv_decode_sub_2bit(cq, orc, fmt):
+    """Q1_0 and TQ2 experts on the routed decode path: the gate and the
+    fused gate/up + SwiGLU (k = 2048) against the oracle and bitwise against
+    cq_gemv / the SwiGLU of the two outputs; the down projection (k = 1536:
+    rows of 216 / 408 bytes, not whole 16-byte pieces) is refused."""
+    wg, wu, wd = experts(fmt)
+    n_tokens = 3
+    ids, _ = gs.routing(n_tokens, E, K, cfg=836)
+    xq_h = orc.quantize_q8_0(gs.activations(n_tokens, H, cfg=836))
+    wgd, wud, xq, idd = to_dev(wg), to_dev(wu), to_dev(xq_h), to_dev(ids)
+    note("moe gemv sub-2-bit gate", gs.NAMES[fmt])
+    g, st = cq.cq_moe_gemv(fmt, wgd, E, F, H, xq, False, idd)
+    g = to_host(g)
+    g_ref, sg = orc.moe_matmul(fmt, wg, E, F, H, xq_h, False, ids)
+    assert_close_to_oracle(g, g_ref, sg, what=f"moe gemv {gs.NAMES[fmt]} gate")
+    for p in range(n_tokens * K):
+        e, t = int(ids.flat[p]), p // K
+        yp = to_host(cq.cq_gemv(fmt, wgd[e * F:(e + 1) * F], F, H, xq[t:t + 1], 1))
+        assert np.array_equal(yp[0], g[p]), p
+    u = to_host(cq.cq_moe_gemv(fmt, wud, E, F, H, xq, False, idd, status=st)[0])
+    note("moe gemv sub-2-bit swiglu", gs.NAMES[fmt])
+    h = to_host(cq.cq_moe_gemv_swiglu(fmt, wgd, wud, E, F, H, xq, idd, status=st)[0])
+    d = ulp_diff(h, orc.swiglu(g.astype(np.float32), u.astype(np.float32)))
+    assert d.max() <= 1 and np.count_nonzero(d) <= max(2, d.size // 1000)
+    assert to_host(st)[0] == 0
+    hq = to_dev(orc.quantize_q8_0(h))
+    with pytest.raises(RuntimeError, match="SHAPE"):
+        cq.cq_moe_gemv(fmt, to_dev(wd), E, H, F, hq, True, idd)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_moe_gemv_invalid_ids(cq, orc, swiglu):
     """Ids outside [0, E): their pairs read no weights and give exact zeros,
