@@ -946,10 +946,12 @@ __device__ __forceinline__ void stream_pass(StreamSmem& s, const StreamLane& L, 
     for (int r = 0; r < 4; ++r) bias[r] = kBias;
     ARegs av;
     WRegs w0, w1, w2;
-    issue_acts(s, xq, xrb, 0, av);
+    // only the token rows of the MT live tiles are staged: 16 rows per wave
+    const bool stager = MT == 4 || __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) < MT;
+    if (stager) issue_acts(s, xq, xrb, 0, av);
     issue_w(L.wrow, 0, L.g, w0);
     issue_w(L.wrow, nsb > 1 ? 1 : 0, L.g, w1);
-    store_acts(s.t[0], av);
+    if (stager) store_acts(s.t[0], av);
     __syncthreads();
 
     v4f acc[MT];
@@ -961,10 +963,10 @@ __device__ __forceinline__ void stream_pass(StreamSmem& s, const StreamLane& L, 
 #define CQ_STREAM_STEP(SB, CUR, FILL)                                             \
     {                                                                                   \
         const int sb_ = (SB);                                                           \
-        issue_acts(s, xq, xrb, sb_ + 1 < nsb ? sb_ + 1 : sb_, av);                      \
+        if (stager) issue_acts(s, xq, xrb, sb_ + 1 < nsb ? sb_ + 1 : sb_, av);          \
         issue_w(L.wrow, sb_ + 2 < nsb ? sb_ + 2 : sb_, L.g, FILL);                      \
         stream_sb<MT>(s.t[sb_ & 1], CUR, L, bias, acc);                                 \
-        store_acts(s.t[(sb_ + 1) & 1], av);                                             \
+        if (stager) store_acts(s.t[(sb_ + 1) & 1], av);                                 \
         __syncthreads();                                                                \
     }
     for (int sb = 0; sb < nsb; sb += 3) {
