@@ -1,7 +1,7 @@
 // gemv.hip -- decode GEMV over GGUF blocks (Q4_0, Q4_1, Q8_0, Q4_K, Q5_K,
-// Q6_K, Q1_0) for 1..8 Q8_0 activation rows; the same streaming kernel also
-// runs the fused gate/up + SwiGLU GEMV and the per-pair routed-expert GEMVs
-// of decode.
+// Q6_K, Q1_0, 2-bit ternary TQ2) for 1..8 Q8_0 activation rows; the same
+// streaming kernel also runs the fused gate/up + SwiGLU GEMV and the
+// per-pair routed-expert GEMVs of decode.
 //
 // Streaming kernel (HBM-bound; the weights are read exactly once):
 //  * A wave owns a contiguous range of rows.  Every row is loaded with
@@ -13,7 +13,7 @@
 //    re-slices its own blocks out of it.
 //  * Each lane owns fixed "columns" of K (one or two 32-value blocks; for
 //    Q4_K / Q5_K one 32-byte nibble chunk = two 32-value sub-blocks; for
-//    Q6_K a 64-value quarter super-block; for Q1_0 half a block) and keeps the
+//    Q6_K a 64-value quarter super-block; for Q1_0 and TQ2 half a block) and keeps the
 //    Q8_0 activation of its columns, for all batch rows, in registers.  The
 //    activations are copied once per workgroup into LDS with coalesced
 //    loads and unpacked from there.
