@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm2_kernel(
         const int kn = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
         load_weights<FMT>(wr, w, n, rb, n0, kn);
         load_x2(xr, xq, xrb, gm, kn);
-#pragma unroll 2
+#pragma unroll
         for (int b = 0; b < KB; ++b) mma_block2<FMT>(cur, b, wm, wn, l32, h, bias, acc);
         __syncthreads();
     }
