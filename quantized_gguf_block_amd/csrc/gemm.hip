@@ -354,7 +354,7 @@ __device__ __forceinline__ void mma_tile(Smem<Tile<WMW, WNW, MI, NI>::BM, 128>& 
         const int kn = ks + 1 < ksteps ? ks + 1 : ks;
         load_weights<FMT>(wr, w, n, rb, n0, kn);
         load_acts<BM>(xr, s, xq, xrb, kn);
-#pragma unroll 2
+#pragma unroll
         for (int b = 0; b < KB; ++b) {
             v4i A[NI], Bv[MI];
 #pragma unroll
