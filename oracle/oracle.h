@@ -85,7 +85,7 @@
  *     00, 01, 11 are 0, +1, -1 [alice-TQ]; code 10, which the encoding never
  *     produces, reads as 0 (the expansion table printed with it maps index 2
  *     to 0).  Value = d * code value.  The pages print no scale placement;
- *     one scale per 128 values is this build's reading.
+ *     one scale per 128 values (the Q1_0 block size) is the reading taken.
  *   - Greedy arg-max: the first index of the largest value (NaN-free rows;
  *     -0 and +0 compare equal).
  *   - Router: the top_k largest logits in descending order (equal logits:
