@@ -126,7 +126,8 @@ def test_golden_block_decodes(orc, blk):
         assert np.array_equal(orc.dequantize(t, raw, 256), exp)
         return
     raw = np.frombuffer(bytes.fromhex(blk["hex"]), np.uint8)
-    got = orc.dequantize(t, raw, 32)
+    assert raw.size == gs.BLOCK_BYTES[t]
+    got = orc.dequantize(t, raw, gs.BLOCK_ELEMS[t])
     if "expected" in blk:
         assert np.array_equal(got, np.array(blk["expected"], np.float64))
     else:
