@@ -352,14 +352,21 @@ template <int FMT, int B>
 __device__ __forceinline__ void chunk_dot_k45(const uint32_t* hdr, const uint32_t* qh, const uint32_t* q,
                                               int c, const Act<FMT>* a, float* acc) {
     const float d = h2f(hdr[0] & 0xFFFFu), dmin = h2f(hdr[0] >> 16);
-    // scale/min bytes of sub-blocks 2c, 2c+1 as byte pairs (low byte: 2c)
-    const uint32_t sh = 16u * (c & 1);
-    const uint32_t lowsrc = (c < 2) ? hdr[1] : hdr[3];     // S[0..3] or S[8..11]
-    const uint32_t A = lowsrc >> sh, Bm = hdr[2] >> sh, V = hdr[1] >> sh;
-    const uint32_t sc_lo = A & 0x3F3Fu, m_lo = Bm & 0x3F3Fu;                        // c < 2
-    const uint32_t sc_hi = (A & 0x0F0Fu) | ((V >> 2) & 0x3030u);                     // c >= 2
-    const uint32_t m_hi = ((A >> 4) & 0x0F0Fu) | ((Bm >> 2) & 0x3030u);
-    const uint32_t scp = (c < 2) ? sc_lo : sc_hi, mp = (c < 2) ? m_lo : m_hi;
+    // 6-bit scale / min of sub-blocks 2c, 2c+1 as byte pairs (low byte: 2c).
+    // With the 12 scale bytes S[0..11] in hdr[1..3], one byte permutation
+    // per pair gathers [S[2c], S[2c+1], 0, 0] (scales, c < 2), [S[4+2c],
+    // S[5+2c], 0, 0] (mins, c < 2), or [S[4+2c], S[5+2c], S[2c-4],
+    // S[2c-3]] (scales, c >= 2: low four bits, then the two top bits in
+    // bits 6-7 of the high bytes), [S[4+2c], S[5+2c], S[2c], S[2c+1]] (mins,
+    // c >= 2: the high four bits, then the top bits).  The selector, mask
+    // and shift depend on c only (loop-invariant for a lane).
+    const uint32_t sel = (c < 2) ? 0x0C0C0100u + 0x0202u * c : 0x01000504u + 0x02020202u * (c - 2);
+    const uint32_t msk = (c < 2) ? 0x3F3Fu : 0x0F0Fu;
+    const uint32_t msh = (c < 2) ? 0u : 4u;
+    const uint32_t ps = __builtin_amdgcn_perm(hdr[3], hdr[1], sel);
+    const uint32_t pm = __builtin_amdgcn_perm(hdr[3], hdr[2], sel);
+    const uint32_t scp = (ps & msk) | ((ps >> 18) & 0x3030u);
+    const uint32_t mp = ((pm >> msh) & msk) | ((pm >> 18) & 0x3030u);
     const float ds0 = d * static_cast<float>(scp & 0xFFu), ds1 = d * static_cast<float>((scp >> 8) & 0xFFu);
     const float dm0 = dmin * static_cast<float>(mp & 0xFFu), dm1 = dmin * static_cast<float>((mp >> 8) & 0xFFu);
     uint32_t lo[8], hi[8];
@@ -1405,7 +1412,6 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
                   const uint8_t* w2 = nullptr, MoeMap mm = {}, int npairs = 1) {
     auto kern = gemv_stream_kernel<FMT, B, SC, kRing, SW, MOE, KS>;
     static const int occ = kGW * resident_blocks_per_cu(kern, kWave * kGW);
-    int per_cu = occ < 8 ? occ : 8;
     // as many waves as fit, each with a whole number of P-row groups where
     // possible: gpw groups per wave, then the fewest waves that cover n,
     // rounded up to whole workgroups (spare waves get no rows).  Units are
@@ -1414,9 +1420,19 @@ int launch_stream(const uint8_t* w, int64_t n, int64_t rb, int ncols, const uint
     // (MOE: the wave slots are shared by the npairs matrices of the launch;
     // KS > 1: a row stream is KS waves)
     constexpr int NSTREAM = kGW / KS;
-    int64_t gmax = static_cast<int64_t>(device_cu_count()) * per_cu / npairs / KS;
-    if (gmax < NSTREAM) gmax = NSTREAM;
     const int64_t groups = (n + upg - 1) / upg;
+    auto streams_for = [&](int cap) {
+        const int per_cu = occ < cap ? occ : cap;
+        const int64_t g = static_cast<int64_t>(device_cu_count()) * per_cu / npairs / KS;
+        return g < NSTREAM ? static_cast<int64_t>(NSTREAM) : g;
+    };
+    // Wave slots per CU: up to 16 where they fit and every stream still gets
+    // at least 8 groups (long matrices: the Q4_K 128256 x 4096 LM head at
+    // batch 1 takes 45.5 against 47.4 us with 8), else up to 8 (shorter
+    // streams are slower with more waves: Q4_1 14336 x 4096 at batch 1 takes
+    // 8.6 us with 16 against 7.6 us with 8).
+    int64_t gmax = streams_for(16);
+    if ((groups + gmax - 1) / gmax < 8) gmax = streams_for(8);
     const int64_t gpw = (groups + gmax - 1) / gmax;
     const int64_t waves = (n + gpw * upg - 1) / (gpw * upg);   // row streams
     const int64_t wgs = (waves + NSTREAM - 1) / NSTREAM, nw = wgs * NSTREAM;
