@@ -242,6 +242,27 @@ def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
         assert_close_to_oracle(y, y_ref, s_ref, what="moe shape")
 
 
+@pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(70, 8, 2, 200, 2048), (300, 4, 2, 2000, 1536),
+                                                          (64, 300, 1, 100, 2048), (1, 32, 4, 1536, 2048)])
+def test_moe_gemm_whole_k_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
+    """The whole-k Q4_K kernel (k of 8 or 6 super-blocks): n not a multiple
+    of 16, several passes per expert (up to 150 tokens), two row groups per
+    wave with a ragged last workgroup (n = 2000 at k = 1536), more experts
+    than CUs with most of them empty, and a single token."""
+    w = gs.expert_weights(FMT, n_experts, n, k, cfg=740 + n_tokens, which=0)
+    ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=740 + n_tokens)
+    offs, pairs = orc.moe_group(ids, n_experts)
+    for x_per_pair in (False, True):
+        rows = n_tokens * top_k if x_per_pair else n_tokens
+        xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=741))
+        note("moe gemm whole k", n_tokens, n_experts, top_k, n, k, x_per_pair)
+        y = to_host(cq.cq_moe_gemm_grouped(FMT, to_dev(w), n_experts, n, k, to_dev(xq),
+                                           x_per_pair, to_dev(offs), to_dev(pairs), n_tokens,
+                                           top_k))
+        y_ref, s_ref = orc.moe_matmul(FMT, w, n_experts, n, k, xq, x_per_pair, ids)
+        assert_close_to_oracle(y, y_ref, s_ref, what="moe whole k")
+
+
 @pytest.mark.parametrize("fmt", [gs.Q4_0, gs.Q4_1, gs.Q8_0, gs.Q5_K, gs.Q6_K], ids=lambda f: gs.NAMES[f])
 @pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(40, 6, 2, 200, 512), (130, 3, 3, 70, 256)])
 def test_moe_gemm_other_formats(cq, orc, fmt, n_tokens, n_experts, top_k, n, k):
