@@ -366,7 +366,10 @@ def secondary(cq, gs, dev, stream):
     xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(4, k, cfg=c["cfg"])).to(dev))
     y = torch.empty((4, n), dtype=torch.float32, device=dev)
     for b in (1, 4):
-        us = burst_us(lambda i: cq.cq_gemv(gs.Q6_K, wl[i % len(wl)], n, k, xq, b, y=y), 40, stream)
+        # ~8 ms of warm-up launches first: the first milliseconds of a sustained
+        # burst after lighter work run slower (the batch-4 launches up to 30 %)
+        us = burst_us(lambda i: cq.cq_gemv(gs.Q6_K, wl[i % len(wl)], n, k, xq, b, y=y), 40, stream,
+                      warm=100)
         gbs = wl[0].numel() / us / 1e3
         out[f"q6_k_lm_head_{n}x{k}_b{b}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                                              "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}

@@ -1050,8 +1050,8 @@ __global__ __launch_bounds__(kStreamThreads, 3) void moe_stream_q4k_kernel(
 // with super-block s + RING of the group, or of the wave's next group.  The
 // arithmetic per super-block is that of stream_sb, in the same order, so
 // the results are those of moe_stream_q4k_kernel bit for bit.  (lfm2moe
-// shapes, 256 tokens, top 4 of 32, C harness: gate/up 32.1 against 34.0 us,
-// down 31.2 against 37.4 us.)
+// shapes, 256 tokens, top 4 of 32, C harness: gate/up 29.4 against 34.0 us,
+// down 28.7 against 37.4 us.)
 constexpr int kSxRow = 80;   // sx row stride (floats): four rows of one read on distinct banks
 
 template <int NSB, int T>
@@ -1063,13 +1063,14 @@ struct WholeSmem {           // NSB super-blocks of T token rows
     int yrow[T];
 };
 
-// Issue the loads of activation block pair item u of this thread (token row
-// r = item / (4 NSB), pair q = item % (4 NSB), blocks 2q and 2q+1); a tile
-// row past the pass's rows reads the pass's first token row.
+// Issue the loads of activation block pair item (token row r = item % T,
+// pair q = item / T: blocks 2q and 2q+1); a tile row past the pass's rows
+// reads the pass's first token row.  Consecutive threads take consecutive
+// token rows, so their dx and sum stores below fall on consecutive banks.
 template <int NSB, int T>
 __device__ __forceinline__ void issue_pair(const WholeSmem<NSB, T>& s, const uint8_t* __restrict__ xq,
                                            int64_t xrb, int item, ARegs& a) {
-    const int r = item / (4 * NSB), q = item % (4 * NSB);
+    const int r = item % T, q = item / T;
     const int gm = s.xrow[r] >= 0 ? s.xrow[r] : s.xrow[0];
     const uint32_t* p = reinterpret_cast<const uint32_t*>(
         xq + static_cast<int64_t>(gm < 0 ? 0 : gm) * xrb + static_cast<int64_t>(2 * q) * 34);
@@ -1081,7 +1082,7 @@ __device__ __forceinline__ void issue_pair(const WholeSmem<NSB, T>& s, const uin
 // Split a loaded pair into the tile: int8 values, dx and dx*sum(q).
 template <int NSB, int T>
 __device__ __forceinline__ void store_pair(WholeSmem<NSB, T>& s, int item, const ARegs& a) {
-    const int r = item / (4 * NSB), q = item % (4 * NSB);
+    const int r = item % T, q = item / T;
     const int sb = q >> 2;
     uint32_t v[17];
 #pragma unroll
