@@ -321,6 +321,26 @@ int cq_moe_gemm_grouped(int wt, const void* w_experts, int64_t n_experts, int64_
                         float* y, int64_t ldy, cq_stream_t stream);
 
 /*
+ * cq_moe_gemm_grouped2 -- two grouped products of the same gathered
+ * activation rows in one call (the routed FFN's gate and up projections,
+ * which read the same token rows): y_a as cq_moe_gemm_grouped gives for
+ * w_a_experts, y_b for w_b_experts, bit for bit.  Where one launch can serve
+ * both (Q4_K at k = 1536 or 2048), each expert's activation rows are split
+ * into the tile once for both matrices; otherwise the two products run one
+ * after the other.  (Cera README, "Supported models": lfm2moe's routed FFN,
+ * gate and up projections of each chosen expert followed by SwiGLU.)
+ *   w_a_experts, w_b_experts  device, the layout of cq_moe_gemm_grouped's
+ *                 w_experts (the same type and shape).
+ *   y_a, y_b      out device fp32 [n_tokens*top_k][ldy] each; the two may not
+ *                 overlap (CQ_ERR_INVALID_ARG).
+ *   Other arguments, results and errors as cq_moe_gemm_grouped.
+ */
+int cq_moe_gemm_grouped2(int wt, const void* w_a_experts, const void* w_b_experts,
+                         int64_t n_experts, int64_t n, int64_t k, const void* xq, int x_per_pair,
+                         const int32_t* offsets, const int32_t* pairs, int64_t n_tokens,
+                         int64_t top_k, float* y_a, float* y_b, int64_t ldy, cq_stream_t stream);
+
+/*
  * cq_moe_gemv -- routed experts at decode: the same product as cq_moe_gemm
  * for a few tokens, taken straight from the routing table, one GEMV per
  * token-expert pair p = t*top_k + s (no grouping call):

@@ -27,7 +27,8 @@ MOE_NOALLOC_MAX_BYTES = 16 << 20
 EXPORTS = [
     "cq_abi_version", "cq_status_string", "cq_block_elems", "cq_block_bytes", "cq_row_bytes",
     "cq_quantize_q8_0", "cq_gemv", "cq_gemv_swiglu", "cq_gemm", "cq_moe_workspace_bytes",
-    "cq_moe_gemm", "cq_moe_gemm_noalloc", "cq_moe_group", "cq_moe_gemm_grouped", "cq_swiglu_quantize_q8_0",
+    "cq_moe_gemm", "cq_moe_gemm_noalloc", "cq_moe_group", "cq_moe_gemm_grouped",
+    "cq_moe_gemm_grouped2", "cq_swiglu_quantize_q8_0",
     "cq_moe_combine", "cq_moe_gemv", "cq_moe_gemv_swiglu", "cq_argmax_workspace_bytes",
     "cq_argmax", "cq_topk_softmax",
 ]
@@ -83,6 +84,7 @@ def signatures():
         "cq_gemm": (I, [I, P, I64, I64, P, I64, P, I64, P]),
         "cq_moe_group": (I, [P, I64, I64, I64, P, P, P, P]),
         "cq_moe_gemm_grouped": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P]),
+        "cq_moe_gemm_grouped2": (I, [I, P, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, I64, P]),
         "cq_moe_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64, I64, I]),
         "cq_moe_gemm": (I, [I, P, I64, I64, I64, P, I, P, P, I64, I64, P, I64, P,
                             ctypes.c_size_t, P]),
@@ -220,6 +222,26 @@ def cq_moe_gemm_grouped(wt, w_experts, n_experts, n, k, xq, x_per_pair, offsets,
         wt, _ptr(w_experts), n_experts, n, k, _ptr(xq), int(bool(x_per_pair)), _ptr(offsets),
         _ptr(pairs), n_tokens, top_k, _ptr(y), ldy, _stream(stream)))
     return y
+
+
+def cq_moe_gemm_grouped2(wt, w_a_experts, w_b_experts, n_experts, n, k, xq, x_per_pair, offsets,
+                         pairs, n_tokens, top_k, y_a=None, y_b=None, ldy=None, stream=None):
+    """Two grouped expert projections of the same activation rows (gate and
+    up) -> (y_a, y_b), each fp32 [n_tokens*top_k][n], row = pair id."""
+    import torch
+    _dev_tensor(w_a_experts, "w_a_experts", torch.uint8)
+    _dev_tensor(w_b_experts, "w_b_experts", torch.uint8)
+    _dev_tensor(xq, "xq", torch.uint8)
+    dev = w_a_experts.device
+    if y_a is None:
+        y_a = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=dev)
+    if y_b is None:
+        y_b = torch.empty((n_tokens * top_k, n), dtype=torch.float32, device=dev)
+    ldy = ldy if ldy is not None else (y_a.stride(0) if y_a.dim() == 2 else n)
+    _check("cq_moe_gemm_grouped2", load().cq_moe_gemm_grouped2(
+        wt, _ptr(w_a_experts), _ptr(w_b_experts), n_experts, n, k, _ptr(xq), int(bool(x_per_pair)),
+        _ptr(offsets), _ptr(pairs), n_tokens, top_k, _ptr(y_a), _ptr(y_b), ldy, _stream(stream)))
+    return y_a, y_b
 
 
 def cq_moe_workspace_bytes(n_tokens, top_k, n_experts, n, flags):

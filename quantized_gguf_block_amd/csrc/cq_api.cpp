@@ -282,6 +282,30 @@ int cq_moe_gemm_grouped(int wt, const void* w_experts, int64_t n_experts, int64_
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
+int cq_moe_gemm_grouped2(int wt, const void* w_a_experts, const void* w_b_experts,
+                         int64_t n_experts, int64_t n, int64_t k, const void* xq, int x_per_pair,
+                         const int32_t* offsets, const int32_t* pairs, int64_t n_tokens,
+                         int64_t top_k, float* y_a, float* y_b, int64_t ldy, cq_stream_t stream) {
+    if (x_per_pair != 0 && x_per_pair != 1) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_moe_gemm(wt, w_a_experts, n_experts, n, k, n_tokens, top_k, ldy)) return rc;
+    if (int rc = check_weights(wt, w_b_experts, n, k)) return rc;
+    if (n == 0 || n_tokens == 0) return CQ_OK;
+    if (!xq || !offsets || !pairs || !y_a || !y_b) return CQ_ERR_INVALID_ARG;
+    if (!aligned(xq, 2) || !aligned(offsets, 4) || !aligned(pairs, 4) || !aligned(y_a, 4) ||
+        !aligned(y_b, 4))
+        return CQ_ERR_ALIGNMENT;
+    // the two outputs' extents (rows of ldy floats, the last one n long) may not overlap
+    using u128 = unsigned __int128;
+    const u128 a0 = reinterpret_cast<uintptr_t>(y_a), b0 = reinterpret_cast<uintptr_t>(y_b);
+    const u128 span = (static_cast<u128>(n_tokens * top_k - 1) * static_cast<uint64_t>(ldy) +
+                       static_cast<uint64_t>(n)) * 4;
+    if (a0 < b0 + span && b0 < a0 + span) return CQ_ERR_INVALID_ARG;
+    if (int rc = check_device()) return rc;
+    return status_of(launch_moe_gemm2(wt, w_a_experts, w_b_experts, n_experts, n, k, xq, x_per_pair,
+                                      offsets, pairs, n_tokens, top_k, y_a, y_b, ldy,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
 static bool moe_flags_ok(int flags) {
     return (flags & ~(CQ_MOE_X_PER_PAIR | CQ_MOE_OUT_COMBINE)) == 0;
 }

@@ -38,6 +38,10 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
                     const void* xq, int x_per_pair, const int32_t* offsets,
                     const int32_t* pairs, int64_t n_tokens, int64_t top_k, float* y,
                     int64_t ldy, hipStream_t stream);
+int launch_moe_gemm2(int wt, const void* w, const void* w2, int64_t n_experts, int64_t n, int64_t k,
+                     const void* xq, int x_per_pair, const int32_t* offsets, const int32_t* pairs,
+                     int64_t n_tokens, int64_t top_k, float* y, float* y2, int64_t ldy,
+                     hipStream_t stream);
 int launch_moe_combine(const float* d, const float* route_w, int64_t n_tokens, int64_t top_k,
                        int64_t n, float* y, int64_t ldy, const int32_t* ids, int64_t n_experts,
                        hipStream_t stream);

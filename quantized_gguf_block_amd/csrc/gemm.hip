@@ -1202,19 +1202,39 @@ __device__ __forceinline__ void whole_sb(const int8_t* ax, const float* pdx, con
 // group 0 are in flight).  Register set s % D holds super-block s; after it
 // is used it is refilled with super-block s + D of the group, or s + D - NSB
 // of the next one.
+// Group grp of a workgroup's list: the first gmat groups are row groups of
+// w (output y), the next gmat those of w2 (output y2), when w2 is given.
+struct GroupRef {
+    const uint8_t* w;
+    float* y;
+    int64_t rg;   // row group within the matrix
+};
+
+__device__ __forceinline__ GroupRef group_ref(const uint8_t* w, const uint8_t* w2, float* y, float* y2,
+                                              int64_t gmat, int64_t grp) {
+    const bool second = w2 != nullptr && grp >= gmat;
+    return GroupRef{second ? w2 : w, second ? y2 : y, second ? grp - gmat : grp};
+}
+
 template <int MT, int NSB, int D, int T>
 __device__ __forceinline__ void whole_groups(const WholeSmem<NSB, T>& s, WRegs (&wr)[D],
-                                             const uint8_t* __restrict__ w, int64_t n, int64_t rb, int e,
+                                             const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2,
+                                             int64_t gmat, int64_t n, int64_t rb, int e,
                                              int64_t grp0, int nw, int rpl, int lane, int rows,
-                                             float* __restrict__ y, int64_t ldy) {
+                                             float* __restrict__ y, float* __restrict__ y2, int64_t ldy) {
     static_assert(NSB % D == 0, "whole sets per group");
     v4i bias;
 #pragma unroll
     for (int r = 0; r < 4; ++r) bias[r] = kBias;
     for (int i = 0; i < rpl; ++i) {
-        const StreamLane L = group_lane(w, n, rb, e, grp0 + static_cast<int64_t>(i) * nw, lane);
+        const GroupRef G = group_ref(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i) * nw);
+        const StreamLane L = group_lane(G.w, n, rb, e, G.rg, lane);
         // past the last group the refills repeat this group's first sets
-        const StreamLane Ln = i + 1 < rpl ? group_lane(w, n, rb, e, grp0 + static_cast<int64_t>(i + 1) * nw, lane) : L;
+        StreamLane Ln = L;
+        if (i + 1 < rpl) {
+            const GroupRef Gn = group_ref(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i + 1) * nw);
+            Ln = group_lane(Gn.w, n, rb, e, Gn.rg, lane);
+        }
         v4f acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -1234,15 +1254,16 @@ __device__ __forceinline__ void whole_groups(const WholeSmem<NSB, T>& s, WRegs (
             else issue_w(Ln.wrow, sb + D - NSB, Ln.g, wr[sb % D]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        store_group<MT>(s, L, rows, acc, y, ldy);
+        store_group<MT>(s, L, rows, acc, G.y, ldy);
     }
 }
 
 template <int NW, int NSB, int MTMAX, int RING>
 __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
-        const uint8_t* __restrict__ w, int64_t n, int64_t rb, int rpl,
-        const uint8_t* __restrict__ xq, int x_per_pair, const int32_t* __restrict__ offsets,
-        const int32_t* __restrict__ pairs, int np, int top_k, float* __restrict__ y, int64_t ldy) {
+        const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2, int64_t gmat, int64_t n,
+        int64_t rb, int rpl, const uint8_t* __restrict__ xq, int x_per_pair,
+        const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs, int np, int top_k,
+        float* __restrict__ y, float* __restrict__ y2, int64_t ldy) {
     constexpr int T = 16 * MTMAX;
     constexpr int NT = NW * 64;
     constexpr int UMAX = T * 4 * NSB / NT;   // block pairs per thread
@@ -1285,7 +1306,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
         constexpr int D = RING;
         WRegs wr[D];
         {
-            const StreamLane L0 = group_lane(w, n, rb, e, grp0, lane);
+            const GroupRef G0 = group_ref(w, w2, y, y2, gmat, grp0);
+            const StreamLane L0 = group_lane(G0.w, n, rb, e, G0.rg, lane);
 #pragma unroll
             for (int sb = 0; sb < D; ++sb) issue_w(L0.wrow, sb, L0.g, wr[sb]);
         }
@@ -1296,11 +1318,11 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
         }
         __syncthreads();
         switch (mt) {
-            case 1: whole_groups<1, NSB, D, T>(s, wr, w, n, rb, e, grp0, NW, rpl, lane, rows, y, ldy); break;
-            case 2: whole_groups<2, NSB, D, T>(s, wr, w, n, rb, e, grp0, NW, rpl, lane, rows, y, ldy); break;
-            case 3: whole_groups<3, NSB, D, T>(s, wr, w, n, rb, e, grp0, NW, rpl, lane, rows, y, ldy); break;
+            case 1: whole_groups<1, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
+            case 2: whole_groups<2, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
+            case 3: whole_groups<3, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
             default:
-                if constexpr (MTMAX >= 4) whole_groups<4, NSB, D, T>(s, wr, w, n, rb, e, grp0, NW, rpl, lane, rows, y, ldy);
+                if constexpr (MTMAX >= 4) whole_groups<4, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy);
                 break;
         }
     }
@@ -1344,6 +1366,35 @@ int launch_gemm(int wt, const void* w, int64_t n, int64_t k, const void* xq, int
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+// The whole-k Q4_K kernel for k of 8 or 6 super-blocks: one workgroup per
+// CU, the experts' row groups (of w, then of w2 when given) spread over the
+// CUs (gpw groups per workgroup, rpl per wave).  Returns false (nothing
+// launched) for other k.
+static bool launch_moe_whole(const uint8_t* wp, const uint8_t* wp2, int64_t n_experts, int64_t n,
+                             int64_t k, int64_t rb, const uint8_t* xp, int x_per_pair,
+                             const int32_t* offsets, const int32_t* pairs, int npi, int tk, float* y,
+                             float* y2, int64_t ldy, hipStream_t stream) {
+    const int64_t nsb = k / 256;
+    if (nsb != 8 && nsb != 6) return false;
+    const int nw = nsb == 8 ? 12 : 8;
+    const int64_t gmat = (n + 15) / 16;
+    const int64_t groups = wp2 ? 2 * gmat : gmat;
+    int64_t wpe = device_cu_count() / n_experts;
+    wpe = wpe < 1 ? 1 : (wpe > groups ? groups : wpe);
+    const int64_t gpw = (groups + wpe - 1) / wpe;
+    const int64_t rpl = (gpw + nw - 1) / nw;
+    const int64_t wgs = (groups + nw * rpl - 1) / (nw * rpl);
+    const dim3 gw(static_cast<unsigned>(wgs), static_cast<unsigned>(n_experts));
+    const int rp = static_cast<int>(rpl);
+    if (nsb == 8)
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<12, 8, 3, 2>), gw, dim3(12 * 64), 0, stream, wp, wp2, gmat, n,
+                           rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+    else
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<8, 6, 4, 3>), gw, dim3(8 * 64), 0, stream, wp, wp2, gmat, n,
+                           rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+    return true;
+}
+
 int moe_shape_ok(int wt, int64_t n, int64_t k) {
     return (k % 256 == 0 && q6k_range_ok(wt, n, k)) ? 0 : -3;
 }
@@ -1371,26 +1422,9 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
         case T_Q5_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q5_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q6_K: hipLaunchKernelGGL(moe_gemm_kernel<T_Q6_K>, g, b, 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy); break;
         case T_Q4_K: {
-            const int64_t nsb = k / 256;
-            if (nsb == 8 || nsb == 6) {
-                // whole-k tile: one workgroup per CU, the experts' row groups
-                // spread over the CUs (gpw per workgroup, rpl per wave)
-                const int nw = nsb == 8 ? 12 : 8;
-                const int64_t groups = (n + 15) / 16;
-                int64_t wpe = device_cu_count() / n_experts;
-                wpe = wpe < 1 ? 1 : (wpe > groups ? groups : wpe);
-                const int64_t gpw = (groups + wpe - 1) / wpe;
-                const int64_t rpl = (gpw + nw - 1) / nw;
-                const int64_t wgs = (groups + nw * rpl - 1) / (nw * rpl);
-                if (rpl > 0x7FFFFFFF) return -3;
-                const dim3 gw(static_cast<unsigned>(wgs), static_cast<unsigned>(n_experts));
-                const int rp = static_cast<int>(rpl);
-                if (nsb == 8)
-                    hipLaunchKernelGGL((moe_whole_q4k_kernel<12, 8, 3, 2>), gw, dim3(12 * 64), 0, stream, wp, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);
-                else
-                    hipLaunchKernelGGL((moe_whole_q4k_kernel<8, 6, 4, 3>), gw, dim3(8 * 64), 0, stream, wp, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);
+            if (launch_moe_whole(wp, nullptr, n_experts, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk,
+                                 y, nullptr, ldy, stream))
                 break;
-            }
             const dim3 gs(static_cast<unsigned>((n + kSbRows - 1) / kSbRows), static_cast<unsigned>(n_experts));
             hipLaunchKernelGGL(moe_stream_q4k_kernel, gs, dim3(kStreamThreads), 0, stream, wp, n, k, rb, xp, x_per_pair, offsets, pairs, npi, tk, y, ldy);
             break;
@@ -1398,6 +1432,29 @@ int launch_moe_gemm(int wt, const void* w, int64_t n_experts, int64_t n, int64_t
         default: return -2;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Two grouped products over the same activation rows (w -> y, w2 -> y2):
+// one launch over both matrices where the whole-k kernel applies (one
+// split of each expert's activation rows serves both), else two launches.
+int launch_moe_gemm2(int wt, const void* w, const void* w2, int64_t n_experts, int64_t n, int64_t k,
+                     const void* xq, int x_per_pair, const int32_t* offsets, const int32_t* pairs,
+                     int64_t n_tokens, int64_t top_k, float* y, float* y2, int64_t ldy,
+                     hipStream_t stream) {
+    if (wt == T_Q4_K) {
+        const int64_t rb = k / 256 * 144;
+        const int64_t np = n_tokens * top_k;
+        if (np > 0x7FFFFFFF) return -3;
+        if (launch_moe_whole(static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(w2), n_experts, n,
+                             k, rb, static_cast<const uint8_t*>(xq), x_per_pair, offsets, pairs,
+                             static_cast<int>(np), static_cast<int>(top_k), y, y2, ldy, stream))
+            return hipGetLastError() == hipSuccess ? 0 : -6;
+    }
+    if (int rc = launch_moe_gemm(wt, w, n_experts, n, k, xq, x_per_pair, offsets, pairs, n_tokens, top_k,
+                                 y, ldy, stream))
+        return rc;
+    return launch_moe_gemm(wt, w2, n_experts, n, k, xq, x_per_pair, offsets, pairs, n_tokens, top_k, y2,
+                           ldy, stream);
 }
 
 }  // namespace cq

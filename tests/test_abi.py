@@ -191,6 +191,24 @@ def test_moe_validation(lib):
              None) == UNSUPPORTED
     assert m(14, P(FAKE), 2, 1 << 20, 2560, P(FAKE), 0, P(FAKE), P(FAKE), 4, 2, P(FAKE),
              1 << 20, None) == SHAPE                                         # Q6_K expert >= 2 GiB
+    m2 = lib.cq_moe_gemm_grouped2
+    YA, YB = P(FAKE), P(FAKE + 4 * 64 * 15)      # 16 pair rows of ldy 64: YB = YA's last row
+    assert m2(12, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YA, YB, 64,
+              None) == INVALID                                           # y_b starts in y_a's last row
+    assert m2(12, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YB, YA, 64,
+              None) == INVALID                                           # (either order)
+    assert m2(12, P(FAKE), None, 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YA,
+              P(FAKE + (1 << 20)), 64, None) == INVALID                    # no second matrix
+    assert m2(12, P(FAKE), P(FAKE + 8), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YA,
+              P(FAKE + (1 << 20)), 64, None) == ALIGN                      # second matrix 8-aligned
+    assert m2(12, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YA, None,
+              64, None) == INVALID                                       # no second output
+    assert m2(12, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 3, P(FAKE), P(FAKE), 4, 4, YA,
+              P(FAKE + (1 << 20)), 64, None) == INVALID                    # x_per_pair
+    assert m2(7, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 4, 4, YA,
+              P(FAKE + (1 << 20)), 64, None) == UNSUPPORTED
+    assert m2(12, P(FAKE), P(FAKE), 32, 64, 256, P(FAKE), 0, P(FAKE), P(FAKE), 0, 4, YA, YA, 64,
+              None) == OK                                                # no tokens: nothing written
     s = lib.cq_swiglu_quantize_q8_0
     assert s(P(FAKE), P(FAKE), 2, 48, None, P(FAKE), None) == SHAPE
     assert s(P(FAKE), P(FAKE + 4), 2, 64, None, P(FAKE), None) == ALIGN

@@ -67,6 +67,53 @@ def test_moe_gate_up(cq):
         print(f"{name}: max |err|/S = {r:.3e}")
 
 
+def test_moe_gate_up_one_call(cq):
+    """Gate and up in one call (one split of each expert's rows for both
+    matrices): each output within 2e-5 * S of the oracle and bitwise equal to
+    the separate grouped call."""
+    wg, wu, wd, x, ids, rw = inputs()
+    ref = oracle_pipeline()
+    offs, pairs = to_dev(ref["offs"]), to_dev(ref["pairs"])
+    xq = to_dev(ref["xq"])
+    note("moe gate+up one call")
+    wgd, wud = to_dev(wg), to_dev(wu)
+    ya, yb = cq.cq_moe_gemm_grouped2(FMT, wgd, wud, E, F, H, xq, False, offs, pairs, T, K)
+    ya, yb = to_host(ya), to_host(yb)
+    assert_close_to_oracle(ya, ref["g"], ref["sg"], what="gate (one call)")
+    assert_close_to_oracle(yb, ref["u"], ref["su"], what="up (one call)")
+    assert np.array_equal(ya, to_host(cq.cq_moe_gemm_grouped(FMT, wgd, E, F, H, xq, False, offs,
+                                                             pairs, T, K)))
+    assert np.array_equal(yb, to_host(cq.cq_moe_gemm_grouped(FMT, wud, E, F, H, xq, False, offs,
+                                                             pairs, T, K)))
+
+
+@pytest.mark.parametrize("fmt,n_tokens,n_experts,top_k,n,k,x_per_pair",
+                         [(gs.Q4_K, 70, 8, 2, 200, 1536, True), (gs.Q4_K, 300, 4, 2, 2000, 2048, False),
+                          (gs.Q4_K, 40, 6, 2, 200, 512, False), (gs.Q8_0, 40, 6, 2, 200, 512, True)],
+                         ids=["q4_k-k1536", "q4_k-k2048-ragged", "q4_k-k512", "q8_0"])
+def test_moe_gemm_grouped2_shapes(cq, orc, fmt, n_tokens, n_experts, top_k, n, k, x_per_pair):
+    """Two projections in one call: one launch for Q4_K at k = 1536 / 2048
+    (ragged n, several passes per expert, two row groups per wave), two
+    launches otherwise; both outputs within tolerance of the oracle and
+    bitwise equal to separate calls."""
+    wa = gs.expert_weights(fmt, n_experts, n, k, cfg=750 + n_tokens, which=0)
+    wb = gs.expert_weights(fmt, n_experts, n, k, cfg=750 + n_tokens, which=1)
+    ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=750 + n_tokens)
+    offs, pairs = orc.moe_group(ids, n_experts)
+    rows = n_tokens * top_k if x_per_pair else n_tokens
+    xq = orc.quantize_q8_0(gs.activations(rows, k, cfg=751))
+    note("moe gemm grouped2", gs.NAMES[fmt], n_tokens, n_experts, top_k, n, k, x_per_pair)
+    args = (n_experts, n, k, to_dev(xq), x_per_pair, to_dev(offs), to_dev(pairs), n_tokens, top_k)
+    wad, wbd = to_dev(wa), to_dev(wb)
+    ya, yb = cq.cq_moe_gemm_grouped2(fmt, wad, wbd, *args)
+    ya, yb = to_host(ya), to_host(yb)
+    for y, w, name in ((ya, wa, "first"), (yb, wb, "second")):
+        y_ref, s_ref = orc.moe_matmul(fmt, w, n_experts, n, k, xq, x_per_pair, ids)
+        assert_close_to_oracle(y, y_ref, s_ref, what=f"grouped2 {name}")
+    assert np.array_equal(ya, to_host(cq.cq_moe_gemm_grouped(fmt, wad, *args)))
+    assert np.array_equal(yb, to_host(cq.cq_moe_gemm_grouped(fmt, wbd, *args)))
+
+
 def test_moe_down(cq):
     wg, wu, wd, x, ids, rw = inputs()
     ref = oracle_pipeline()
