@@ -1210,13 +1210,14 @@ struct GroupRef {
     int64_t rg;   // row group within the matrix
 };
 
+template <bool PAIR>
 __device__ __forceinline__ GroupRef group_ref(const uint8_t* w, const uint8_t* w2, float* y, float* y2,
                                               int64_t gmat, int64_t grp) {
-    const bool second = w2 != nullptr && grp >= gmat;
+    const bool second = PAIR && grp >= gmat;
     return GroupRef{second ? w2 : w, second ? y2 : y, second ? grp - gmat : grp};
 }
 
-template <int MT, int NSB, int D, int T>
+template <int MT, int NSB, int D, int T, bool PAIR>
 __device__ __forceinline__ void whole_groups(const WholeSmem<NSB, T>& s, WRegs (&wr)[D],
                                              const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2,
                                              int64_t gmat, int64_t n, int64_t rb, int e,
@@ -1227,12 +1228,12 @@ __device__ __forceinline__ void whole_groups(const WholeSmem<NSB, T>& s, WRegs (
 #pragma unroll
     for (int r = 0; r < 4; ++r) bias[r] = kBias;
     for (int i = 0; i < rpl; ++i) {
-        const GroupRef G = group_ref(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i) * nw);
+        const GroupRef G = group_ref<PAIR>(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i) * nw);
         const StreamLane L = group_lane(G.w, n, rb, e, G.rg, lane);
         // past the last group the refills repeat this group's first sets
         StreamLane Ln = L;
         if (i + 1 < rpl) {
-            const GroupRef Gn = group_ref(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i + 1) * nw);
+            const GroupRef Gn = group_ref<PAIR>(w, w2, y, y2, gmat, grp0 + static_cast<int64_t>(i + 1) * nw);
             Ln = group_lane(Gn.w, n, rb, e, Gn.rg, lane);
         }
         v4f acc[MT];
@@ -1258,7 +1259,7 @@ __device__ __forceinline__ void whole_groups(const WholeSmem<NSB, T>& s, WRegs (
     }
 }
 
-template <int NW, int NSB, int MTMAX, int RING>
+template <int NW, int NSB, int MTMAX, int RING, bool PAIR>
 __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
         const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2, int64_t gmat, int64_t n,
         int64_t rb, int rpl, const uint8_t* __restrict__ xq, int x_per_pair,
@@ -1306,7 +1307,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
         constexpr int D = RING;
         WRegs wr[D];
         {
-            const GroupRef G0 = group_ref(w, w2, y, y2, gmat, grp0);
+            const GroupRef G0 = group_ref<PAIR>(w, w2, y, y2, gmat, grp0);
             const StreamLane L0 = group_lane(G0.w, n, rb, e, G0.rg, lane);
 #pragma unroll
             for (int sb = 0; sb < D; ++sb) issue_w(L0.wrow, sb, L0.g, wr[sb]);
@@ -1318,11 +1319,11 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void moe_whole_q4k_kernel(
         }
         __syncthreads();
         switch (mt) {
-            case 1: whole_groups<1, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
-            case 2: whole_groups<2, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
-            case 3: whole_groups<3, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
+            case 1: whole_groups<1, NSB, D, T, PAIR>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
+            case 2: whole_groups<2, NSB, D, T, PAIR>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
+            case 3: whole_groups<3, NSB, D, T, PAIR>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy); break;
             default:
-                if constexpr (MTMAX >= 4) whole_groups<4, NSB, D, T>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy);
+                if constexpr (MTMAX >= 4) whole_groups<4, NSB, D, T, PAIR>(s, wr, w, w2, gmat, n, rb, e, grp0, NW, rpl, lane, rows, y, y2, ldy);
                 break;
         }
     }
@@ -1386,12 +1387,20 @@ static bool launch_moe_whole(const uint8_t* wp, const uint8_t* wp2, int64_t n_ex
     const int64_t wgs = (groups + nw * rpl - 1) / (nw * rpl);
     const dim3 gw(static_cast<unsigned>(wgs), static_cast<unsigned>(n_experts));
     const int rp = static_cast<int>(rpl);
-    if (nsb == 8)
-        hipLaunchKernelGGL((moe_whole_q4k_kernel<12, 8, 3, 2>), gw, dim3(12 * 64), 0, stream, wp, wp2, gmat, n,
-                           rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+    // (the two-matrix launch is its own instantiation, so a kernel trace
+    // tells it from the single-matrix one)
+    if (nsb == 8 && wp2)
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<12, 8, 3, 2, true>), gw, dim3(12 * 64), 0, stream, wp, wp2,
+                           gmat, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+    else if (nsb == 8)
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<12, 8, 3, 2, false>), gw, dim3(12 * 64), 0, stream, wp, wp2,
+                           gmat, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+    else if (wp2)
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<8, 6, 4, 3, true>), gw, dim3(8 * 64), 0, stream, wp, wp2,
+                           gmat, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
     else
-        hipLaunchKernelGGL((moe_whole_q4k_kernel<8, 6, 4, 3>), gw, dim3(8 * 64), 0, stream, wp, wp2, gmat, n,
-                           rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
+        hipLaunchKernelGGL((moe_whole_q4k_kernel<8, 6, 4, 3, false>), gw, dim3(8 * 64), 0, stream, wp, wp2,
+                           gmat, n, rb, rp, xp, x_per_pair, offsets, pairs, npi, tk, y, y2, ldy);
     return true;
 }
 
