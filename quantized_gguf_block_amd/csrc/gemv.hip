@@ -96,9 +96,10 @@ template <int FMT> struct Act {
 };
 template <> struct Act<T_Q4_K> {
     uint32_t qa[8], qb[8];  // the two 32-value blocks under one nibble chunk
-    float dxa, dxb;
-    float ndxa, ndxb;       // -12582912 * dx
+    float dxa, dxb;         // (Q4_K: dxb / 16, see chunk_dot_k45)
+    float ndxa, ndxb;       // -12582912 * dx (of the dx held)
     float sa, sb;           // dx * sum(q) of each block
+    int startb;             // Q4_K: kBias + 128 * sum(qb), the high-nibble chain's start
 };
 template <> struct Act<T_Q5_K> : Act<T_Q4_K> {};
 
@@ -237,6 +238,10 @@ __device__ __forceinline__ void load_act_rs(__amdgpu_buffer_rsrc_t rs, int xo, i
         load_q8_rs(rs, xo + (2 * col + 1) * 34, a.qb, &a.dxb, &sb);
         a.sa = a.dxa * static_cast<float>(sa);
         a.sb = a.dxb * static_cast<float>(sb);
+        if constexpr (FMT == T_Q4_K) {
+            a.startb = kBias + 128 * sb;
+            a.dxb *= 0.0625f;
+        }
         a.ndxa = -kBiasF * a.dxa;
         a.ndxb = -kBiasF * a.dxb;
     } else if constexpr (FMT == T_Q1_0) {
@@ -369,11 +374,17 @@ __device__ __forceinline__ void chunk_dot_k45(const uint32_t* hdr, const uint32_
     const uint32_t mp = ((pm >> msh) & msk) | ((pm >> 18) & 0x3030u);
     const float ds0 = d * static_cast<float>(scp & 0xFFu), ds1 = d * static_cast<float>((scp >> 8) & 0xFFu);
     const float dm0 = dmin * static_cast<float>(mp & 0xFFu), dm1 = dmin * static_cast<float>((mp >> 8) & 0xFFu);
+    // Q4_K: the high nibbles h stay in place with the top bit flipped, a
+    // byte (q & 0xF0) ^ 0x80 that reads as the signed value 16h - 128 (one
+    // three-input bitwise op instead of a shift and a mask); its chain starts
+    // at kBias + 128 * sum(qb), so it ends at kBias + 16 * sum(h * qb), and dxb
+    // is held divided by 16 (exact): the same s * dx as the plain nibbles give.
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         lo[t] = q[t] & 0x0F0F0F0Fu;
-        hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+        if constexpr (FMT == T_Q4_K) hi[t] = (q[t] & 0xF0F0F0F0u) ^ 0x80808080u;
+        else hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
         if constexpr (FMT == T_Q5_K) {
             // bits 2c and 2c+1 of each qh byte become bit 4 of the low and
             // high values
@@ -386,7 +397,9 @@ __device__ __forceinline__ void chunk_dot_k45(const uint32_t* hdr, const uint32_
 #pragma unroll
     for (int j = 0; j < B; ++j) {
         const int sa = dot8<B == 1, true>(lo, a[j].qa, bias);
-        const int sb = dot8<B == 1, true>(hi, a[j].qb, bias);
+        int sb;
+        if constexpr (FMT == T_Q4_K) sb = dot8<B == 1, false>(hi, a[j].qb, a[j].startb);
+        else sb = dot8<B == 1, true>(hi, a[j].qb, bias);
         const float xa = fmaf(__int_as_float(sa), a[j].dxa, a[j].ndxa);
         const float xb = fmaf(__int_as_float(sb), a[j].dxb, a[j].ndxb);
         float v = fmaf(xa, ds0, acc[j]);
@@ -571,15 +584,15 @@ __device__ __forceinline__ void column_dot(const uint8_t* lds, int off, const Ac
         const float ds0 = d * static_cast<float>(sc0), dm0 = dmin * static_cast<float>(m0);
         const float ds1 = d * static_cast<float>(sc1), dm1 = dmin * static_cast<float>(m1);
         const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        uint32_t lo[8], hi[8];
+        uint32_t lo[8], hi[8];   // (high nibbles as in chunk_dot_k45)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             lo[t] = q[t] & 0x0F0F0F0Fu;
-            hi[t] = (q[t] >> 4) & 0x0F0F0F0Fu;
+            hi[t] = (q[t] & 0xF0F0F0F0u) ^ 0x80808080u;
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int sa = kBias, sb = kBias, sa1 = 0, sb1 = 0;  // four chains at batch 1
+            int sa = kBias, sb = a[j].startb, sa1 = 0, sb1 = 0;  // four chains at batch 1
             int& sa2 = B == 1 ? sa1 : sa;
             int& sb2 = B == 1 ? sb1 : sb;
 #pragma unroll
@@ -1147,8 +1160,8 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                     int sum = 0;
 #pragma unroll
                     for (int u = 0; u < 8; ++u) sum = sdot4(q[u], 0x01010101u, sum);
-                    xau[gi] = (FMT == T_Q4_0 || FMT == T_Q1_0) ? __int_as_float(sum)
-                                                               : dx * static_cast<float>(sum);
+                    xau[gi] = (FMT == T_Q4_0 || FMT == T_Q1_0 || FMT == T_Q4_K)
+                                  ? __int_as_float(sum) : dx * static_cast<float>(sum);
                 }
             }
         }
@@ -1203,8 +1216,16 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
                 a.qb[4] = b1.x; a.qb[5] = b1.y; a.qb[6] = b1.z; a.qb[7] = b1.w;
                 a.dxa = xda[ga];
                 a.dxb = xda[gb];
-                a.sa = xau[ga];
-                a.sb = xau[gb];
+                if constexpr (FMT == T_Q4_K) {   // (the table holds the integer sums)
+                    const int suma = __float_as_int(xau[ga]), sumb = __float_as_int(xau[gb]);
+                    a.sa = a.dxa * static_cast<float>(suma);
+                    a.sb = a.dxb * static_cast<float>(sumb);
+                    a.startb = kBias + 128 * sumb;
+                    a.dxb *= 0.0625f;
+                } else {
+                    a.sa = xau[ga];
+                    a.sb = xau[gb];
+                }
                 a.ndxa = -kBiasF * a.dxa;
                 a.ndxb = -kBiasF * a.dxb;
             } else {
