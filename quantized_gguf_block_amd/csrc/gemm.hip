@@ -1049,9 +1049,12 @@ __global__ __launch_bounds__(kStreamThreads, 3) void moe_stream_q4k_kernel(
 // super-block each: set s % RING is refilled, as soon as it has been used,
 // with super-block s + RING of the group, or of the wave's next group.  The
 // arithmetic per super-block is that of stream_sb, in the same order, so
-// the results are those of moe_stream_q4k_kernel bit for bit.  (lfm2moe
-// shapes, 256 tokens, top 4 of 32, C harness: gate/up 29.4 against 34.0 us,
-// down 28.7 against 37.4 us.)
+// the results are those of moe_stream_q4k_kernel bit for bit.  With PAIR
+// the row groups run over two matrices that read the same activation rows
+// (w, then w2: the routed FFN's gate and up), so one split serves both.
+// (lfm2moe shapes, 256 tokens, top 4 of 32, C harness: gate/up 29.4
+// against 34.0 us, down 28.7 against 37.4 us; gate + up in one launch 48
+// against 59 us for two.)
 constexpr int kSxRow = 80;   // sx row stride (floats): four rows of one read on distinct banks
 
 template <int NSB, int T>
