@@ -290,12 +290,14 @@ def test_moe_gemm_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
 
 
 @pytest.mark.parametrize("n_tokens,n_experts,top_k,n,k", [(70, 8, 2, 200, 2048), (300, 4, 2, 2000, 1536),
-                                                          (64, 300, 1, 100, 2048), (1, 32, 4, 1536, 2048)])
+                                                          (64, 300, 1, 100, 2048), (1, 32, 4, 1536, 2048),
+                                                          (20, 3, 2, 8, 1536)])
 def test_moe_gemm_whole_k_shapes(cq, orc, n_tokens, n_experts, top_k, n, k):
     """The whole-k Q4_K kernel (k of 8 or 6 super-blocks): n not a multiple
     of 16, several passes per expert (up to 150 tokens), two row groups per
     wave with a ragged last workgroup (n = 2000 at k = 1536), more experts
-    than CUs with most of them empty, and a single token."""
+    than CUs with most of them empty, a single token, and fewer rows than
+    one 16-row group (n = 8)."""
     w = gs.expert_weights(FMT, n_experts, n, k, cfg=740 + n_tokens, which=0)
     ids, _ = gs.routing(n_tokens, n_experts, top_k, cfg=740 + n_tokens)
     offs, pairs = orc.moe_group(ids, n_experts)
