@@ -291,8 +291,10 @@ def prefill_gemm(cq, gs, dev, stream):
         wl = copies_of(gs.weights(c["fmt"], n, k, cfg=c["cfg"]), dev, 512 * 2**20)
         xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c["cfg"])).to(dev))
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        # ~12 ms of untimed launches first (as for the GEMV steps: the first
+        # milliseconds of sustained load after lighter work run slower)
         us = bracketed_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y),
-                          40 if m == 2048 else 100, stream)
+                          40 if m == 2048 else 100, stream, warm=30 if m == 2048 else 120)
         tops = 2 * m * n * k / us / 1e6
         res[m] = (us, tops)
         out[f"q4_0_gemm_{m}x{n}x{k}"] = {"us": round(us, 2), "TOPS": round(tops, 1),
@@ -391,7 +393,8 @@ def secondary(cq, gs, dev, stream):
         wl = copies_of(gs.weights(c["fmt"], n, k, cfg=c["cfg"]), dev, 512 * 2**20)
         xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c["cfg"])).to(dev))
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        us = burst_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y), 40, stream)
+        us = burst_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y), 40, stream,
+                      warm=60)
         tops = 2 * m * n * k / us / 1e6
         out[f"{gs.NAMES[c['fmt']]}_gemm_{m}x{n}x{k}"] = {
             "us": round(us, 2), "TOPS": round(tops, 1),

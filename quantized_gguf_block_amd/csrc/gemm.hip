@@ -566,16 +566,23 @@ __device__ __forceinline__ void store_w2(Smem2<FMT>& s, const WRaw<FMT>& r) {
     for (int bl = 0; bl < 2; ++bl) {
         const int b = 2 * half + bl;
         uint32_t o[8];
-        s.dw[b][row] = h2f(half_at(r.v, bl * BS));
         if constexpr (FMT == T_Q8_0) {
+            s.dw[b][row] = h2f(half_at(r.v, bl * BS));
             extract<8>(r.v, bl * BS + 2, o);
         } else {
+            // Q4_0: each nibble q goes to the top of its byte with the top
+            // bit flipped, (q << 4 or q) & 0xF0 ^ 0x80 = the signed byte
+            // 16 (q - 8) (a shift and one three-input bitwise op, or just the
+            // latter), so the MFMA sums 16 x the integer dot; the block scale
+            // is held divided by 16 (exact), and t = D*dx - bias*dx rounds
+            // to 16 x the plain t, so the products are bitwise unchanged.
+            s.dw[b][row] = h2f(half_at(r.v, bl * BS)) * 0.0625f;
             uint32_t q[4];
             extract<4>(r.v, bl * BS + 2, q);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                o[i] = nib_lo_s8(q[i]);
-                o[4 + i] = nib_hi_s8(q[i]);
+                o[i] = ((q[i] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+                o[4 + i] = (q[i] & 0xF0F0F0F0u) ^ 0x80808080u;
             }
         }
         *reinterpret_cast<uint4*>(s.w + lds_off(row, 2 * b)) = make_uint4(o[0], o[1], o[2], o[3]);
