@@ -105,23 +105,6 @@ def burst_us(fn, reps, stream, warm=3):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
-def bracketed_us(fn, reps, stream, warm=3):
-    """Average duration of one call fn(i) over `reps` calls, each between its
-    own pair of HIP events on the launch stream (what a kernel trace reports
-    per dispatch, plus the event packets' own few microseconds)."""
-    import torch
-    for i in range(warm):
-        fn(i)
-    torch.cuda.synchronize()
-    ev = [events() for _ in range(reps)]
-    for i in range(reps):
-        ev[i][0].record(stream)
-        fn(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
-
-
 def graph_us(fn, nsteps, reps, stream):
     """Average duration of one call fn(i) with fn(0) .. fn(nsteps-1) captured
     in one HIP graph and replayed `reps` times between HIP events: the GPU
@@ -281,7 +264,7 @@ def main():
 def prefill_gemm(cq, gs, dev, stream):
     """Q4_0 prefill GEMM 14336 x 4096 at 2048 and 512 tokens: weights rotated
     through copies (>= 512 MB), activations quantized once; int8 TOPS from
-    HIP events around bursts of back-to-back launches."""
+    HIP events around bursts of back-to-back launches after a warm-up."""
     import torch
     out = {}
     res = {}
@@ -292,9 +275,11 @@ def prefill_gemm(cq, gs, dev, stream):
         xq = cq.cq_quantize_q8_0(torch.from_numpy(gs.activations(m, k, cfg=c["cfg"])).to(dev))
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         # ~12 ms of untimed launches first (as for the GEMV steps: the first
-        # milliseconds of sustained load after lighter work run slower)
-        us = bracketed_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y),
-                          40 if m == 2048 else 100, stream, warm=30 if m == 2048 else 120)
+        # milliseconds of sustained load after lighter work run slower), then
+        # a burst of back-to-back launches between two HIP events (an event
+        # pair around each launch would add the packets' own ~5 us to each)
+        us = burst_us(lambda i: cq.cq_gemm(c["fmt"], wl[i % len(wl)], n, k, xq, m, y=y),
+                      40 if m == 2048 else 100, stream, warm=30 if m == 2048 else 120)
         tops = 2 * m * n * k / us / 1e6
         res[m] = (us, tops)
         out[f"q4_0_gemm_{m}x{n}x{k}"] = {"us": round(us, 2), "TOPS": round(tops, 1),
