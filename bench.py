@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_I8_PEAK_TOPS = 5030.0
 CSRC = "quantized_gguf_block_amd/csrc/"
-GEMV_SOURCES = (CSRC + "gemv.hip", CSRC + "cq_device.h")
+GEMV_SOURCES = (CSRC + "gemv.hip", CSRC + "gemv_mfma.hip", CSRC + "cq_device.h")
 GEMM_SOURCES = (CSRC + "gemm.hip", CSRC + "cq_device.h")
 
 
@@ -142,7 +142,7 @@ def copies_of(host, dev, min_bytes, min_copies=2):
 
 
 def lm_head_kernel(batch):
-    return f"gemv_stream_kernel<12, {batch}, 1, 4, false, false, 1>"
+    return f"gemv_q4k_mfma_kernel<{batch}>"
 
 
 def gemm_kernel_name():
@@ -234,7 +234,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 dot4 + fp32 scale (Q4_K weights, Q8_0 activations)",
+        "dtype": "int8 MFMA dots + fp32 scale (Q4_K weights, Q8_0 activations)",
         "data": "synthetic",
         "config": {"workload": "LM-head decode GEMV 128256x4096, GGUF Q4_K, batch 1 (decode) and "
                                "batch 4 (speculative verify), the 4 activation rows quantized to "

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libcq.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["cq_api.cpp", "quantize.hip", "gemv.hip", "gemm.hip", "moe.hip", "select.hip"]
+SOURCES = ["cq_api.cpp", "quantize.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "moe.hip", "select.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -16,6 +16,13 @@ int launch_swiglu_quantize_q8_0(const float* g, const float* u, int64_t ld, int6
                                 int64_t k, float* h, void* hq, hipStream_t stream);
 int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
                 float* y, int64_t ldy, hipStream_t stream);
+// Q4_K GEMV with 4096-value rows on the 4x4x4 int8 matrix cores (gemv_mfma.hip):
+// taken for matrices of at least kMfmaMinRows rows, 1..8 activation rows and a
+// 16-byte aligned xq; otherwise launch_gemv uses the streaming kernel.
+constexpr int64_t kMfmaMinRows = 32768;
+bool gemv_q4k_mfma_ok(int64_t n, int64_t k, int64_t batch, const void* xq);
+int launch_gemv_q4k_mfma(const void* w, int64_t n, const void* xq, int64_t batch, float* y,
+                         int64_t ldy, hipStream_t stream);
 int launch_gemv_swiglu(int wt, const void* w_gate, const void* w_up, int64_t n, int64_t k,
                        const void* xq, int64_t batch, float* h, int64_t ldh, hipStream_t stream);
 int launch_moe_gemv(int wt, const void* w_experts, int64_t n_experts, int64_t n, int64_t k,

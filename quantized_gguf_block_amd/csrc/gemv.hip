@@ -1551,6 +1551,10 @@ int gemv_shape_ok(int wt, int64_t k, int64_t batch) {
 
 int launch_gemv(int wt, const void* w, int64_t n, int64_t k, const void* xq, int64_t batch,
                 float* y, int64_t ldy, hipStream_t stream) {
+    // tall Q4_K matrices with 4096-value rows: integer dots on the matrix
+    // cores (gemv_mfma.hip); the choice does not depend on the batch size
+    if (wt == T_Q4_K && gemv_q4k_mfma_ok(n, k, batch, xq))
+        return launch_gemv_q4k_mfma(w, n, xq, batch, y, ldy, stream);
     if (gemv_shape_ok(wt, k, batch) != 0) return -3;
     const int64_t bs = block_bytes_of(wt);
     const int64_t qk = block_elems_of(wt);

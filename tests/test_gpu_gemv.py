@@ -195,3 +195,54 @@ def test_gemv_max_k(cq, orc, fmt):
     x2 = to_dev(orc.quantize_q8_0(gs.activations(1, k2, cfg=311)))
     with pytest.raises(RuntimeError, match="SHAPE"):
         cq.cq_gemv(fmt, w2, 2, k2, x2, 1)
+
+
+# Q4_K matrices with 4096-value rows and at least this many rows take the
+# matrix-core kernel (integer dots on 4x4x4 int8 MFMA blocks)
+MFMA_MIN_ROWS = 32768
+
+
+@pytest.mark.parametrize("n", [MFMA_MIN_ROWS - 1, MFMA_MIN_ROWS, MFMA_MIN_ROWS + 3])
+def test_gemv_q4k_matrix_core_path(cq, orc, n):
+    """Every output against the oracle at batch 1 (each of 8 rows) and at
+    batch 2, 3, 4, 5 and 8 (5..8: two 4-row launches), each batch row bitwise
+    the batch-1 result; ragged row counts (not a multiple of the 4-row step),
+    and the row count just below the switch (the streaming kernel)."""
+    k = 4096
+    w = gs.weights(gs.Q4_K, n, k, cfg=310 + n % 7)
+    xq = orc.quantize_q8_0(gs.activations(8, k, cfg=310))
+    y_ref, s_ref = orc.matmul(gs.Q4_K, w, n, k, xq, 8)
+    wd = to_dev(w)
+    note("gemv q4_k matrix-core path", n)
+    y1 = [to_host(cq.cq_gemv(gs.Q4_K, wd, n, k, to_dev(xq[b:b + 1]), 1))[0] for b in range(8)]
+    assert_close_to_oracle(np.stack(y1), y_ref, s_ref, what=f"q4_k n{n} b1")
+    for batch in (2, 3, 4, 5, 8):
+        yb = to_host(cq.cq_gemv(gs.Q4_K, wd, n, k, to_dev(xq[:batch]), batch))
+        assert_close_to_oracle(yb, y_ref[:batch], s_ref[:batch], what=f"q4_k n{n} b{batch}")
+        for b in range(batch):
+            assert np.array_equal(yb[b], y1[b]), (batch, b)
+
+
+def test_gemv_q4k_matrix_core_invariants(cq, orc):
+    """On the matrix-core kernel: two runs bitwise equal, doubling every d and
+    dmin doubles y bitwise, permuting weight rows permutes y, and a strided
+    output leaves the columns past n alone."""
+    import torch
+    n, k = MFMA_MIN_ROWS + 6, 4096
+    w = gs.weights(gs.Q4_K, n, k, cfg=311)
+    xq = orc.quantize_q8_0(gs.activations(3, k, cfg=311))
+    note("gemv q4_k matrix-core invariants")
+    y0 = run_gemv(cq, gs.Q4_K, w, n, k, xq, 3)
+    assert np.array_equal(y0, run_gemv(cq, gs.Q4_K, w, n, k, xq, 3))
+    w2 = w.copy().reshape(-1, gs.BLOCK_BYTES[gs.Q4_K])
+    for o in (0, 2):
+        h = w2[:, o:o + 2].copy().view(np.float16)
+        w2[:, o:o + 2] = (h * np.float16(2)).view(np.uint8)
+    assert np.array_equal(run_gemv(cq, gs.Q4_K, w2.reshape(n, -1), n, k, xq, 3), 2 * y0)
+    perm = np.random.default_rng(2).permutation(n)
+    assert np.array_equal(run_gemv(cq, gs.Q4_K, w[perm], n, k, xq, 3), y0[:, perm])
+    y = torch.full((3, n + 40), -7.0, device="cuda")
+    cq.cq_gemv(gs.Q4_K, to_dev(w), n, k, to_dev(xq), 3, y=y, ldy=n + 40)
+    yh = to_host(y)
+    assert np.array_equal(yh[:, :n], y0)
+    assert np.all(yh[:, n:] == -7.0)
