@@ -246,3 +246,24 @@ def test_gemv_q4k_matrix_core_invariants(cq, orc):
     yh = to_host(y)
     assert np.array_equal(yh[:, :n], y0)
     assert np.all(yh[:, n:] == -7.0)
+
+
+def test_gemv_q4k_tall_unaligned_activations(cq, orc):
+    """A tall Q4_K matrix with the activations 2 bytes past a 16-byte
+    boundary (the streaming kernel): within the oracle's bound, and each batch
+    row bitwise the batch-1 call on that row at the same alignment."""
+    import torch
+    n, k, B = MFMA_MIN_ROWS + 2, 4096, 4
+    w = gs.weights(gs.Q4_K, n, k, cfg=312)
+    xq = orc.quantize_q8_0(gs.activations(B, k, cfg=312))
+    y_ref, s_ref = orc.matmul(gs.Q4_K, w, n, k, xq, B)
+    wd = to_dev(w)
+    buf = torch.zeros(xq.size + 16, dtype=torch.uint8, device="cuda")
+    buf[2:2 + xq.size] = to_dev(xq.reshape(-1))
+    xu = buf[2:2 + xq.size].view(B, -1)
+    note("gemv q4_k tall unaligned")
+    yb = to_host(cq.cq_gemv(gs.Q4_K, wd, n, k, xu, B))
+    assert_close_to_oracle(yb, y_ref, s_ref, what="q4_k tall unaligned")
+    for b in range(B):
+        y1 = to_host(cq.cq_gemv(gs.Q4_K, wd, n, k, xu[b:b + 1], 1))
+        assert np.array_equal(y1[0], yb[b]), b
