@@ -288,6 +288,11 @@ int launch_b(const uint8_t* w, int64_t n, const uint8_t* xq, int64_t xrb, float*
     const int64_t steps = (n + kStepRows - 1) / kStepRows;
     int64_t waves = static_cast<int64_t>(device_cu_count()) * kWaves;
     if (waves > steps) waves = steps;
+    // as few waves as keep the most steps per wave: nearly all of them then
+    // run that many steps and end together (128256 rows: 1004 waves, 940 of
+    // them with 32 steps, instead of 1024 waves, 320 with 32)
+    const int64_t spw = (steps + waves - 1) / waves;
+    waves = (steps + spw - 1) / spw;
     const int64_t wgs = (waves + kWaves - 1) / kWaves, nw = wgs * kWaves;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(kWave * kWaves), 0, stream, w, n,
                        steps / nw, static_cast<int>(steps % nw), xq, xrb, y, ldy);
