@@ -267,3 +267,19 @@ def test_gemv_q4k_tall_unaligned_activations(cq, orc):
     for b in range(B):
         y1 = to_host(cq.cq_gemv(gs.Q4_K, wd, n, k, xu[b:b + 1], 1))
         assert np.array_equal(y1[0], yb[b]), b
+
+
+def test_gemv_q4k_matrix_core_zeros_exact(cq, orc):
+    """On the matrix-core kernel: weights whose 6-bit scales and mins are all
+    zero (every weight exactly 0), and all-zero activations, give outputs
+    that are exactly zero."""
+    n, k = MFMA_MIN_ROWS + 1, 4096
+    w = gs.weights(gs.Q4_K, n, k, cfg=313)
+    wz = w.copy()
+    wz.reshape(-1, gs.BLOCK_BYTES[gs.Q4_K])[:, 4:16] = 0
+    xq = orc.quantize_q8_0(gs.activations(3, k, cfg=313))
+    note("gemv q4_k matrix-core zero weights")
+    assert not run_gemv(cq, gs.Q4_K, wz, n, k, xq, 3).any()
+    x0 = orc.quantize_q8_0(np.zeros((3, k), dtype=np.float32))
+    note("gemv q4_k matrix-core zero activations")
+    assert not run_gemv(cq, gs.Q4_K, w, n, k, x0, 3).any()
