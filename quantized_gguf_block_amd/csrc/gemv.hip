@@ -340,9 +340,9 @@ __device__ __forceinline__ void q6k_column_dot(const uint8_t* lds, int off, int 
         for (int t = 0; t < 4; ++t) q[t] = q6k_quant4(qla[t], qlb[t], qh[t], g);
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            int s = a[j].start[g];
+            int s = sdot4_v(q[0], a[j].q[g][0], a[j].start[g]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) s = sdot4(q[t], a[j].q[g][t], s);
+            for (int t = 1; t < 4; ++t) s = sdot4(q[t], a[j].q[g][t], s);
             const float sx = fmaf(__int_as_float(s), a[j].dx[g], a[j].ndx[g]);
             acc[j] = fmaf(sx, dsc, acc[j]);
         }
@@ -427,9 +427,9 @@ __device__ __forceinline__ void q10_column_dot(const uint8_t* lds, int off, int 
             e[t] = (__builtin_amdgcn_ubfe(bits[j], 4 * t, 4) * 0x00408102u) & 0x02020202u;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            int s = a[b].start[j];
+            int s = sdot4_v(e[0], a[b].q[j][0], a[b].start[j]);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) s = sdot4(e[t], a[b].q[j][t], s);
+            for (int t = 1; t < 8; ++t) s = sdot4(e[t], a[b].q[j][t], s);
             const float sx = fmaf(__int_as_float(s), a[b].dx[j], a[b].ndx[j]);
             acc[b] = fmaf(sx, d, acc[b]);
         }
