@@ -1052,6 +1052,11 @@ __global__ __launch_bounds__(kWave * kGW) void gemv_stream_kernel(
         if constexpr (KS > 1) {
             const int left = bytes - slice_off;
             bytes = left < 0 ? 0 : (left > slice_bytes<FMT, C>() ? slice_bytes<FMT, C>() : left);
+            // (the clamp is formed with a vector instruction; the value is
+            // wave-uniform, and reading it back into a scalar register keeps
+            // the compiler from wrapping each load in a loop over the
+            // descriptor values)
+            bytes = __builtin_amdgcn_readfirstlane(bytes);
             base += slice_off;
         }
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(base, bytes);
